@@ -1,0 +1,47 @@
+"""ctypes loader for the device filler (input data only)."""
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import gen
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_synth.so")
+_lib = None
+_tables = {}
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        _lib = ctypes.CDLL(LIB_PATH)
+        f = _lib.dsa_synth_fill_bf16_normal
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                      ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    return _lib
+
+
+def _table(device):
+    import torch
+    key = str(device)
+    if key not in _tables:
+        t = torch.from_numpy(gen.normal_table_bf16().view(np.int16).copy())
+        _tables[key] = t.to(device)
+    return _tables[key]
+
+
+def fill_bf16_normal(t, seed, tag, offset=0):
+    """Fill the contiguous bf16 CUDA tensor ``t`` with stream (seed, tag) from ``offset``."""
+    import torch
+    assert t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()
+    stream = torch.cuda.current_stream(t.device).cuda_stream
+    rc = lib().dsa_synth_fill_bf16_normal(t.data_ptr(), t.numel(), offset, seed, tag,
+                                          _table(t.device).data_ptr(), stream)
+    if rc != 0:
+        raise RuntimeError(f"dsa_synth_fill_bf16_normal failed: {rc}")
+    return t
