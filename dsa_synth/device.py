@@ -45,3 +45,28 @@ def fill_bf16_normal(t, seed, tag, offset=0):
     if rc != 0:
         raise RuntimeError(f"dsa_synth_fill_bf16_normal failed: {rc}")
     return t
+
+
+def upload(w, device="cuda"):
+    """Device tensors of workload ``w``: K/V pools filled on the device, the
+    small tensors copied from the host.  Returns a dict of torch tensors."""
+    import torch
+
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    k = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    v = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    fill_bf16_normal(k, w.seed, gen.TAG_K)
+    fill_bf16_normal(v, w.seed, gen.TAG_V)
+
+    def t(a, dtype=None):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            x = x.view(dtype)
+        return x.to(device)
+
+    return dict(
+        k_cache=k, v_cache=v, idx_keys=t(w.idx_keys), idx_scale=t(w.idx_scale),
+        block_table=t(w.block_table.astype(np.int32)), seq_lens=t(w.seq_lens.astype(np.int32)),
+        q=t(w.q_bits.view(np.int16), torch.bfloat16),
+        q_idx=t(w.q_idx_bits.view(np.int16), torch.bfloat16), w_idx=t(w.w),
+        q_seq=None if w.decode else t(w.q_seq), q_pos=None if w.decode else t(w.q_pos))

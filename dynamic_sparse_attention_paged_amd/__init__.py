@@ -1,0 +1,222 @@
+"""MI355X (gfx950) dynamic sparse attention over a paged KV cache.
+
+A thin Python binding over libdsa.so (C ABI in include/dsa.h): argument
+marshalling only.  Every step of the method runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream.  There is no
+CPU or PyTorch fallback: if libdsa.so is missing the calls raise.
+
+    kv = PagedKV(k_cache, v_cache, idx_keys, idx_scale, block_table, seq_lens)
+    qs = Queries(q, q_idx, w_idx, q_seq=None, q_pos=None)
+    out, lse = decode_fused(kv, qs, top_k, softmax_scale)
+"""
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+__all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
+           "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "index_topk",
+           "workspace_size", "abi_version"]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_lib.STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+@dataclass
+class PagedKV:
+    k_cache: torch.Tensor      # bf16 [P, 64, Hkv, 128]
+    v_cache: torch.Tensor      # bf16 [P, 64, Hkv, 128]
+    idx_keys: torch.Tensor     # uint8 (E4M3 codes) [P, dI]
+    idx_scale: torch.Tensor    # f32 [P]
+    block_table: torch.Tensor  # int32 [B, max_blocks]
+    seq_lens: torch.Tensor     # int32 [B]
+
+    def struct(self):
+        def ptr(t):
+            return t.data_ptr() if t is not None else None
+        k = self.k_cache
+        P, bs, hkv, d = k.shape if k is not None else (self.idx_keys.shape[0], 64, 1, 128)
+        return _lib.PagedKVStruct(
+            ptr(self.k_cache), ptr(self.v_cache), ptr(self.idx_keys), ptr(self.idx_scale),
+            ptr(self.block_table), ptr(self.seq_lens), P, bs, hkv, d,
+            self.idx_keys.shape[1] if self.idx_keys is not None else 0,
+            self.block_table.shape[0], self.block_table.shape[1])
+
+
+@dataclass
+class Queries:
+    q: Optional[torch.Tensor]        # bf16 [Nq, Hq, 128]
+    q_idx: Optional[torch.Tensor]    # bf16 [Nq, HI, dI]
+    w_idx: Optional[torch.Tensor]    # f32 [Nq, HI]
+    q_seq: Optional[torch.Tensor] = None  # int32 [Nq]
+    q_pos: Optional[torch.Tensor] = None  # int32 [Nq]
+
+    @property
+    def num_queries(self):
+        t = self.q if self.q is not None else self.q_idx
+        return t.shape[0]
+
+    def struct(self):
+        def ptr(t):
+            return t.data_ptr() if t is not None else None
+        hq = self.q.shape[1] if self.q is not None else 0
+        hi = self.q_idx.shape[1] if self.q_idx is not None else 0
+        return _lib.QueriesStruct(self.num_queries, hq, hi, ptr(self.q_seq), ptr(self.q_pos),
+                                  ptr(self.q), ptr(self.q_idx), ptr(self.w_idx))
+
+
+def _check_tensors(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+def _check(status):
+    if status != 0:
+        lib = _lib.load()
+        raise DSAError(status, lib.dsa_last_error().decode())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _kv_tensors(kv):
+    return (kv.k_cache, kv.v_cache, kv.idx_keys, kv.idx_scale, kv.block_table, kv.seq_lens)
+
+
+def _q_tensors(qs):
+    return (qs.q, qs.q_idx, qs.w_idx, qs.q_seq, qs.q_pos)
+
+
+def abi_version():
+    return _lib.load().dsa_abi_version()
+
+
+def workspace_size(op, kv, qs, top_k):
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_workspace_size(op, ctypes.byref(kvs), ctypes.byref(qss), top_k,
+                                  ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def index_score(kv, qs, scores=None):
+    """fp32 [Nq, max_blocks] block scores (-inf where not visible)."""
+    lib = _lib.load()
+    _check_tensors(*_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.idx_keys.device
+    if scores is None:
+        scores = torch.empty(qs.num_queries, kv.block_table.shape[1], dtype=torch.float32,
+                             device=dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_index_score(ctypes.byref(kvs), ctypes.byref(qss), scores.data_ptr(),
+                               _stream(dev)))
+    return scores
+
+
+def topk_blocks(scores, kv, qs, top_k, block_idx=None, block_cnt=None):
+    """(int32 [Nq, top_k] ascending logical ids, -1 padded; int32 [Nq] counts)."""
+    lib = _lib.load()
+    _check_tensors(scores, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = scores.device
+    nq = qs.num_queries
+    if block_idx is None:
+        block_idx = torch.empty(nq, top_k, dtype=torch.int32, device=dev)
+    if block_cnt is None:
+        block_cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_topk_blocks(scores.data_ptr(), ctypes.byref(kvs), ctypes.byref(qss), top_k,
+                               block_idx.data_ptr(), block_cnt.data_ptr(), _stream(dev)))
+    return block_idx, block_cnt
+
+
+def sparse_attn_decode(kv, qs, block_idx, block_cnt, top_k, softmax_scale, out=None,
+                       lse=None, workspace=None):
+    lib = _lib.load()
+    _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.k_cache.device
+    nq, hq = qs.q.shape[0], qs.q.shape[1]
+    if out is None:
+        out = torch.empty(nq, hq, 128, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(nq, hq, dtype=torch.float32, device=dev)
+    need = workspace_size(_lib.OP_ATTN_DECODE, kv, qs, top_k)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_sparse_attn_decode(ctypes.byref(kvs), ctypes.byref(qss), block_idx.data_ptr(),
+                                      block_cnt.data_ptr(), top_k, float(softmax_scale),
+                                      out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), _stream(dev)))
+    return out, lse
+
+
+def sparse_attn_prefill(kv, qs, block_idx, block_cnt, top_k, softmax_scale, out=None, lse=None):
+    lib = _lib.load()
+    _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.k_cache.device
+    nq, hq = qs.q.shape[0], qs.q.shape[1]
+    if out is None:
+        out = torch.empty(nq, hq, 128, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(nq, hq, dtype=torch.float32, device=dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_sparse_attn_prefill(ctypes.byref(kvs), ctypes.byref(qss),
+                                       block_idx.data_ptr(), block_cnt.data_ptr(), top_k,
+                                       float(softmax_scale), out.data_ptr(), lse.data_ptr(),
+                                       _stream(dev)))
+    return out, lse
+
+
+def decode_fused(kv, qs, top_k, softmax_scale, out=None, lse=None, block_idx=None,
+                 block_cnt=None, workspace=None):
+    """Scoring, selection and attention in one call.  Returns (out, lse, block_idx, block_cnt);
+    block_idx / block_cnt are None unless tensors are passed in to receive them."""
+    lib = _lib.load()
+    _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.k_cache.device
+    nq, hq = qs.q.shape[0], qs.q.shape[1]
+    if out is None:
+        out = torch.empty(nq, hq, 128, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(nq, hq, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(workspace_size(_lib.OP_DECODE_FUSED, kv, qs, top_k), dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_sparse_decode_fused(
+        ctypes.byref(kvs), ctypes.byref(qss), top_k, float(softmax_scale), out.data_ptr(),
+        lse.data_ptr(), block_idx.data_ptr() if block_idx is not None else None,
+        block_cnt.data_ptr() if block_cnt is not None else None, workspace.data_ptr(),
+        workspace.numel(), _stream(dev)))
+    return out, lse, block_idx, block_cnt
+
+
+def index_topk(kv, qs, top_k, block_idx=None, block_cnt=None, workspace=None):
+    lib = _lib.load()
+    _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.idx_keys.device
+    nq = qs.num_queries
+    if block_idx is None:
+        block_idx = torch.empty(nq, top_k, dtype=torch.int32, device=dev)
+    if block_cnt is None:
+        block_cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _workspace(workspace_size(_lib.OP_INDEX_TOPK, kv, qs, top_k), dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_index_topk(ctypes.byref(kvs), ctypes.byref(qss), top_k, block_idx.data_ptr(),
+                              block_cnt.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                              _stream(dev)))
+    return block_idx, block_cnt

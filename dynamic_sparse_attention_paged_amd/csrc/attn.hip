@@ -1,0 +1,306 @@
+// Sparse attention over the gathered K/V of the selected blocks.
+//
+// What is computed ([P1] "Day-0 Adaptation for Massive LLMs...", section
+// 4(3): gather the selected blocks, then sparse attention; [P4] "Day-0
+// Adaptation for Large Language Models...", full-vs-sparse table: only the
+// index-selected pairs, otherwise the full-attention formula; [P5] "KV Cache
+// Layout": whole blocks read through the block table): for query head h with
+// KV head g = h / G (G = Hq / Hkv), over the tokens t of the selected blocks
+// with position j*64 + t <= pos and < seq_len,
+//   x_t = scale <q_h, K_t>,  out_h = sum_t e^(x_t - m) V_t / sum_t e^(x_t - m),
+//   lse_h = m + ln sum_t e^(x_t - m).
+//
+// Decode is HBM-bound: one (query, KV head, split) per workgroup, four waves,
+// each wave streaming whole 64-token blocks of head g (K and V rows of 256 B
+// at a 2 KiB stride).  Per block and wave, with the G query heads of g as the
+// 16 MFMA columns:
+//   S^T[64 tok x 16 heads] = K[64 x 128] . Q^T        16 x mfma 16x16x32 bf16
+//   online softmax per head (lane's head = lane % 16 in every tile)
+//   O^T[128 x 16] += V^T[128 x 64] . P^T[64 x 16]       32 x mfma (P = hi + lo bf16)
+// K is an MFMA operand straight from global memory (8 consecutive dims per
+// lane).  V must be read with 8 tokens per lane, so it is staged in LDS.
+// P is split into a bf16 high part and a bf16 residual, which keeps the
+// softmax weights at ~16 significant bits through the bf16 MFMA.
+// The four waves' states, then (if split) the workgroups' states, are merged
+// with the usual max / rescale rule; logits are kept in base 2.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kVRow = 132;  // LDS row of V in uint16: 128 dims + 4 pad (264 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(i16x8 a, i16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs: round to nearest even
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+struct WaveState {
+  float m;      // running max (base-2 logits) of the lane's head
+  float l;      // running sum of 2^(x - m)
+  f32x4 o[8];   // O^T tiles: o[dt][i] = O[head = lane%16][d = 16 dt + 4 (lane/16) + i]
+};
+
+// Process one selected block for one wave.
+__device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kbase,
+                                             const uint16_t* __restrict__ vbase, int hkv,
+                                             const i16x8 (&qf)[4], float scale2, int tok0,
+                                             int pos, int len, uint16_t* vs, WaveState& st) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, gq = lane >> 4;
+  const size_t tok_stride = (size_t)hkv * kHeadDim;  // elements between consecutive tokens
+
+  // K fragments: A operand rows = tokens 16T + r, k = dims 32c + 8gq .. +8
+  i16x8 kf[4][4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      kf[T][c] = *reinterpret_cast<const i16x8*>(kbase + (size_t)(16 * T + r) * tok_stride +
+                                                 32 * c + 8 * gq);
+  // V rows: lane loads dims 8r .. 8r+8 of tokens gq + 4u, u = 0..15
+  i16x8 vr[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    vr[u] = *reinterpret_cast<const i16x8*>(vbase + (size_t)(gq + 4 * u) * tok_stride + 8 * r);
+
+  // S^T = K . Q^T
+  f32x4 sc[4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = mfma_bf16(kf[T][c], qf[c], acc);
+    sc[T] = acc;
+  }
+  // stage V in LDS (row-major [token][dim], padded rows); wave-private region
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    uint16_t* dst = vs + (gq + 4 * u) * kVRow + 8 * r;
+    const uint2* src = reinterpret_cast<const uint2*>(&vr[u]);
+    reinterpret_cast<uint2*>(dst)[0] = src[0];
+    reinterpret_cast<uint2*>(dst)[1] = src[1];
+  }
+
+  // mask + scale (base 2); sc[T][i] is token 16T + 4gq + i of head r
+  float mx = -INFINITY;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = tok0 + 16 * T + 4 * gq + i;
+      const float x = (a <= pos && a < len) ? sc[T][i] * scale2 : -INFINITY;
+      sc[T][i] = x;
+      mx = fmaxf(mx, x);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = (st.m == -INFINITY) ? 0.f : exp2f(st.m - m_new);
+  float rs = 0.f;
+  i16x8 ph[2], pl[2];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = sc[T][i];
+      const float p = (x == -INFINITY) ? 0.f : exp2f(x - m_new);
+      rs += p;
+      const uint32_t hb = f32_to_bf16_bits(p);
+      const uint32_t lb = f32_to_bf16_bits(p - bf16_bits_to_f32(hb));
+      ph[T >> 1][(T & 1) * 4 + i] = (short)hb;
+      pl[T >> 1][(T & 1) * 4 + i] = (short)lb;
+    }
+  rs += __shfl_xor(rs, 16, 64);
+  rs += __shfl_xor(rs, 32, 64);
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+
+  // O^T += V^T . P^T ; k-slot (gq, i) <-> token 16 (2 ks + i/4) + 4 gq + i%4
+  // LDS writes of this wave complete and not reordered past the reads below
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      i16x8 va;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = 16 * (2 * ks + (i >> 2)) + 4 * gq + (i & 3);
+        va[i] = (short)vs[tok * kVRow + 16 * dt + r];
+      }
+      st.o[dt] = mfma_bf16(va, ph[ks], st.o[dt]);
+      st.o[dt] = mfma_bf16(va, pl[ks], st.o[dt]);
+    }
+  }
+  // reads done before the next block overwrites vs
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// grid (splits, Hkv, Nq), block 256.  partials: [Nq][Hq][splits] x {m, l, o[128]}
+__global__ __launch_bounds__(kAttnThreads) void sparse_attn_split(
+    KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ partials) {
+  __shared__ uint16_t vs_all[kAttnWaves][64 * kVRow];
+  __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
+
+  const int sp = blockIdx.x, g = blockIdx.y, qi = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, gq = lane >> 4;
+  const int G = Q.hq / kv.num_kv_heads;
+  const int s = query_seq(Q, qi);
+  const int len = kv.seq_lens[s];
+  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  const int n_sel = cnt[qi];
+  const int per = (top_k + splits - 1) / splits;
+  const int b0 = sp * per, b1 = min(n_sel, b0 + per);
+
+  // Q^T fragments (B operand): column = head r of group g, k = dims 32c + 8gq .. +8
+  i16x8 qf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (r < G) {
+      qf[c] = *reinterpret_cast<const i16x8*>(Q.q + ((size_t)qi * Q.hq + g * G + r) * kHeadDim +
+                                             32 * c + 8 * gq);
+    } else {
+      qf[c] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  WaveState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t* vs = vs_all[wave];
+  const int32_t* sel = idx + (size_t)qi * top_k;
+  const int32_t* trow = kv.table + (size_t)s * kv.maxb;
+  for (int b = b0 + wave; b < b1; b += kAttnWaves) {
+    const int j = sel[b];
+    const int p = trow[j];
+    const size_t base = ((size_t)p * kBlockSize * kv.num_kv_heads + g) * kHeadDim;
+    attend_block(kv.k + base, kv.v + base, kv.num_kv_heads, qf, scale2, j * kBlockSize, pos, len,
+                 vs, st);
+  }
+
+  // ---- merge the four waves through LDS (reusing the V staging area)
+  __syncthreads();
+  float* wo = reinterpret_cast<float*>(&vs_all[0][0]);  // [wave][16 heads][128]
+  if (gq == 0) {
+    wm[wave][r] = st.m;
+    wl[wave][r] = st.l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wo[(wave * 16 + r) * kHeadDim + 16 * dt + 4 * gq + i] = st.o[dt][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * kHeadDim; e += kAttnThreads) {
+    const int h = e / kHeadDim, d = e % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wm[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      // wave accumulators are unnormalised: sum_t 2^(x_t - m_w) V_t
+      const float mw = wm[w][h];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      L += f * wl[w][h];
+      O += f * wo[(w * 16 + h) * kHeadDim + d];
+    }
+    const int hg = g * G + h;
+    if (splits == 1) {
+      out[((size_t)qi * Q.hq + hg) * kHeadDim + d] = O / L;
+      if (lse && d == 0) lse[(size_t)qi * Q.hq + hg] = (M + log2f(L)) * kLn2;
+    } else {
+      float* pp = partials + (((size_t)qi * Q.hq + hg) * splits + sp) * (kHeadDim + 2);
+      pp[2 + d] = (L > 0.f) ? O / L : 0.f;
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = L;
+      }
+    }
+  }
+}
+
+// grid (Nq * Hq), block 128: merge the split partials of one (query, head).
+__global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict__ partials,
+                                                         int splits, int hq,
+                                                         float* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  const int qh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* pp = partials + (size_t)qh * splits * (kHeadDim + 2);
+  float M = -INFINITY;
+  for (int i = 0; i < splits; ++i) M = fmaxf(M, pp[i * (kHeadDim + 2)]);
+  float L = 0.f, O = 0.f;
+  for (int i = 0; i < splits; ++i) {
+    const float* q = pp + i * (kHeadDim + 2);
+    const float f = (q[0] == -INFINITY) ? 0.f : q[1] * exp2f(q[0] - M);
+    L += f;
+    O += f * q[2 + d];
+  }
+  out[(size_t)qh * kHeadDim + d] = O / L;
+  if (lse && d == 0) lse[qh] = (M + log2f(L)) * kLn2;
+  (void)hq;
+}
+
+}  // namespace
+
+int attn_num_splits(int nq, int hkv, int top_k, bool prefill) {
+  if (prefill) return 1;
+  // Aim for >= ~2048 workgroups (8 per CU), but keep >= 2 blocks per wave.
+  const long units = (long)nq * hkv;
+  if (units <= 0) return 1;
+  int splits = (int)((2048 + units - 1) / units);
+  const int max_splits = (top_k + 2 * kAttnWaves - 1) / (2 * kAttnWaves);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  return splits;
+}
+
+size_t attn_partials_bytes(int nq, int hq, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)nq * hq * splits * (kHeadDim + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* idx,
+                              const int32_t* cnt, int top_k, float scale, float* out, float* lse,
+                              float* partials, int splits, hipStream_t st) {
+  const float scale2 = scale * kLog2e;
+  hipLaunchKernelGGL(sparse_attn_split, dim3(splits, kv.num_kv_heads, Q.nq), dim3(kAttnThreads),
+                     0, st, kv, Q, idx, cnt, top_k, scale2, splits, out, lse, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(merge_splits, dim3(Q.nq * Q.hq), dim3(kHeadDim), 0, st, partials, splits,
+                     Q.hq, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

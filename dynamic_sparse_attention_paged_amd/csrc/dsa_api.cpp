@@ -1,0 +1,305 @@
+// C-ABI entry points: host-side validation, workspace layout, dispatch.
+// Every check runs before anything is enqueued, so an invalid call has no
+// side effects and needs no GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsa_status ok() {
+  g_err[0] = '\0';
+  return DSA_OK;
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+enum Need : unsigned {
+  kNeedIndex = 1u,  // idx_keys, idx_scale, q_idx, w_idx
+  kNeedAttn = 2u,   // k_cache, v_cache, q
+};
+
+dsa_status check_common(const dsa_paged_kv* kv, const dsa_queries* qs, unsigned need) {
+  if (!kv || !qs) return fail(DSA_ERR_NULL, "kv and qs must not be NULL");
+  if (qs->num_queries < 0) return fail(DSA_ERR_SHAPE, "num_queries < 0");
+  if (kv->block_size != dsa::kBlockSize)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
+  if (kv->head_dim != dsa::kHeadDim)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: this build supports 128", kv->head_dim);
+  if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1 ||
+      kv->num_kv_heads < 1)
+    return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq, num_kv_heads must be >= 1");
+  if (!kv->block_table || !kv->seq_lens) return fail(DSA_ERR_NULL, "block_table/seq_lens NULL");
+  if (!qs->q_seq && qs->num_queries > kv->num_seqs)
+    return fail(DSA_ERR_SHAPE, "decode batch (q_seq NULL) needs num_queries <= num_seqs");
+  if (need & kNeedIndex) {
+    if (kv->idx_dim != 64 && kv->idx_dim != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "idx_dim %d: supported 64, 128", kv->idx_dim);
+    if (qs->idx_heads < 1 || qs->idx_heads > dsa::kMaxIdxHeads)
+      return fail(DSA_ERR_UNSUPPORTED, "idx_heads %d: supported 1..16", qs->idx_heads);
+    if (!kv->idx_keys || !kv->idx_scale || !qs->q_idx || !qs->w_idx)
+      return fail(DSA_ERR_NULL, "idx_keys/idx_scale/q_idx/w_idx NULL");
+    if (!aligned(kv->idx_keys, 16) || !aligned(qs->q_idx, 16) || !aligned(kv->idx_scale, 4) ||
+        !aligned(qs->w_idx, 4))
+      return fail(DSA_ERR_ALIGN, "idx_keys/q_idx need 16 B, idx_scale/w_idx 4 B alignment");
+  }
+  if (need & kNeedAttn) {
+    if (qs->num_q_heads < 1 || qs->num_q_heads % kv->num_kv_heads != 0)
+      return fail(DSA_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                  qs->num_q_heads, kv->num_kv_heads);
+    if (qs->num_q_heads / kv->num_kv_heads > dsa::kMaxGroup)
+      return fail(DSA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+    if (!kv->k_cache || !kv->v_cache || !qs->q) return fail(DSA_ERR_NULL, "k_cache/v_cache/q NULL");
+    if (!aligned(kv->k_cache, 16) || !aligned(kv->v_cache, 16) || !aligned(qs->q, 16))
+      return fail(DSA_ERR_ALIGN, "k_cache/v_cache/q need 16 B alignment");
+  }
+  return DSA_OK;
+}
+
+dsa_status check_topk(int32_t top_k) {
+  if (top_k < 1 || top_k > dsa::kMaxTopK) return fail(DSA_ERR_SHAPE, "top_k %d not in 1..4096", top_k);
+  return DSA_OK;
+}
+
+dsa::KvView kv_view(const dsa_paged_kv* kv) {
+  dsa::KvView v;
+  v.k = static_cast<const uint16_t*>(kv->k_cache);
+  v.v = static_cast<const uint16_t*>(kv->v_cache);
+  v.idx_keys = kv->idx_keys;
+  v.idx_scale = kv->idx_scale;
+  v.table = kv->block_table;
+  v.seq_lens = kv->seq_lens;
+  v.num_blocks = kv->num_blocks;
+  v.num_kv_heads = kv->num_kv_heads;
+  v.idx_dim = kv->idx_dim;
+  v.num_seqs = kv->num_seqs;
+  v.maxb = kv->max_blocks_per_seq;
+  return v;
+}
+
+dsa::QView q_view(const dsa_queries* qs) {
+  dsa::QView v;
+  v.nq = qs->num_queries;
+  v.hq = qs->num_q_heads;
+  v.hi = qs->idx_heads;
+  v.q_seq = qs->q_seq;
+  v.q_pos = qs->q_pos;
+  v.q = static_cast<const uint16_t*>(qs->q);
+  v.q_idx = static_cast<const uint16_t*>(qs->q_idx);
+  v.w = qs->w_idx;
+  return v;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Fused-decode workspace: scores | idx | cnt | attention partials.
+struct FusedLayout {
+  size_t scores, idx, cnt, partials, total;
+  int splits;
+};
+
+FusedLayout fused_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k) {
+  FusedLayout f;
+  const size_t nq = (size_t)qs->num_queries;
+  f.scores = 0;
+  f.idx = align_up(f.scores + nq * kv->max_blocks_per_seq * sizeof(float));
+  f.cnt = align_up(f.idx + nq * top_k * sizeof(int32_t));
+  f.partials = align_up(f.cnt + nq * sizeof(int32_t));
+  f.splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
+  f.total = align_up(f.partials + dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads,
+                                                           f.splits));
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_err; }
+
+const char* dsa_status_str(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "null pointer";
+    case DSA_ERR_SHAPE: return "bad shape";
+    case DSA_ERR_UNSUPPORTED: return "unsupported size";
+    case DSA_ERR_ALIGN: return "misaligned pointer";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+dsa_status dsa_workspace_size(int op, const dsa_paged_kv* kv, const dsa_queries* qs,
+                              int32_t top_k, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_NULL, "bytes NULL");
+  *bytes = 0;
+  dsa_status st;
+  switch (op) {
+    case DSA_OP_ATTN_DECODE: {
+      if ((st = check_common(kv, qs, kNeedAttn)) != DSA_OK) return st;
+      if ((st = check_topk(top_k)) != DSA_OK) return st;
+      const int splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
+      *bytes = dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads, splits);
+      return ok();
+    }
+    case DSA_OP_DECODE_FUSED: {
+      if ((st = check_common(kv, qs, kNeedAttn | kNeedIndex)) != DSA_OK) return st;
+      if ((st = check_topk(top_k)) != DSA_OK) return st;
+      *bytes = fused_layout(kv, qs, top_k).total;
+      return ok();
+    }
+    case DSA_OP_INDEX_TOPK: {
+      if ((st = check_common(kv, qs, kNeedIndex)) != DSA_OK) return st;
+      if ((st = check_topk(top_k)) != DSA_OK) return st;
+      *bytes = align_up((size_t)qs->num_queries * kv->max_blocks_per_seq * sizeof(float));
+      return ok();
+    }
+  }
+  return fail(DSA_ERR_SHAPE, "unknown op %d", op);
+}
+
+dsa_status dsa_index_score(const dsa_paged_kv* kv, const dsa_queries* qs, float* scores,
+                           hipStream_t stream) {
+  dsa_status st = check_common(kv, qs, kNeedIndex);
+  if (st != DSA_OK) return st;
+  if (!scores) return fail(DSA_ERR_NULL, "scores NULL");
+  if (!aligned(scores, 4)) return fail(DSA_ERR_ALIGN, "scores needs 4 B alignment");
+  if (qs->num_queries == 0) return ok();
+  return hip_status(dsa::launch_index_score(kv_view(kv), q_view(qs), scores, stream),
+                    "index_score launch");
+}
+
+dsa_status dsa_topk_blocks(const float* scores, const dsa_paged_kv* kv, const dsa_queries* qs,
+                           int32_t top_k, int32_t* block_idx, int32_t* block_cnt,
+                           hipStream_t stream) {
+  dsa_status st = check_common(kv, qs, 0);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!scores || !block_idx || !block_cnt) return fail(DSA_ERR_NULL, "scores/block_idx/block_cnt NULL");
+  if (!aligned(scores, 4) || !aligned(block_idx, 4) || !aligned(block_cnt, 4))
+    return fail(DSA_ERR_ALIGN, "scores/block_idx/block_cnt need 4 B alignment");
+  if (qs->num_queries == 0) return ok();
+  return hip_status(dsa::launch_topk(scores, kv_view(kv), q_view(qs), top_k, block_idx, block_cnt,
+                                     stream),
+                    "topk launch");
+}
+
+static dsa_status attn_common(const dsa_paged_kv* kv, const dsa_queries* qs,
+                              const int32_t* block_idx, const int32_t* block_cnt, int32_t top_k,
+                              float* out) {
+  dsa_status st = check_common(kv, qs, kNeedAttn);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!block_idx || !block_cnt || !out) return fail(DSA_ERR_NULL, "block_idx/block_cnt/out NULL");
+  if (!aligned(block_idx, 4) || !aligned(block_cnt, 4) || !aligned(out, 4))
+    return fail(DSA_ERR_ALIGN, "block_idx/block_cnt/out need 4 B alignment");
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                  const int32_t* block_idx, const int32_t* block_cnt,
+                                  int32_t top_k, float softmax_scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = attn_common(kv, qs, block_idx, block_cnt, top_k, out);
+  if (st != DSA_OK) return st;
+  const int splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
+  const size_t need = dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
+  if (qs->num_queries == 0) return ok();
+  return hip_status(dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
+                                            softmax_scale, out, lse,
+                                            static_cast<float*>(workspace), splits, stream),
+                    "sparse_attn_decode launch");
+}
+
+dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                   const int32_t* block_idx, const int32_t* block_cnt,
+                                   int32_t top_k, float softmax_scale, float* out, float* lse,
+                                   hipStream_t stream) {
+  dsa_status st = attn_common(kv, qs, block_idx, block_cnt, top_k, out);
+  if (st != DSA_OK) return st;
+  if (!qs->q_seq || !qs->q_pos) return fail(DSA_ERR_NULL, "prefill needs q_seq and q_pos");
+  if (qs->num_queries == 0) return ok();
+  return hip_status(dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
+                                            softmax_scale, out, lse, nullptr, 1, stream),
+                    "sparse_attn_prefill launch");
+}
+
+dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                                   float softmax_scale, float* out, float* lse,
+                                   int32_t* block_idx_out, int32_t* block_cnt_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = check_common(kv, qs, kNeedAttn | kNeedIndex);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!out) return fail(DSA_ERR_NULL, "out NULL");
+  if (!aligned(out, 4)) return fail(DSA_ERR_ALIGN, "out needs 4 B alignment");
+  if ((block_idx_out && !aligned(block_idx_out, 4)) || (block_cnt_out && !aligned(block_cnt_out, 4)))
+    return fail(DSA_ERR_ALIGN, "block_idx_out/block_cnt_out need 4 B alignment");
+  const FusedLayout f = fused_layout(kv, qs, top_k);
+  if (!workspace || workspace_bytes < f.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, f.total);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
+  if (qs->num_queries == 0) return ok();
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + f.scores);
+  int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + f.idx);
+  int32_t* cnt = block_cnt_out ? block_cnt_out : reinterpret_cast<int32_t*>(ws + f.cnt);
+  const dsa::KvView kvv = kv_view(kv);
+  const dsa::QView qv = q_view(qs);
+  hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
+  if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
+  e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
+  if (e != hipSuccess) return hip_status(e, "fused: topk launch");
+  e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse,
+                              reinterpret_cast<float*>(ws + f.partials), f.splits, stream);
+  return hip_status(e, "fused: attention launch");
+}
+
+dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                          int32_t* block_idx, int32_t* block_cnt, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = check_common(kv, qs, kNeedIndex);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!block_idx || !block_cnt) return fail(DSA_ERR_NULL, "block_idx/block_cnt NULL");
+  if (!aligned(block_idx, 4) || !aligned(block_cnt, 4))
+    return fail(DSA_ERR_ALIGN, "block_idx/block_cnt need 4 B alignment");
+  const size_t need = align_up((size_t)qs->num_queries * kv->max_blocks_per_seq * sizeof(float));
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
+  if (qs->num_queries == 0) return ok();
+  float* scores = static_cast<float*>(workspace);
+  const dsa::KvView kvv = kv_view(kv);
+  const dsa::QView qv = q_view(qs);
+  hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
+  if (e != hipSuccess) return hip_status(e, "index_topk: score launch");
+  return hip_status(dsa::launch_topk(scores, kvv, qv, top_k, block_idx, block_cnt, stream),
+                    "index_topk: topk launch");
+}
+
+}  // extern "C"

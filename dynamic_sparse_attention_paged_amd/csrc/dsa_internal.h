@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI layer (dsa_api.cpp) and the gfx950
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kBlockSize = 64;   // tokens per KV block
+constexpr int kHeadDim = 128;    // attention head dim
+constexpr int kMaxGroup = 16;    // max query heads per KV head
+constexpr int kMaxIdxHeads = 16;
+constexpr int kMaxTopK = 4096;
+
+struct KvView {
+  const uint16_t* k;        // bf16 [P, 64, Hkv, 128]
+  const uint16_t* v;
+  const uint8_t* idx_keys;  // [P, dI]
+  const float* idx_scale;   // [P]
+  const int32_t* table;     // [B, maxb]
+  const int32_t* seq_lens;  // [B]
+  int num_blocks, num_kv_heads, idx_dim, num_seqs, maxb;
+};
+
+struct QView {
+  int nq, hq, hi;
+  const int32_t* q_seq;     // nullable: query i -> sequence i
+  const int32_t* q_pos;     // nullable: seq_lens[s] - 1
+  const uint16_t* q;        // bf16 [Nq, Hq, 128]
+  const uint16_t* q_idx;    // bf16 [Nq, HI, dI]
+  const float* w;           // [Nq, HI]
+};
+
+// Per-query (sequence, position, local block) resolution shared by kernels.
+__host__ __device__ inline int query_seq(const QView& q, int i) { return q.q_seq ? q.q_seq[i] : i; }
+
+hipError_t launch_index_score(const KvView& kv, const QView& q, float* scores, hipStream_t s);
+hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, int top_k,
+                       int32_t* idx, int32_t* cnt, hipStream_t s);
+
+// Split-K sparse attention.  num_splits == 1 writes out/lse directly;
+// otherwise partial softmax states go to `partials` and a merge pass follows.
+int attn_num_splits(int nq, int hkv, int top_k, bool prefill);
+size_t attn_partials_bytes(int nq, int hq, int splits);
+hipError_t launch_sparse_attn(const KvView& kv, const QView& q, const int32_t* idx,
+                              const int32_t* cnt, int top_k, float scale, float* out, float* lse,
+                              float* partials, int splits, hipStream_t s);
+
+}  // namespace dsa

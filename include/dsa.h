@@ -1,0 +1,205 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) dynamic sparse attention library.
+ *
+ * Query-driven dynamic sparse attention over a paged (block-managed) KV cache:
+ * every query scores one coarse FP8 key per KV block, keeps the Top-K blocks
+ * and runs exact softmax attention over the gathered K/V of those blocks only.
+ *
+ * Sources (the operations below restate what these pages describe):
+ *   [P1] "Day-0 Adaptation for Massive LLMs: Overcoming Sparse Attention and
+ *        MXFP4 Expert Weights" (intl.cloud.baidu.com/en/article/9584108)
+ *   [P3] "Day-0 Adaptation for Trillion-Parameter Models: Engineering
+ *        Practices and Technical Breakdown" (.../article/9581058)
+ *   [P4] "Day-0 Adaptation for Large Language Models: From Architecture
+ *        Analysis to Inference Serving" (.../article/9584606)
+ *   [P5] "Day-0 Readiness for Trillion-Parameter Models: Engineering Sparse
+ *        Attention and Expert Weight Compression" (.../article/9576887)
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *     The library never allocates, frees, copies host<->device or
+ *     synchronizes; it only enqueues kernels on `stream` (NULL = the default
+ *     stream).  Results are valid once the stream reaches them.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a negative dsa_status and enqueues nothing.
+ *     dsa_last_error() then holds a thread-local message.  A failed launch
+ *     returns DSA_ERR_HIP with the HIP error text in dsa_last_error().
+ *   - Device data (table entries, lengths, positions) is trusted: block
+ *     table entries of visible blocks must lie in [0, num_blocks),
+ *     seq_lens[s] <= max_blocks_per_seq * block_size, q_pos < seq_lens[q_seq],
+ *     and all floating inputs must be finite.  Violations are undefined.
+ *   - Entry points keep no state between calls and are thread-safe; calls
+ *     sharing a workspace buffer must be ordered on one stream.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  DSA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range                */
+  DSA_ERR_UNSUPPORTED = -3, /* a size this build has no kernel for               */
+  DSA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented            */
+  DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than dsa_workspace_size */
+  DSA_ERR_HIP = -6          /* the HIP runtime reported an error                 */
+} dsa_status;
+
+/*
+ * One layer of the paged KV cache ([P5] "KV Cache Layout":
+ * [block_id][token_in_block][head][dim], reached through a block table that
+ * maps each sequence's logical block j to a physical block), together with
+ * the coarse per-block index keys used for block selection ([P1] section
+ * 4(2): compressed index blocks kept apart from the fine-grained KV blocks).
+ */
+typedef struct {
+  const void* k_cache;         /* bf16 [num_blocks, block_size, num_kv_heads, head_dim], 16 B aligned */
+  const void* v_cache;         /* bf16, same shape as k_cache, 16 B aligned                           */
+  const uint8_t* idx_keys;     /* E4M3 (OCP, bias 7, max 448) codes [num_blocks, idx_dim], 16 B aligned */
+  const float* idx_scale;      /* fp32 [num_blocks], > 0: key value = scale * E4M3 value              */
+  const int32_t* block_table;  /* int32 [num_seqs, max_blocks_per_seq]: logical -> physical block    */
+  const int32_t* seq_lens;     /* int32 [num_seqs]: tokens in the cache, current token included      */
+  int32_t num_blocks;          /* physical blocks in the pool, >= 1                                  */
+  int32_t block_size;          /* tokens per block; this build: 64                                  */
+  int32_t num_kv_heads;        /* >= 1                                                               */
+  int32_t head_dim;            /* this build: 128                                                    */
+  int32_t idx_dim;             /* coarse key length: 64 or 128                                       */
+  int32_t num_seqs;            /* >= 1                                                               */
+  int32_t max_blocks_per_seq;  /* row length of block_table, >= 1                                    */
+} dsa_paged_kv;
+
+/*
+ * A batch of queries.  Decode: q_seq == NULL means query i belongs to
+ * sequence i (num_queries <= num_seqs); q_pos == NULL means each query sits
+ * at the last cached position, seq_lens[s] - 1 (its own K/V already written).
+ * Chunked prefill: q_seq and q_pos give the sequence and absolute position
+ * of every query; the chunk's K/V must already be in the cache.
+ */
+typedef struct {
+  int32_t num_queries;         /* Nq >= 0 (0: every call is a no-op)                                */
+  int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads, Hq / Hkv <= 16                     */
+  int32_t idx_heads;           /* indexer heads HI, 1..16                                            */
+  const int32_t* q_seq;        /* int32 [Nq] or NULL                                                 */
+  const int32_t* q_pos;        /* int32 [Nq] or NULL                                                 */
+  const void* q;               /* bf16 [Nq, Hq, head_dim], 16 B aligned                              */
+  const void* q_idx;           /* bf16 [Nq, HI, idx_dim], 16 B aligned                               */
+  const float* w_idx;          /* fp32 [Nq, HI]: per-query, per-indexer-head weights                 */
+} dsa_queries;
+
+/*
+ * Index scoring ([P1] section 4(1) "Index Selection": score the compressed
+ * representation of every earlier KV block against the query; [P3] section
+ * 4.1 "lightweight scoring"; [P5] "Index Selection Path": low-precision
+ * inputs).  For query q of sequence s at position pos, and each logical block
+ * j with j * block_size <= pos (causal block mask), p = block_table[s][j]:
+ *
+ *   sq[h]   = smallest power of two with max_d |q_idx[q,h,d]| <= 448 sq[h]
+ *   q8[h,:] = E4M3(q_idx[q,h,:] / sq[h]), round to nearest even
+ *   D[h]    = sum_d q8[h,d] * idx_keys[p,d]          (exact)
+ *   S[q,j]  = sum_h w_idx[q,h] * max(0, (sq[h] * idx_scale[p]) * D[h])
+ *
+ * evaluated in float64 in that order and rounded once to fp32.  Columns j of
+ * invisible blocks (j * block_size > pos, or j >= max_blocks_per_seq) are -inf.
+ *
+ * scores: fp32 [num_queries, max_blocks_per_seq], 4 B aligned, written whole.
+ * Needs idx_keys, idx_scale, block_table, seq_lens, q_idx, w_idx.
+ */
+dsa_status dsa_index_score(const dsa_paged_kv* kv, const dsa_queries* qs, float* scores,
+                           hipStream_t stream);
+
+/*
+ * Top-K block selection ([P1] section 4(1): Top-K relevant blocks, no full
+ * sort; [P5] "Index Selection Path": index order must match the downstream
+ * gather; padding for ragged selections, [P1] section 4(1)).  For each query
+ * the local block l = pos / block_size is always kept; the other top_k - 1
+ * are the visible blocks j < l with the largest scores[q, j], equal scores
+ * going to the lower j (-0.0 == +0.0).  Output in ascending logical block id
+ * (so l is last), padded with -1 to top_k; block_cnt[q] = min(top_k, l + 1).
+ *
+ * scores: fp32 [Nq, max_blocks_per_seq] as written by dsa_index_score.
+ * block_idx: int32 [Nq, top_k]; block_cnt: int32 [Nq].  1 <= top_k <= 4096.
+ * Needs block_table (unused), seq_lens, and q_pos/q_seq if given.
+ */
+dsa_status dsa_topk_blocks(const float* scores, const dsa_paged_kv* kv, const dsa_queries* qs,
+                           int32_t top_k, int32_t* block_idx, int32_t* block_cnt,
+                           hipStream_t stream);
+
+/*
+ * Sparse attention of decode queries over their selected blocks ([P1]
+ * section 4(3): gather the selected blocks, then sparse attention; [P4]
+ * full-vs-sparse table: only index-selected pairs).  For each query head h
+ * with KV head g = h / (Hq / Hkv), over the tokens t of the selected logical
+ * blocks block_idx[q, 0 .. block_cnt[q]) whose position j*bs + t is <= pos
+ * and < seq_len:
+ *
+ *   x_t = softmax_scale * <q[q,h,:], K[p_j, t, g, :]>
+ *   out[q,h,:] = sum_t e^(x_t - m) V[p_j, t, g, :] / sum_t e^(x_t - m),
+ *   lse[q,h]   = m + ln sum_t e^(x_t - m)                 (m = max_t x_t)
+ *
+ * The selected blocks are split across workgroups and the partial softmax
+ * states are merged in a final pass.  block_idx entries must be visible
+ * logical ids or -1 beyond block_cnt; the local block must be among them.
+ * out: fp32 [Nq, Hq, head_dim]; lse: fp32 [Nq, Hq] or NULL.
+ * workspace: device buffer of at least dsa_workspace_size(DSA_OP_ATTN_DECODE)
+ * bytes, 256 B aligned (may be NULL when that size is 0).
+ */
+dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                  const int32_t* block_idx, const int32_t* block_cnt,
+                                  int32_t top_k, float softmax_scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sparse attention of a chunk of prefill queries ([P3] section 4.3 and [P5]
+ * "Differentiated Adaptation of Prefill and Decode": the prefill path is
+ * compute-bound and batches many queries).  Same result as
+ * dsa_sparse_attn_decode; q_seq and q_pos are required.  No workspace.
+ */
+dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                   const int32_t* block_idx, const int32_t* block_cnt,
+                                   int32_t top_k, float softmax_scale, float* out, float* lse,
+                                   hipStream_t stream);
+
+/*
+ * One-call decode ([P5] "Differentiated Adaptation of Prefill and Decode":
+ * fuse index selection, gather and attention in decode): dsa_index_score,
+ * dsa_topk_blocks and dsa_sparse_attn_decode in one entry point with the
+ * same results.  block_idx_out / block_cnt_out (nullable) receive the
+ * selection.  workspace: at least dsa_workspace_size(DSA_OP_DECODE_FUSED).
+ */
+dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                                   float softmax_scale, float* out, float* lse,
+                                   int32_t* block_idx_out, int32_t* block_cnt_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Scoring and selection in one entry point ([P3] section 4.1: top-k fused
+ * with the scoring before it to avoid materialising intermediate tensors).
+ * Same block_idx / block_cnt as dsa_index_score followed by dsa_topk_blocks.
+ * workspace: at least dsa_workspace_size(DSA_OP_INDEX_TOPK) bytes.
+ */
+dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                          int32_t* block_idx, int32_t* block_cnt, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace sizes.  op: one of the DSA_OP_* values. */
+enum { DSA_OP_ATTN_DECODE = 1, DSA_OP_DECODE_FUSED = 2, DSA_OP_INDEX_TOPK = 3 };
+dsa_status dsa_workspace_size(int op, const dsa_paged_kv* kv, const dsa_queries* qs,
+                              int32_t top_k, size_t* bytes);
+
+const char* dsa_status_str(dsa_status s);
+const char* dsa_last_error(void); /* thread-local; "" after a successful call */
+int dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

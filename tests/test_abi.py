@@ -1,0 +1,117 @@
+"""The C ABI on the host: the library loads, exports every symbol that
+include/dsa.h declares, and rejects invalid arguments before touching the
+GPU (these calls never reach a kernel launch, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_sparse_attention_paged_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libdsa.so not built: run __graft_entry__.build()")
+    return _lib.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_lib.EXPORTS) == set(names)
+    assert lib.dsa_abi_version() == 1
+
+
+FAKE = 0x10000  # a 64 KiB-aligned non-NULL address: never dereferenced on the host
+
+
+def _kv(**over):
+    f = dict(k_cache=FAKE, v_cache=FAKE, idx_keys=FAKE, idx_scale=FAKE, block_table=FAKE,
+             seq_lens=FAKE, num_blocks=10, block_size=64, num_kv_heads=2, head_dim=128,
+             idx_dim=128, num_seqs=2, max_blocks_per_seq=5)
+    f.update(over)
+    return _lib.PagedKVStruct(**f)
+
+
+def _qs(**over):
+    f = dict(num_queries=2, num_q_heads=8, idx_heads=4, q_seq=None, q_pos=None, q=FAKE,
+             q_idx=FAKE, w_idx=FAKE)
+    f.update(over)
+    return _lib.QueriesStruct(**f)
+
+
+def _score(lib, kv, qs, scores=FAKE):
+    return lib.dsa_index_score(ctypes.byref(kv), ctypes.byref(qs), scores, None)
+
+
+def _attn(lib, kv, qs, top_k=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
+    return lib.dsa_sparse_attn_decode(ctypes.byref(kv), ctypes.byref(qs), FAKE, FAKE, top_k,
+                                      0.1, out, None, ws, ws_bytes, None)
+
+
+def test_validation_errors(lib):
+    E = {v: k for k, v in _lib.STATUS.items()}
+    assert lib.dsa_index_score(None, None, FAKE, None) == E["DSA_ERR_NULL"]
+    assert "NULL" in lib.dsa_last_error().decode()
+    assert _score(lib, _kv(block_size=128), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+    assert _score(lib, _kv(head_dim=64), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+    assert _score(lib, _kv(idx_dim=96), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+    assert _score(lib, _kv(), _qs(idx_heads=17)) == E["DSA_ERR_UNSUPPORTED"]
+    assert _score(lib, _kv(idx_keys=None), _qs()) == E["DSA_ERR_NULL"]
+    assert _score(lib, _kv(idx_keys=FAKE + 8), _qs()) == E["DSA_ERR_ALIGN"]
+    assert _score(lib, _kv(), _qs(), scores=None) == E["DSA_ERR_NULL"]
+    assert _score(lib, _kv(), _qs(num_queries=3)) == E["DSA_ERR_SHAPE"]  # decode: Nq > seqs
+    assert _score(lib, _kv(num_blocks=0), _qs()) == E["DSA_ERR_SHAPE"]
+    assert _attn(lib, _kv(), _qs(num_q_heads=7)) == E["DSA_ERR_SHAPE"]  # Hq % Hkv
+    assert _attn(lib, _kv(num_kv_heads=1), _qs(num_q_heads=32)) == E["DSA_ERR_UNSUPPORTED"]
+    assert _attn(lib, _kv(), _qs(), top_k=0) == E["DSA_ERR_SHAPE"]
+    assert _attn(lib, _kv(), _qs(), top_k=5000) == E["DSA_ERR_SHAPE"]
+    assert _attn(lib, _kv(k_cache=FAKE + 2), _qs()) == E["DSA_ERR_ALIGN"]
+    assert _attn(lib, _kv(), _qs(), out=None) == E["DSA_ERR_NULL"]
+    assert lib.dsa_sparse_attn_prefill(ctypes.byref(_kv()), ctypes.byref(_qs()), FAKE, FAKE, 4,
+                                       0.1, FAKE, None, None) == E["DSA_ERR_NULL"]  # q_seq/q_pos
+
+
+def test_workspace_contract(lib):
+    E = {v: k for k, v in _lib.STATUS.items()}
+    kv, qs = _kv(), _qs()
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_workspace_size(_lib.OP_DECODE_FUSED, ctypes.byref(kv), ctypes.byref(qs), 4,
+                                  ctypes.byref(n)) == 0
+    assert n.value > 0
+    st = lib.dsa_sparse_decode_fused(ctypes.byref(kv), ctypes.byref(qs), 4, 0.1, FAKE, None, None,
+                                     None, FAKE, n.value - 1, None)
+    assert st == E["DSA_ERR_WORKSPACE"]
+    st = lib.dsa_sparse_decode_fused(ctypes.byref(kv), ctypes.byref(qs), 4, 0.1, FAKE, None, None,
+                                     None, FAKE + 64, n.value, None)
+    assert st == E["DSA_ERR_ALIGN"]
+    m = ctypes.c_size_t(0)
+    assert lib.dsa_workspace_size(_lib.OP_INDEX_TOPK, ctypes.byref(kv), ctypes.byref(qs), 4,
+                                  ctypes.byref(m)) == 0
+    assert m.value >= 2 * 5 * 4
+    assert lib.dsa_workspace_size(99, ctypes.byref(kv), ctypes.byref(qs), 4,
+                                  ctypes.byref(m)) == E["DSA_ERR_SHAPE"]
+
+
+def test_empty_batch_is_a_noop(lib):
+    # Nq == 0 returns DSA_OK without launching anything (no GPU needed)
+    assert _score(lib, _kv(), _qs(num_queries=0)) == 0
+    assert _attn(lib, _kv(), _qs(num_queries=0)) == 0
+    assert lib.dsa_last_error().decode() == ""
+
+
+def test_status_strings(lib):
+    for s in _lib.STATUS:
+        assert lib.dsa_status_str(s)

@@ -1,0 +1,174 @@
+"""GPU parity: the HIP library against the float64 oracle on seeded inputs.
+
+Each stage is checked in isolation (scoring on its own; Top-K fed the
+oracle's scores; attention fed the oracle's indices) and end to end.
+Scores must equal the oracle's float64 score rounded to fp32 bit for bit;
+indices must be identical (swaps only among oracle scores within 1e-6
+relative); attention within 2e-3 max-abs and 1e-2 max-rel (|oracle| >= 0.2).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from dsa_synth import workload
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as m
+    m._lib.load()  # must be the HIP library; raises if not built
+    return m
+
+
+SMALL_DECODE_CASES = [
+    dict(seed=2001),  # ragged lens incl. 1 and 64 tokens, Hq 16 / Hkv 2, HI 4 x 128, K 8
+    dict(seed=2002, hq=8, hkv=1, hi=4, di=64, top_k=8, lens=(4096, 64 * 9 + 3, 130)),
+    dict(seed=2003, hq=64, hkv=8, hi=8, di=128, top_k=32, lens=(64 * 70, 64 * 33 - 5, 64 * 31)),
+    dict(seed=2004, hq=4, hkv=4, hi=1, di=128, top_k=1, lens=(700, 64, 1)),
+    dict(seed=2005, hq=32, hkv=2, hi=16, di=64, top_k=200, lens=(64 * 150 + 1, 64 * 199)),
+    dict(seed=2006, hq=12, hkv=3, hi=3, di=128, top_k=5, lens=(64 * 40 - 1, 64 * 6)),
+]
+
+
+def _run_all_stages(dsa, w, label):
+    kv, qs = parity.to_device(w)
+    maxb = w.block_table.shape[1]
+    K = w.top_k
+    scores = dsa.index_score(kv, qs)
+    idx, cnt = dsa.topk_blocks(scores, kv, qs, K)
+    out, lse = dsa.sparse_attn_decode(kv, qs, idx, cnt, K, w.softmax_scale) if w.decode else \
+        dsa.sparse_attn_prefill(kv, qs, idx, cnt, K, w.softmax_scale)
+    torch.cuda.synchronize()
+    scores_h = scores.cpu().numpy()
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+
+    # stage-isolated runs: Top-K on the oracle's scores, attention on the oracle's indices
+    refs = [parity.oracle_query(w, qi) for qi in range(w.num_queries)]
+    ref_scores = np.full((w.num_queries, maxb), -np.inf, dtype=np.float32)
+    ref_idx = np.stack([r["idx"] for r in refs]).astype(np.int32)
+    ref_cnt = np.array([r["cnt"] for r in refs], dtype=np.int32)
+    for qi, r in enumerate(refs):
+        ref_scores[qi, r["cand"]] = r["scores"].astype(np.float32)
+    idx2, cnt2 = dsa.topk_blocks(torch.from_numpy(ref_scores).cuda(), kv, qs, K)
+    ri, rc = torch.from_numpy(ref_idx).cuda(), torch.from_numpy(ref_cnt).cuda()
+    out2, lse2 = dsa.sparse_attn_decode(kv, qs, ri, rc, K, w.softmax_scale) if w.decode else \
+        dsa.sparse_attn_prefill(kv, qs, ri, rc, K, w.softmax_scale)
+    torch.cuda.synchronize()
+
+    worst = (0.0, 0.0)
+    for qi, r in enumerate(refs):
+        bad = parity.check_scores_exact(scores_h[qi], r, maxb)
+        assert bad.size == 0, f"{label} q{qi}: scores differ at {bad[:8]}"
+        assert np.array_equal(idx2[qi].cpu().numpy(), r["idx"]), f"{label} q{qi}: topk(oracle scores)"
+        assert int(cnt2[qi]) == r["cnt"]
+        ok, _ = parity.check_indices(idx_h[qi], cnt_h[qi], r, K)
+        assert ok, f"{label} q{qi}: idx {idx_h[qi]} cnt {cnt_h[qi]} vs {r['idx']} {r['cnt']}"
+        for o, l in ((out_h[qi], lse_h[qi]), (out2[qi].cpu().numpy(), lse2[qi].cpu().numpy())):
+            good, a, rel = parity.attn_ok(o, r["out"])
+            assert good, f"{label} q{qi}: attention max-abs {a:.3e} max-rel {rel:.3e}"
+            la, _ = parity.attn_errors(l, r["lse"])
+            assert la <= 1e-3, f"{label} q{qi}: lse max-abs {la:.3e}"
+            worst = (max(worst[0], a), max(worst[1], rel))
+    _say(f"{label}: {w.num_queries} queries ok; worst attention max-abs {worst[0]:.2e} "
+         f"max-rel {worst[1]:.2e}")
+    return kv, qs, refs
+
+
+@pytest.mark.parametrize("case", SMALL_DECODE_CASES, ids=[str(c["seed"]) for c in SMALL_DECODE_CASES])
+def test_small_decode_stages(dsa, case):
+    w = workload.small_decode(**case)
+    _say(f"small_decode {case}")
+    kv, qs, refs = _run_all_stages(dsa, w, f"small_decode[{case['seed']}]")
+    # fused entry point: same results
+    K = w.top_k
+    bi = torch.empty(w.num_queries, K, dtype=torch.int32, device="cuda")
+    bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, K, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    bi2, bc2 = dsa.index_topk(kv, qs, K)
+    torch.cuda.synchronize()
+    for qi, r in enumerate(refs):
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        assert np.array_equal(bi2[qi].cpu().numpy(), r["idx"]) and int(bc2[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"fused q{qi}: {a:.3e} {rel:.3e}"
+
+
+@pytest.mark.parametrize("seed,count,L,top_k", [(2101, 200, 64 * 20 - 5, 6),
+                                                (2102, 130, 64 * 3 + 1, 2),
+                                                (2103, 257, 64 * 40, 64)])
+def test_small_prefill_stages(dsa, seed, count, L, top_k):
+    w = workload.small_prefill(seed=seed, count=count, L=L, top_k=top_k)
+    _say(f"small_prefill seed={seed} count={count} L={L} K={top_k}")
+    _run_all_stages(dsa, w, f"small_prefill[{seed}]")
+
+
+def test_tiny_decode_config(dsa):
+    w = workload.tiny_decode()
+    _say("tiny_decode (1 x 4096, K 8)")
+    kv, qs, refs = _run_all_stages(dsa, w, "tiny_decode")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    good, a, rel = parity.attn_ok(out[0].cpu().numpy(), refs[0]["out"])
+    assert good
+
+
+def test_device_filler_matches_host_generator(dsa):
+    from dsa_synth import gen
+    w = workload.small_decode(seed=2001)
+    kv, _ = parity.to_device(w)
+    k = kv.k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    v = kv.v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(k, w.pool_bits(gen.TAG_K))
+    assert np.array_equal(v, w.pool_bits(gen.TAG_V))
+
+
+def test_dense_equivalence_when_k_covers_everything(dsa):
+    """Top-K >= visible blocks: the sparse result is dense causal attention."""
+    from oracle import dense_attention, bf16_bits_to_f64
+    w = workload.small_decode(seed=2011, lens=(64 * 12 - 7, 64 * 5, 33), top_k=16)
+    kv, qs = parity.to_device(w)
+    out, lse, _, _ = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    for qi in range(w.num_queries):
+        s, pos, L = int(w.q_seq[qi]), int(w.q_pos[qi]), int(w.seq_lens[qi])
+        ref, _ = dense_attention(bf16_bits_to_f64(w.q_bits[qi]), w.block_table[s], pos, L, 64,
+                                 lambda p: bf16_bits_to_f64(w.k_block_bits(p)),
+                                 lambda p: bf16_bits_to_f64(w.v_block_bits(p)),
+                                 w.softmax_scale, w.num_kv_heads)
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), ref)
+        assert good, (qi, a, rel)
+
+
+def test_v_one_gives_one(dsa):
+    """Softmax weights sum to one: with V == 1 every output is 1."""
+    w = workload.small_decode(seed=2012)
+    kv, qs = parity.to_device(w)
+    kv.v_cache.fill_(1.0)
+    out, _, _, _ = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(out - 1.0)).item() <= 1e-5
+
+
+def test_run_to_run_bit_determinism(dsa):
+    w = workload.small_decode(seed=2013, hq=64, hkv=8, hi=8, top_k=32,
+                              lens=(64 * 300, 64 * 280 + 9, 64 * 77))
+    kv, qs = parity.to_device(w)
+    a = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)[0].clone()
+    b = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)[0].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
