@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Throughput of the dynamic-sparse-attention hot path on one MI355X.
+
+A step is one pass of the whole decode hot path -- block-table walk, FP8
+indexer scoring, Top-K selection, gather + split-K attention and merge --
+through the fused entry point, over one batch of 32 decode queries with a
+32768-token paged context each (64-token blocks, 64 query / 8 KV heads of
+128, indexer 8 x 128 E4M3, Top-K 32).  Inputs are resident in HBM before the
+timed region.  Distinct query batches rotate over the same cache so that
+consecutive steps select different blocks (the 256 MiB last-level cache
+cannot serve a step from the previous one).
+
+Printed: one JSON line with queries/s, the roofline of the dominant kernel
+(sparse attention: HBM bytes per launch / its HIP-event duration), and the
+oracle timed on the host on a bounded sample.  Extra fields report the other
+workloads (tiny, ragged, million-token decode; the chunked-prefill indexer).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/sec + achieved HBM GB/s (% roofline); prefill indexer MFMA %"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_split_batched_decode.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_bytes(w, cnt):
+    """Algorithmic HBM bytes of the attention kernel for one launch over the batch:
+    whole selected K+V blocks of each KV head, the selected ids and their table
+    entries, Q (bf16), out (fp32) and lse (fp32)."""
+    blk = w.block_size * w.num_kv_heads * w.head_dim * 2 * 2
+    per_q_fixed = w.num_q_heads * w.head_dim * (2 + 4) + w.num_q_heads * 4 + 4
+    return int(sum(int(c) * (blk + 8) for c in cnt)) + w.num_queries * per_q_fixed
+
+
+def index_bytes(w):
+    """Algorithmic bytes of the block-table walk + scoring: per visible block a
+    table entry, a coarse key row and a scale; per query q_idx (bf16) and w."""
+    tot = 0
+    for qi in range(w.num_queries):
+        nvis = int(w.q_pos[qi]) // w.block_size + 1
+        tot += nvis * (4 + w.idx_dim + 4) + w.idx_heads * (w.idx_dim * 2 + 4) + 4
+    return tot
+
+
+def index_flops(w):
+    return sum(2 * w.idx_heads * w.idx_dim * (int(p) // w.block_size + 1) for p in w.q_pos)
+
+
+class Device:
+    """One workload on the device, with `nsets` rotating query batches."""
+
+    def __init__(self, w, nsets, qseed0=5000):
+        import torch
+        import dynamic_sparse_attention_paged_amd as dsa
+        from dsa_synth import device as synth_dev, workload
+
+        self.w = w
+        t = synth_dev.upload(w)
+        self.kv = dsa.PagedKV(t["k_cache"], t["v_cache"], t["idx_keys"], t["idx_scale"],
+                              t["block_table"], t["seq_lens"])
+        self.sets = [dsa.Queries(t["q"], t["q_idx"], t["w_idx"], t["q_seq"], t["q_pos"])]
+        self.hosts = [w]
+        for i in range(1, nsets):
+            v = workload.with_query_seed(w, qseed0 + i)
+            self.hosts.append(v)
+
+            def dev(a, dtype=None):
+                import numpy as np
+                x = torch.from_numpy(np.ascontiguousarray(a))
+                return (x.view(dtype) if dtype is not None else x).cuda()
+            import numpy as np
+            self.sets.append(dsa.Queries(dev(v.q_bits.view(np.int16), torch.bfloat16),
+                                         dev(v.q_idx_bits.view(np.int16), torch.bfloat16),
+                                         dev(v.w), t["q_seq"], t["q_pos"]))
+        nq, hq = w.num_queries, w.num_q_heads
+        self.out = torch.empty(nq, hq, w.head_dim, dtype=torch.float32, device="cuda")
+        self.lse = torch.empty(nq, hq, dtype=torch.float32, device="cuda")
+        self.idx = [torch.empty(nq, w.top_k, dtype=torch.int32, device="cuda") for _ in self.sets]
+        self.cnt = [torch.empty(nq, dtype=torch.int32, device="cuda") for _ in self.sets]
+        from dynamic_sparse_attention_paged_amd import _lib
+        op = _lib.OP_DECODE_FUSED if w.decode else _lib.OP_INDEX_TOPK
+        self.ws = dsa.make_workspace(op, self.kv, self.sets[0], w.top_k)
+        self.ws_attn = dsa.make_workspace(_lib.OP_ATTN_DECODE, self.kv, self.sets[0], w.top_k)
+        self.scores = torch.empty(nq, w.block_table.shape[1], dtype=torch.float32, device="cuda")
+        self.dsa = dsa
+
+    def fused(self, i, with_idx=False):
+        s = i % len(self.sets)
+        self.dsa.decode_fused(self.kv, self.sets[s], self.w.top_k, self.w.softmax_scale,
+                              out=self.out, lse=self.lse,
+                              block_idx=self.idx[s] if with_idx else None,
+                              block_cnt=self.cnt[s] if with_idx else None, workspace=self.ws)
+
+    def select(self):
+        for s in range(len(self.sets)):
+            self.dsa.index_topk(self.kv, self.sets[s], self.w.top_k, block_idx=self.idx[s],
+                                block_cnt=self.cnt[s], workspace=self.ws)
+
+    def attn(self, i):
+        s = i % len(self.sets)
+        if self.w.decode:
+            self.dsa.sparse_attn_decode(self.kv, self.sets[s], self.idx[s], self.cnt[s],
+                                        self.w.top_k, self.w.softmax_scale, out=self.out,
+                                        lse=self.lse, workspace=self.ws_attn)
+        else:
+            self.dsa.sparse_attn_prefill(self.kv, self.sets[s], self.idx[s], self.cnt[s],
+                                         self.w.top_k, self.w.softmax_scale, out=self.out,
+                                         lse=self.lse)
+
+    def score(self, i):
+        s = i % len(self.sets)
+        self.dsa.index_score(self.kv, self.sets[s], scores=self.scores)
+
+    def topk(self, i):
+        s = i % len(self.sets)
+        self.dsa.topk_blocks(self.scores, self.kv, self.sets[s], self.w.top_k,
+                             block_idx=self.idx[s], block_cnt=self.cnt[s])
+
+
+def event_time_ms(fn, n, warmup):
+    """Average HIP-event time (ms) of fn(i) over n calls on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def traffic_from_profile():
+    """Measured HBM bytes per launch of the attention kernel, if the counters in
+    profiles/ were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if t.get("attn_src_sha256") != src:
+            return None
+        return t.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle on the host: scoring + selection + attention for as many queries
+    of the batch as fit in ~budget_s (K/V generation excluded from the timing)."""
+    import numpy as np
+    from oracle import bf16_bits_to_f64, select_blocks, sparse_attention
+    from oracle.pipeline import score_query
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    spent, done = 0.0, 0
+    for qi in range(w.num_queries):
+        s, pos = int(w.q_seq[qi]), int(w.q_pos[qi])
+        L = int(w.seq_lens[s])
+        qidx = bf16_bits_to_f64(w.q_idx_bits[qi])
+        t0 = time.perf_counter()
+        cand, sc, loc = score_query(qidx, w.w[qi], w.block_table[s], pos, L, w.block_size,
+                                    w.idx_keys, w.idx_scale)
+        idx, cnt = select_blocks(cand, sc.astype(np.float32), loc, w.top_k)
+        t1 = time.perf_counter()
+        blocks = {int(w.block_table[s][j]): (bf16_bits_to_f64(w.k_block_bits(int(w.block_table[s][j]))),
+                                             bf16_bits_to_f64(w.v_block_bits(int(w.block_table[s][j]))))
+                  for j in idx[:cnt]}
+        t2 = time.perf_counter()
+        sparse_attention(bf16_bits_to_f64(w.q_bits[qi]), idx[:cnt], w.block_table[s], pos, L,
+                         w.block_size, lambda p: blocks[p][0], lambda p: blocks[p][1],
+                         w.softmax_scale, w.num_kv_heads)
+        t3 = time.perf_counter()
+        spent += (t1 - t0) + (t3 - t2)
+        done += 1
+        if spent >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return dict(value=done / spent, unit="queries/s", cores=1, kind="oracle",
+                sample=f"{done} of {w.num_queries} queries of {w.name} (float64 NumPy, "
+                       f"1 thread; K/V regeneration not timed)", seconds=round(spent, 2))
+
+
+def decode_extra(w, steps, nsets):
+    """q/s and HBM GB/s of a decode workload through the fused entry point."""
+    import torch
+    D = Device(w, nsets)
+    ms = event_time_ms(D.fused, steps, 3)
+    D.select()
+    torch.cuda.synchronize()
+    attn_ms = event_time_ms(D.attn, steps, 3)
+    cnt = D.cnt[0].cpu().numpy()
+    byts = attn_bytes(w, cnt) + index_bytes(w)
+    res = dict(workload=w.name, queries=w.num_queries, ms_per_step=round(ms, 5),
+               queries_per_s=round(w.num_queries / (ms * 1e-3), 1),
+               path_gbps=round(byts / (ms * 1e-3) / 1e9, 1),
+               path_frac_of_hbm=round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               attn_kernel_ms=round(attn_ms, 5),
+               attn_kernel_gbps=round(attn_bytes(w, cnt) / (attn_ms * 1e-3) / 1e9, 1))
+    del D
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_indexer_extra(steps):
+    """Chunked-prefill indexer: TFLOP/s and fraction of the FP8 MFMA peak."""
+    import torch
+    from dsa_synth import workload
+    w = workload.chunked_prefill()
+    D = Device(w, 1)
+    ms = event_time_ms(D.score, steps, 2)
+    fl = index_flops(w)
+    tk_ms = event_time_ms(D.topk, steps, 2)
+    at_ms = event_time_ms(D.attn, max(2, steps // 4), 1)
+    res = dict(workload=w.name, score_kernel_ms=round(ms, 4),
+               algorithmic_gflop=round(fl / 1e9, 3),
+               tflops=round(fl / (ms * 1e-3) / 1e12, 2),
+               frac_of_fp8_mfma_peak=round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+               note="scoring runs exact float64 FMAs (FP8 MFMA accumulation is inexact on "
+                    "gfx950); fraction is against the FP8 dense peak",
+               topk_ms=round(tk_ms, 4), attention_ms=round(at_ms, 3))
+    del D
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--query-sets", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from dsa_synth import workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = workload.batched_decode()
+    log(f"workload {w.name}: pool {w.num_blocks} blocks, {args.query_sets} query sets")
+    D = Device(w, args.query_sets)
+
+    # timed region: K fused steps, inputs resident
+    for i in range(args.warmup):
+        D.fused(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        D.fused(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    log(f"fused step {ms_step * 1e3:.1f} us")
+
+    # dominant kernel (attention) on the same stream, HIP events over the loop
+    D.select()
+    torch.cuda.synchronize()
+    attn_ms = event_time_ms(D.attn, args.steps, 3)
+    score_ms = event_time_ms(D.score, args.steps, 3)
+    topk_ms = event_time_ms(D.topk, args.steps, 3)
+    cnt = D.cnt[0].cpu().numpy()
+    a_bytes = attn_bytes(w, cnt)
+    path_bytes = a_bytes + index_bytes(w)
+    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.num_queries / (ms_step * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.num_queries, "context_tokens": 32768,
+                   "block_size": 64, "q_heads": 64, "kv_heads": 8, "head_dim": 128,
+                   "idx_heads": 8, "idx_dim": 128, "top_k": w.top_k,
+                   "query_sets": args.query_sets, "entry": "dsa_sparse_decode_fused"},
+        "hbm_gbps": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "sparse_attn_split", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "bytes_per_launch": a_bytes,
+                     "avg_launch_ms": round(attn_ms, 5)},
+        "stages_ms": {"index_score": round(score_ms, 5), "topk": round(topk_ms, 5),
+                      "sparse_attn": round(attn_ms, 5)},
+    }
+    del D
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        extras = {}
+        for name, fn, steps in (("tiny_decode", workload.tiny_decode, 200),
+                                ("million_decode", workload.million_decode, 50),
+                                ("ragged_decode", workload.ragged_decode, 20)):
+            log(f"extra: {name}")
+            extras[name] = decode_extra(fn(), steps, 4 if name != "tiny_decode" else 8)
+        log("extra: chunked_prefill indexer")
+        extras["chunked_prefill"] = prefill_indexer_extra(5)
+        result["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

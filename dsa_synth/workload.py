@@ -236,3 +236,16 @@ def small_prefill(seed=2101, L=64 * 20 - 5, count=200, hq=16, hkv=2, hi=4, di=12
     perm = gen.permutation(seed, gen.TAG_TABLE, P)
     return build(f"small_prefill_s{seed}", seed, [L], perm[None, :nb], P, hq=hq, hkv=hkv,
                  hi=hi, di=di, top_k=top_k, prefill=(0, L - count, count))
+
+
+def with_query_seed(w, qseed):
+    """A copy of ``w`` whose queries (q, q_idx, w) come from stream seed ``qseed``;
+    the cache, keys and tables are shared.  Used to rotate distinct query batches
+    over one cache so that consecutive steps select different blocks."""
+    import copy
+    q, qi, ww = _queries(qseed, w.num_queries, w.num_q_heads, w.head_dim, w.idx_heads,
+                         w.idx_dim)
+    v = copy.copy(w)
+    v.q_bits, v.q_idx_bits, v.w = q, qi, ww
+    v.meta = dict(w.meta, query_seed=qseed)
+    return v

@@ -20,7 +20,7 @@ from . import _lib
 
 __all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
            "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "index_topk",
-           "workspace_size", "abi_version"]
+           "workspace_size", "make_workspace", "abi_version"]
 
 
 class DSAError(RuntimeError):
@@ -110,7 +110,13 @@ def workspace_size(op, kv, qs, top_k):
 
 
 def _workspace(nbytes, device):
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    # zero-filled once: the library keeps its ticket counters at zero between calls
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def make_workspace(op, kv, qs, top_k):
+    """A zero-filled workspace for ``op`` (reusable across calls with the same sizes)."""
+    return _workspace(workspace_size(op, kv, qs, top_k), kv.block_table.device)
 
 
 def index_score(kv, qs, scores=None):

@@ -25,6 +25,7 @@
 // with the usual max / rescale rule; logits are kept in base 2.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include "dsa_internal.h"
 
@@ -37,7 +38,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kVRow = 132;  // LDS row of V in uint16: 128 dims + 4 pad (264 B)
+constexpr int kNumCUs = 256;   // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -61,30 +62,44 @@ struct WaveState {
   f32x4 o[8];   // O^T tiles: o[dt][i] = O[head = lane%16][d = 16 dt + 4 (lane/16) + i]
 };
 
-// Process one selected block for one wave.
-__device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kbase,
-                                             const uint16_t* __restrict__ vbase, int hkv,
-                                             const i16x8 (&qf)[4], float scale2, int tok0,
-                                             int pos, int len, uint16_t* vs, WaveState& st) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, gq = lane >> 4;
-  const size_t tok_stride = (size_t)hkv * kHeadDim;  // elements between consecutive tokens
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-  // K fragments: A operand rows = tokens 16T + r, k = dims 32c + 8gq .. +8
-  i16x8 kf[4][4];
+// V tile of one block and KV head in LDS: 64 token rows of 256 B, no padding.
+// The 16 B chunk c (dims 8c .. 8c+7) of token row t sits in chunk slot
+// c ^ (2 (t & 3)), which makes the transposed reads below bank-conflict free.
+// Loaded straight from global memory into LDS (16 B per lane, lane l of a
+// load landing at LDS offset 16 l), so V takes no registers.
+__device__ __forceinline__ void dma_v(const uint16_t* __restrict__ vbase, size_t tok_stride,
+                                      int lane, uint16_t* vs) {
+  const int row_in = lane >> 4;                 // token within the 4-row group
+  const int chunk = (lane & 15) ^ (2 * row_in);  // data chunk this lane fetches
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const uint16_t* src = vbase + (size_t)(4 * u + row_in) * tok_stride + 8 * chunk;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(vs + 512 * u), 16, 0, 0);
+  }
+}
+
+// K tile as MFMA A operands: k[T][c] = K[token 16T + r][dims 32c + 8gq .. +8]
+__device__ __forceinline__ void load_k(const uint16_t* __restrict__ kbase, size_t tok_stride,
+                                       int r, int gq, i16x8 (&kf)[4][4]) {
 #pragma unroll
   for (int T = 0; T < 4; ++T)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       kf[T][c] = *reinterpret_cast<const i16x8*>(kbase + (size_t)(16 * T + r) * tok_stride +
                                                  32 * c + 8 * gq);
-  // V rows: lane loads dims 8r .. 8r+8 of tokens gq + 4u, u = 0..15
-  i16x8 vr[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u)
-    vr[u] = *reinterpret_cast<const i16x8*>(vbase + (size_t)(gq + 4 * u) * tok_stride + 8 * r);
+}
 
-  // S^T = K . Q^T
+// One selected block for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+__device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x8 (&qf)[4],
+                                             float scale2, int tok0, int pos, int len,
+                                             const uint16_t* vs, WaveState& st) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, gq = lane >> 4;
+
   f32x4 sc[4];
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
@@ -93,15 +108,6 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kbase,
     for (int c = 0; c < 4; ++c) acc = mfma_bf16(kf[T][c], qf[c], acc);
     sc[T] = acc;
   }
-  // stage V in LDS (row-major [token][dim], padded rows); wave-private region
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    uint16_t* dst = vs + (gq + 4 * u) * kVRow + 8 * r;
-    const uint2* src = reinterpret_cast<const uint2*>(&vr[u]);
-    reinterpret_cast<uint2*>(dst)[0] = src[0];
-    reinterpret_cast<uint2*>(dst)[1] = src[1];
-  }
-
   // mask + scale (base 2); sc[T][i] is token 16T + 4gq + i of head r
   float mx = -INFINITY;
 #pragma unroll
@@ -138,35 +144,40 @@ __device__ __forceinline__ void attend_block(const uint16_t* __restrict__ kbase,
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
 
-  // O^T += V^T . P^T ; k-slot (gq, i) <-> token 16 (2 ks + i/4) + 4 gq + i%4
-  // LDS writes of this wave complete and not reordered past the reads below
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
+  // O^T += V^T . P^T.  k-slot s = 4h + i of lane group gq <-> token 16 (2 ks + h) + 4 gq + i.
+  // ds_read_b64_tr_b16: within a 16-lane group, lane 4a+b receives element i
+  // from the 4 u16 at the address of lane 4i+a, offset b.  Lane 4i+a therefore
+  // points at token 16 (2 ks + h) + 4 gq + i, dims 16 dt + 4a .. +3, and lane
+  // (gq, r) receives V[token(s)][16 dt + r] for its four slots.
+  const int ti = (lane >> 2) & 3, ta = lane & 3;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       i16x8 va;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = 16 * (2 * ks + (i >> 2)) + 4 * gq + (i & 3);
-        va[i] = (short)vs[tok * kVRow + 16 * dt + r];
+      for (int h = 0; h < 2; ++h) {
+        const int t = 16 * (2 * ks + h) + 4 * gq + ti;
+        const int slot = 2 * (dt ^ ti) + (ta >> 1);  // chunk (2 dt + ta/2) ^ 2 (t & 3)
+        const uint16_t* a = vs + t * 128 + 8 * slot + 4 * (ta & 1);
+        const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a);
+        va[4 * h + 0] = v4[0];
+        va[4 * h + 1] = v4[1];
+        va[4 * h + 2] = v4[2];
+        va[4 * h + 3] = v4[3];
       }
       st.o[dt] = mfma_bf16(va, ph[ks], st.o[dt]);
       st.o[dt] = mfma_bf16(va, pl[ks], st.o[dt]);
     }
   }
-  // reads done before the next block overwrites vs
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_wave_barrier();
 }
 
-// grid (splits, Hkv, Nq), block 256.  partials: [Nq][Hq][splits] x {m, l, o[128]}
+// grid (splits, Hkv, Nq), block 256.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_split(
     KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ partials) {
-  __shared__ uint16_t vs_all[kAttnWaves][64 * kVRow];
+  __shared__ uint16_t vs_all[kAttnWaves][64 * kHeadDim];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
 
   const int sp = blockIdx.x, g = blockIdx.y, qi = blockIdx.z;
@@ -200,12 +211,34 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_split(
   uint16_t* vs = vs_all[wave];
   const int32_t* sel = idx + (size_t)qi * top_k;
   const int32_t* trow = kv.table + (size_t)s * kv.maxb;
-  for (int b = b0 + wave; b < b1; b += kAttnWaves) {
-    const int j = sel[b];
-    const int p = trow[j];
-    const size_t base = ((size_t)p * kBlockSize * kv.num_kv_heads + g) * kHeadDim;
-    attend_block(kv.k + base, kv.v + base, kv.num_kv_heads, qf, scale2, j * kBlockSize, pos, len,
-                 vs, st);
+  const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
+  const size_t blk_elems = (size_t)kBlockSize * tok_stride;
+
+  // The wave's blocks are b0 + wave + 4 i.  Their logical ids and physical
+  // blocks are fetched up front, one per lane (64 at a time), so that the
+  // loop never waits on a dependent table read before issuing block loads.
+  const int nmine = b1 > b0 + wave ? (b1 - b0 - wave + kAttnWaves - 1) / kAttnWaves : 0;
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int cn = min(64, nmine - c0);
+    int my_j = 0, my_p = 0;
+    if (lane < cn) {
+      my_j = sel[b0 + wave + kAttnWaves * (c0 + lane)];
+      my_p = trow[my_j];
+    }
+    for (int i = 0; i < cn; ++i) {
+      const int j = __builtin_amdgcn_readlane(my_j, i);
+      const int p = __builtin_amdgcn_readlane(my_p, i);
+      const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
+      // previous block's LDS reads are complete before the DMA overwrites vs
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      dma_v(kv.v + base, tok_stride, lane, vs);
+      i16x8 kf[4][4];
+      load_k(kv.k + base, tok_stride, r, gq, kf);
+      __builtin_amdgcn_s_waitcnt(0);  // V in LDS and K in registers
+      __builtin_amdgcn_wave_barrier();
+      attend_block(kf, qf, scale2, j * kBlockSize, pos, len, vs, st);
+    }
   }
 
   // ---- merge the four waves through LDS (reusing the V staging area)
@@ -251,8 +284,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_split(
 
 // grid (Nq * Hq), block 128: merge the split partials of one (query, head).
 __global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict__ partials,
-                                                         int splits, int hq,
-                                                         float* __restrict__ out,
+                                                         int splits, float* __restrict__ out,
                                                          float* __restrict__ lse) {
   const int qh = blockIdx.x;
   const int d = threadIdx.x;
@@ -268,18 +300,23 @@ __global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict
   }
   out[(size_t)qh * kHeadDim + d] = O / L;
   if (lse && d == 0) lse[qh] = (M + log2f(L)) * kLn2;
-  (void)hq;
 }
 
 }  // namespace
 
 int attn_num_splits(int nq, int hkv, int top_k, bool prefill) {
   if (prefill) return 1;
-  // Aim for >= ~2048 workgroups (8 per CU), but keep >= 2 blocks per wave.
+  // Tuning override (same results, different launch shape): DSA_ATTN_SPLITS=n
+  if (const char* e = getenv("DSA_ATTN_SPLITS")) {
+    const int n = atoi(e);
+    if (n >= 1) return n < top_k ? n : top_k;
+  }
+  // Split the selected blocks only as far as needed to give every CU a
+  // workgroup, keeping at least one block per wave.
   const long units = (long)nq * hkv;
   if (units <= 0) return 1;
-  int splits = (int)((2048 + units - 1) / units);
-  const int max_splits = (top_k + 2 * kAttnWaves - 1) / (2 * kAttnWaves);
+  int splits = (int)((kNumCUs + units - 1) / units);
+  const int max_splits = (top_k + kAttnWaves - 1) / kAttnWaves;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   return splits;
@@ -299,7 +336,7 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(merge_splits, dim3(Q.nq * Q.hq), dim3(kHeadDim), 0, st, partials, splits,
-                     Q.hq, out, lse);
+                     out, lse);
   return hipGetLastError();
 }
 

@@ -110,22 +110,36 @@ dsa::QView q_view(const dsa_queries* qs) {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Fused-decode workspace: scores | idx | cnt | attention partials.
-struct FusedLayout {
-  size_t scores, idx, cnt, partials, total;
+// Attention workspace: split partials.
+struct AttnLayout {
+  size_t partials, total;
   int splits;
+};
+
+AttnLayout attn_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k, size_t base) {
+  AttnLayout a;
+  a.splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
+  a.partials = base;
+  a.total = align_up(a.partials + dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads,
+                                                           a.splits));
+  if (a.splits <= 1) a.total = base;
+  return a;
+}
+
+// Fused-decode workspace: attention layout | scores | idx | cnt.
+struct FusedLayout {
+  AttnLayout attn;
+  size_t scores, idx, cnt, total;
 };
 
 FusedLayout fused_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k) {
   FusedLayout f;
   const size_t nq = (size_t)qs->num_queries;
-  f.scores = 0;
+  f.attn = attn_layout(kv, qs, top_k, 0);
+  f.scores = align_up(f.attn.total);
   f.idx = align_up(f.scores + nq * kv->max_blocks_per_seq * sizeof(float));
   f.cnt = align_up(f.idx + nq * top_k * sizeof(int32_t));
-  f.partials = align_up(f.cnt + nq * sizeof(int32_t));
-  f.splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
-  f.total = align_up(f.partials + dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads,
-                                                           f.splits));
+  f.total = align_up(f.cnt + nq * sizeof(int32_t));
   return f;
 }
 
@@ -159,8 +173,7 @@ dsa_status dsa_workspace_size(int op, const dsa_paged_kv* kv, const dsa_queries*
     case DSA_OP_ATTN_DECODE: {
       if ((st = check_common(kv, qs, kNeedAttn)) != DSA_OK) return st;
       if ((st = check_topk(top_k)) != DSA_OK) return st;
-      const int splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
-      *bytes = dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads, splits);
+      *bytes = attn_layout(kv, qs, top_k, 0).total;
       return ok();
     }
     case DSA_OP_DECODE_FUSED: {
@@ -223,16 +236,19 @@ dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   dsa_status st = attn_common(kv, qs, block_idx, block_cnt, top_k, out);
   if (st != DSA_OK) return st;
-  const int splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
-  const size_t need = dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads, splits);
+  const AttnLayout a = attn_layout(kv, qs, top_k, 0);
+  const size_t need = a.total;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
   if (need > 0 && !aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
   if (qs->num_queries == 0) return ok();
-  return hip_status(dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
-                                            softmax_scale, out, lse,
-                                            static_cast<float*>(workspace), splits, stream),
-                    "sparse_attn_decode launch");
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(
+      dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
+                              softmax_scale, out, lse,
+                              a.splits > 1 ? reinterpret_cast<float*>(ws + a.partials) : nullptr,
+                              a.splits, stream),
+      "sparse_attn_decode launch");
 }
 
 dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs,
@@ -274,8 +290,10 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
   if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
   e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
   if (e != hipSuccess) return hip_status(e, "fused: topk launch");
+  const bool split = f.attn.splits > 1;
   e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse,
-                              reinterpret_cast<float*>(ws + f.partials), f.splits, stream);
+                              split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr,
+                              f.attn.splits, stream);
   return hip_status(e, "fused: attention launch");
 }
 

@@ -41,7 +41,8 @@ hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, in
                        int32_t* idx, int32_t* cnt, hipStream_t s);
 
 // Split-K sparse attention.  num_splits == 1 writes out/lse directly;
-// otherwise partial softmax states go to `partials` and a merge pass follows.
+// otherwise partial softmax states go to `partials` and a merge kernel follows
+// on the same stream.
 int attn_num_splits(int nq, int hkv, int top_k, bool prefill);
 size_t attn_partials_bytes(int nq, int hq, int splits);
 hipError_t launch_sparse_attn(const KvView& kv, const QView& q, const int32_t* idx,

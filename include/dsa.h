@@ -150,7 +150,8 @@ dsa_status dsa_topk_blocks(const float* scores, const dsa_paged_kv* kv, const ds
  * logical ids or -1 beyond block_cnt; the local block must be among them.
  * out: fp32 [Nq, Hq, head_dim]; lse: fp32 [Nq, Hq] or NULL.
  * workspace: device buffer of at least dsa_workspace_size(DSA_OP_ATTN_DECODE)
- * bytes, 256 B aligned (may be NULL when that size is 0).
+ * bytes, 256 B aligned (may be NULL when that size is 0); it holds the
+ * split partials.  Calls that share a workspace must not overlap in time.
  */
 dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
                                   const int32_t* block_idx, const int32_t* block_cnt,
@@ -173,7 +174,8 @@ dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs
  * fuse index selection, gather and attention in decode): dsa_index_score,
  * dsa_topk_blocks and dsa_sparse_attn_decode in one entry point with the
  * same results.  block_idx_out / block_cnt_out (nullable) receive the
- * selection.  workspace: at least dsa_workspace_size(DSA_OP_DECODE_FUSED).
+ * selection.  workspace: at least dsa_workspace_size(DSA_OP_DECODE_FUSED)
+ * bytes, 256 B aligned.
  */
 dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
                                    float softmax_scale, float* out, float* lse,
