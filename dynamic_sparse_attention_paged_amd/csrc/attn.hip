@@ -36,8 +36,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kNumCUs = 256;   // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -172,8 +170,9 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
   }
 }
 
-// grid (splits, Hkv, Nq), block 256.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_split(
+// grid (splits, Hkv, Nq), block 64 W.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
+template <int kAttnWaves>
+__global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ partials) {
@@ -253,7 +252,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_split(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wo[(wave * 16 + r) * kHeadDim + 16 * dt + 4 * gq + i] = st.o[dt][i];
   __syncthreads();
-  for (int e = threadIdx.x; e < G * kHeadDim; e += kAttnThreads) {
+  for (int e = threadIdx.x; e < G * kHeadDim; e += 64 * kAttnWaves) {
     const int h = e / kHeadDim, d = e % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
@@ -304,22 +303,29 @@ __global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict
 
 }  // namespace
 
-int attn_num_splits(int nq, int hkv, int top_k, bool prefill) {
-  if (prefill) return 1;
-  // Tuning override (same results, different launch shape): DSA_ATTN_SPLITS=n
-  if (const char* e = getenv("DSA_ATTN_SPLITS")) {
-    const int n = atoi(e);
-    if (n >= 1) return n < top_k ? n : top_k;
-  }
-  // Split the selected blocks only as far as needed to give every CU a
-  // workgroup, keeping at least one block per wave.
+AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill) {
+  AttnPlan a;
   const long units = (long)nq * hkv;
-  if (units <= 0) return 1;
-  int splits = (int)((kNumCUs + units - 1) / units);
-  const int max_splits = (top_k + kAttnWaves - 1) / kAttnWaves;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  return splits;
+  // Enough (query, KV head) pairs to give every CU a workgroup: no split.
+  // Otherwise the selected blocks are split across workgroups until every
+  // CU has one.
+  // (eight waves per workgroup measured no faster than four for batched decode)
+  a.waves = prefill ? 8 : 4;
+  a.splits = 1;
+  if (!prefill && units > 0 && units < kNumCUs) {
+    int splits = (int)((kNumCUs + units - 1) / units);
+    const int max_splits = (top_k + a.waves - 1) / a.waves;  // >= one block per wave
+    a.splits = splits < max_splits ? splits : max_splits;
+    if (a.splits < 1) a.splits = 1;
+  }
+  // Tuning override (same results, different launch shape): DSA_ATTN_SPLITS=n
+  if (!prefill) {
+    if (const char* e = getenv("DSA_ATTN_SPLITS")) {
+      const int n = atoi(e);
+      if (n >= 1) a.splits = n < top_k ? n : top_k;
+    }
+  }
+  return a;
 }
 
 size_t attn_partials_bytes(int nq, int hq, int splits) {
@@ -329,14 +335,20 @@ size_t attn_partials_bytes(int nq, int hq, int splits) {
 
 hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* idx,
                               const int32_t* cnt, int top_k, float scale, float* out, float* lse,
-                              float* partials, int splits, hipStream_t st) {
+                              float* partials, AttnPlan plan, hipStream_t st) {
   const float scale2 = scale * kLog2e;
-  hipLaunchKernelGGL(sparse_attn_split, dim3(splits, kv.num_kv_heads, Q.nq), dim3(kAttnThreads),
-                     0, st, kv, Q, idx, cnt, top_k, scale2, splits, out, lse, partials);
+  const dim3 grid(plan.splits, kv.num_kv_heads, Q.nq);
+  if (plan.waves == 8) {
+    hipLaunchKernelGGL(sparse_attn_split<8>, grid, dim3(512), 0, st, kv, Q, idx, cnt, top_k,
+                       scale2, plan.splits, out, lse, partials);
+  } else {
+    hipLaunchKernelGGL(sparse_attn_split<4>, grid, dim3(256), 0, st, kv, Q, idx, cnt, top_k,
+                       scale2, plan.splits, out, lse, partials);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(merge_splits, dim3(Q.nq * Q.hq), dim3(kHeadDim), 0, st, partials, splits,
-                     out, lse);
+  if (e != hipSuccess || plan.splits == 1) return e;
+  hipLaunchKernelGGL(merge_splits, dim3(Q.nq * Q.hq), dim3(kHeadDim), 0, st, partials,
+                     plan.splits, out, lse);
   return hipGetLastError();
 }
 

@@ -113,16 +113,16 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 // Attention workspace: split partials.
 struct AttnLayout {
   size_t partials, total;
-  int splits;
+  dsa::AttnPlan plan;
 };
 
 AttnLayout attn_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k, size_t base) {
   AttnLayout a;
-  a.splits = dsa::attn_num_splits(qs->num_queries, kv->num_kv_heads, top_k, false);
+  a.plan = dsa::attn_plan(qs->num_queries, kv->num_kv_heads, top_k, false);
   a.partials = base;
   a.total = align_up(a.partials + dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads,
-                                                           a.splits));
-  if (a.splits <= 1) a.total = base;
+                                                           a.plan.splits));
+  if (a.plan.splits <= 1) a.total = base;
   return a;
 }
 
@@ -246,8 +246,9 @@ dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
   return hip_status(
       dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
                               softmax_scale, out, lse,
-                              a.splits > 1 ? reinterpret_cast<float*>(ws + a.partials) : nullptr,
-                              a.splits, stream),
+                              a.plan.splits > 1 ? reinterpret_cast<float*>(ws + a.partials)
+                                                : nullptr,
+                              a.plan, stream),
       "sparse_attn_decode launch");
 }
 
@@ -260,7 +261,10 @@ dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs
   if (!qs->q_seq || !qs->q_pos) return fail(DSA_ERR_NULL, "prefill needs q_seq and q_pos");
   if (qs->num_queries == 0) return ok();
   return hip_status(dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
-                                            softmax_scale, out, lse, nullptr, 1, stream),
+                                            softmax_scale, out, lse, nullptr,
+                                            dsa::attn_plan(qs->num_queries, kv->num_kv_heads,
+                                                           top_k, true),
+                                            stream),
                     "sparse_attn_prefill launch");
 }
 
@@ -290,10 +294,10 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
   if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
   e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
   if (e != hipSuccess) return hip_status(e, "fused: topk launch");
-  const bool split = f.attn.splits > 1;
+  const bool split = f.attn.plan.splits > 1;
   e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse,
                               split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr,
-                              f.attn.splits, stream);
+                              f.attn.plan, stream);
   return hip_status(e, "fused: attention launch");
 }
 

@@ -43,10 +43,14 @@ hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, in
 // Split-K sparse attention.  num_splits == 1 writes out/lse directly;
 // otherwise partial softmax states go to `partials` and a merge kernel follows
 // on the same stream.
-int attn_num_splits(int nq, int hkv, int top_k, bool prefill);
+struct AttnPlan {
+  int waves;   // waves per workgroup (4 or 8)
+  int splits;  // workgroups per (query, KV head)
+};
+AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill);
 size_t attn_partials_bytes(int nq, int hq, int splits);
 hipError_t launch_sparse_attn(const KvView& kv, const QView& q, const int32_t* idx,
                               const int32_t* cnt, int top_k, float scale, float* out, float* lse,
-                              float* partials, int splits, hipStream_t s);
+                              float* partials, AttnPlan plan, hipStream_t s);
 
 }  // namespace dsa
