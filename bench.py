@@ -109,6 +109,22 @@ class Device:
                               block_idx=self.idx[s] if with_idx else None,
                               block_cnt=self.cnt[s] if with_idx else None, workspace=self.ws)
 
+    def capture(self):
+        """One HIP graph per query set holding a whole fused step (the library
+        allocates and synchronizes nothing, so a step is capturable)."""
+        import torch
+        self.graphs = []
+        torch.cuda.synchronize()
+        for s in range(len(self.sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.fused(s)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self, i):
+        self.graphs[i % len(self.graphs)].replay()
+
     def select(self):
         for s in range(len(self.sets)):
             self.dsa.index_topk(self.kv, self.sets[s], self.w.top_k, block_idx=self.idx[s],
@@ -209,7 +225,8 @@ def decode_extra(w, steps, nsets):
     """q/s and HBM GB/s of a decode workload through the fused entry point."""
     import torch
     D = Device(w, nsets)
-    ms = event_time_ms(D.fused, steps, 3)
+    D.capture()
+    ms = event_time_ms(D.replay, steps, 3)
     D.select()
     torch.cuda.synchronize()
     attn_ms = event_time_ms(D.attn, steps, 3)
@@ -257,6 +274,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -275,13 +294,17 @@ def main():
     log(f"workload {w.name}: pool {w.num_blocks} blocks, {args.query_sets} query sets")
     D = Device(w, args.query_sets)
 
-    # timed region: K fused steps, inputs resident
+    # timed region: K fused steps replayed from HIP graphs, inputs resident
+    step = D.fused
+    if not args.no_graph:
+        D.capture()
+        step = D.replay
     for i in range(args.warmup):
-        D.fused(i)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        D.fused(i)
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -323,7 +346,8 @@ def main():
         "config": {"workload": w.name, "batch": w.num_queries, "context_tokens": 32768,
                    "block_size": 64, "q_heads": 64, "kv_heads": 8, "head_dim": 128,
                    "idx_heads": 8, "idx_dim": 128, "top_k": w.top_k,
-                   "query_sets": args.query_sets, "entry": "dsa_sparse_decode_fused"},
+                   "query_sets": args.query_sets, "entry": "dsa_sparse_decode_fused",
+                   "launch": "eager" if args.no_graph else "hip_graph_replay"},
         "hbm_gbps": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "sparse_attn_split", "bound": "hbm",

@@ -18,10 +18,10 @@
 // The gfx950 FP8 MFMA does not accumulate exactly (it aligns products to the
 // largest one and drops low bits), so it cannot reproduce these scores.
 //
-// Mapping: one lane per logical block.  The block-table row is read
-// coalesced (64 consecutive int32 per wave); each lane reads its block's
-// whole key row (dI bytes, 16 B loads).  The query's decoded FP8 values live
-// in LDS as float64 [dI][HP] and are read as wave-uniform broadcasts.
+// Mapping: four lanes per logical block, each owning a quarter of the key
+// row (16 or 32 B, read with 16 B loads); 16 blocks per wave.  The query's
+// decoded FP8 values live in LDS as float64 [dI][HP]; a read serves the 16
+// lanes of a quarter with one broadcast address.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -30,7 +30,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kScoreThreads = 128;  // lanes = logical blocks per workgroup
+constexpr int kScoreThreads = 256;
+constexpr int kBlocksPerWg = 64;  // 4 lanes per block
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
@@ -99,6 +100,9 @@ __device__ void load_query(const QView& Q, int qi, double* qv, double* sq, doubl
   __syncthreads();
 }
 
+// Lanes: 4 per block (dims DI/4 each), 16 blocks per wave, 64 per workgroup.
+// Partial dot products of exact products are exact in float64, so the order
+// in which the four lanes' partials are combined does not matter.
 template <int DI, int HP>
 __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QView Q,
                                                                    float* __restrict__ scores) {
@@ -106,50 +110,68 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   __shared__ double sq[HP], wq[HP];
   __shared__ uint32_t amax_bits[HP];
   __shared__ int expo[HP];
+  constexpr int kSlice = DI / 4;  // dims per lane
 
   const int qi = blockIdx.y;
-  const int j = blockIdx.x * kScoreThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gq = lane >> 4;
+  const int j = blockIdx.x * kBlocksPerWg + wave * 16 + (lane & 15);
   const int s = query_seq(Q, qi);
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
   const int local = pos / kBlockSize;
-  const int first_invisible = local + 1;
+  float* row = scores + (size_t)qi * kv.maxb;
 
   // Workgroups whose blocks are all invisible only write -inf.
-  if ((int)(blockIdx.x * kScoreThreads) >= first_invisible) {
-    if (j < kv.maxb) scores[(size_t)qi * kv.maxb + j] = -INFINITY;
+  if (blockIdx.x * kBlocksPerWg > local) {
+    if (gq == 0 && j < kv.maxb) row[j] = -INFINITY;
     return;
+  }
+  // Block-table entry, key slice and scale are requested before the query
+  // prologue so that their latency overlaps it.
+  const bool visible = j <= local && j < kv.maxb;
+  int p = 0;
+  uint4 kw[kSlice / 16];
+  float ks_f = 0.f;
+  if (visible) {
+    p = kv.table[(size_t)s * kv.maxb + j];
+    const uint4* krow = reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)p * DI + gq * kSlice);
+#pragma unroll
+    for (int i = 0; i < kSlice / 16; ++i) kw[i] = krow[i];
+    if (gq == 0) ks_f = kv.idx_scale[p];
   }
   load_query<DI, HP>(Q, qi, qv, sq, wq, amax_bits, expo);
-  if (j >= kv.maxb) return;
-  if (j >= first_invisible) {
-    scores[(size_t)qi * kv.maxb + j] = -INFINITY;
-    return;
-  }
-  const int p = kv.table[(size_t)s * kv.maxb + j];
-  const uint4* krow = reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)p * DI);
-  uint4 kw[DI / 16];
-#pragma unroll
-  for (int i = 0; i < DI / 16; ++i) kw[i] = krow[i];
-  const double ks = (double)kv.idx_scale[p];
-
   double acc[HP];
 #pragma unroll
   for (int h = 0; h < HP; ++h) acc[h] = 0.0;
+  if (visible) {
 #pragma unroll
-  for (int i = 0; i < DI / 16; ++i) {
-    const uint32_t words[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+    for (int i = 0; i < kSlice / 16; ++i) {
+      const uint32_t words[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
+      for (int wd = 0; wd < 4; ++wd) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int d = i * 16 + wd * 4 + b;
-        const double kd = (double)e4m3_byte_to_f32(words[wd], b);
+        for (int b = 0; b < 4; ++b) {
+          const int d = gq * kSlice + i * 16 + wd * 4 + b;
+          const double kd = (double)e4m3_byte_to_f32(words[wd], b);
 #pragma unroll
-        for (int h = 0; h < HP; ++h) acc[h] = fma(qv[d * HP + h], kd, acc[h]);
+          for (int h = 0; h < HP; ++h) acc[h] = fma(qv[d * HP + h], kd, acc[h]);
+        }
       }
     }
   }
+  // combine the four dim slices (exact)
+#pragma unroll
+  for (int h = 0; h < HP; ++h) {
+    acc[h] += __shfl_xor(acc[h], 16, 64);
+    acc[h] += __shfl_xor(acc[h], 32, 64);
+  }
+  if (gq != 0 || j >= kv.maxb) return;
+  if (!visible) {
+    row[j] = -INFINITY;
+    return;
+  }
+  const double ks = (double)ks_f;
   double S = 0.0;
   {
 #pragma clang fp contract(off)
@@ -160,12 +182,12 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
       S = S + wq[h] * r;
     }
   }
-  scores[(size_t)qi * kv.maxb + j] = (float)S;
+  row[j] = (float)S;
 }
 
 template <int DI, int HP>
 hipError_t launch_t(const KvView& kv, const QView& Q, float* scores, hipStream_t st) {
-  dim3 grid((kv.maxb + kScoreThreads - 1) / kScoreThreads, Q.nq);
+  dim3 grid((kv.maxb + kBlocksPerWg - 1) / kBlocksPerWg, Q.nq);
   hipLaunchKernelGGL((index_score_exact<DI, HP>), grid, dim3(kScoreThreads), 0, st, kv, Q,
                      scores);
   return hipGetLastError();

@@ -10,11 +10,13 @@
 //     equal scores going to the lower j (and -0.0 == +0.0);
 //   - output in ascending j (so l is last), -1 padded, count = min(K, l+1).
 //
-// Method: scores become order-preserving uint32 keys; four 8-bit MSB-first
-// histogram passes find the key T of the (K-1)-th largest candidate; every
-// key > T is kept and, of the keys == T, the lowest-j ones up to the
-// remaining count.  The ascending compaction is a workgroup prefix sum over
-// contiguous j ranges, which yields the output order without any sort.
+// Method: scores become order-preserving uint32 keys and the key T of the
+// (K-1)-th largest candidate is found by four 8-bit MSB-first radix passes
+// over an LDS histogram -- one wave per query with the keys in registers for
+// up to 2048 candidates, a 1024-thread workgroup per query for longer lists.  Every key > T is kept and, of the keys
+// == T, the lowest-j ones up to the remaining count.  Compaction over
+// contiguous j ranges with a prefix sum yields the ascending output order
+// without any sort.
 #include <hip/hip_runtime.h>
 
 #include "dsa_internal.h"
@@ -22,8 +24,7 @@
 namespace dsa {
 namespace {
 
-constexpr int kTopkThreads = 256;
-constexpr int kTopkLdsKeys = 15360;  // candidates cached in LDS (60 KiB, + ~2 KiB static)
+constexpr int kTopkLdsKeys = 16384;  // candidates cached in LDS (64 KiB)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f == 0.0f) f = 0.0f;  // -0.0 and +0.0 compare equal
@@ -31,32 +32,49 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; returns this thread's prefix and
-// the total in *total.  `buf` holds kTopkThreads uint32 of LDS.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf, uint32_t* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTopkThreads; off <<= 1) {
-    const uint32_t add = tid >= off ? buf[tid - off] : 0u;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
-  }
-  const uint32_t incl = buf[tid];
-  *total = buf[kTopkThreads - 1];
-  __syncthreads();
-  return incl - v;
+// Inclusive prefix sum across the 64 lanes of a wave with DPP:
+// Hillis-Steele within each 16-lane row (row_shr 1, 2, 4, 8), then the row
+// totals are broadcast forward (row_bcast:15 into rows 1 and 3, row_bcast:31
+// into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
-template <bool kKeysInLds>
-__global__ __launch_bounds__(kTopkThreads) void topk_radix(const float* __restrict__ scores,
-                                                           KvView kv, QView Q, int top_k,
-                                                           int32_t* __restrict__ out_idx,
-                                                           int32_t* __restrict__ out_cnt) {
-  extern __shared__ uint32_t keys[];  // kTopkLdsKeys when kKeysInLds
+// Exclusive prefix sum over the workgroup (wave scans + one cross-wave step).
+// Returns this thread's prefix; *total receives the workgroup sum.
+template <int kThreads>
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
+  constexpr int kWaves = kThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = wave_tot[w];
+    before += w < wave ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();  // wave_tot may be reused by the next scan
+  *total = tot;
+  return before + x - v;
+}
+
+template <int kThreads, bool kKeysInLds>
+__global__ __launch_bounds__(kThreads) void topk_radix(const float* __restrict__ scores,
+                                                       KvView kv, QView Q, int top_k,
+                                                       int32_t* __restrict__ out_idx,
+                                                       int32_t* __restrict__ out_cnt) {
+  __shared__ uint32_t keys[kKeysInLds ? kTopkLdsKeys : 1];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_buf[kTopkThreads];
+  __shared__ uint32_t wave_tot[kThreads / 64];
   __shared__ uint32_t sel_prefix, sel_remaining;
 
   const int tid = threadIdx.x;
@@ -71,20 +89,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix(const float* __restri
   int32_t* out = out_idx + (size_t)qi * top_k;
 
   if (n <= need) {  // everything visible is kept
-    for (int i = tid; i < top_k; i += kTopkThreads) out[i] = i <= local ? i : -1;
+    for (int i = tid; i < top_k; i += kThreads) out[i] = i <= local ? i : -1;
     if (tid == 0) out_cnt[qi] = local + 1;
     return;
   }
   if (kKeysInLds) {
-    for (int j = tid; j < n; j += kTopkThreads) keys[j] = order_key(row[j]);
+    // eight loads in flight per thread (clamped in-row indices, masked stores)
+    for (int base = 0; base < n; base += 8 * kThreads) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = row[min(base + u * kThreads + tid, kv.maxb - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = base + u * kThreads + tid;
+        if (j < n) keys[j] = order_key(v[u]);
+      }
+    }
   }
-  if (tid == 0) { sel_prefix = 0u; sel_remaining = (uint32_t)need; }
+  if (tid == 0) {
+    sel_prefix = 0u;
+    sel_remaining = (uint32_t)need;
+  }
   uint32_t mask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0u;  // kTopkThreads == 256 bins
+    for (int b = tid; b < 256; b += kThreads) hist[b] = 0u;
     __syncthreads();
     const uint32_t prefix = sel_prefix;
-    for (int j = tid; j < n; j += kTopkThreads) {
+    for (int j = tid; j < n; j += kThreads) {
       const uint32_t k = kKeysInLds ? keys[j] : order_key(row[j]);
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
     }
@@ -96,15 +127,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix(const float* __restri
       const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
                      h3 = hist[4 * tid + 3];
       const uint32_t mine = h0 + h1 + h2 + h3;
-      // inclusive suffix sum over lanes tid..63
-      uint32_t suf = mine;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(suf, off, 64);
-        if (tid + off < 64) suf += o;
-      }
-      const uint32_t above = suf - mine;  // keys in digits > 4 tid + 3
+      const uint32_t incl = wave_incl_scan(mine);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      const uint32_t suf = total - incl + mine;  // inclusive suffix sum over lanes tid..63
+      const uint32_t above = suf - mine;         // keys in digits > 4 tid + 3
       if (above < remaining && remaining <= suf) {
-        // crossing inside this lane's four digits, scanning from the top
         uint32_t c = above;
         int d = 3;
         const uint32_t hs[4] = {h0, h1, h2, h3};
@@ -123,7 +150,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix(const float* __restri
   const uint32_t take_eq = sel_remaining;  // keys == T to keep, lowest j first
 
   // Ascending compaction over contiguous ranges.
-  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
+  const int chunk = (n + kThreads - 1) / kThreads;
   const int j0 = min(n, tid * chunk), j1 = min(n, j0 + chunk);
   uint32_t n_gt = 0, n_eq = 0;
   for (int j = j0; j < j1; ++j) {
@@ -132,10 +159,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix(const float* __restri
     n_eq += k == T;
   }
   uint32_t total;
-  const uint32_t eq_before = block_exclusive_scan(n_eq, scan_buf, &total);
-  const uint32_t eq_take_here =
-      eq_before >= take_eq ? 0u : min(n_eq, take_eq - eq_before);
-  const uint32_t out_before = block_exclusive_scan(n_gt + eq_take_here, scan_buf, &total);
+  const uint32_t eq_before = block_exclusive_scan<kThreads>(n_eq, wave_tot, &total);
+  const uint32_t eq_take_here = eq_before >= take_eq ? 0u : min(n_eq, take_eq - eq_before);
+  const uint32_t out_before = block_exclusive_scan<kThreads>(n_gt + eq_take_here, wave_tot, &total);
   uint32_t o = out_before, eq_seen = 0;
   for (int j = j0; j < j1; ++j) {
     const uint32_t k = kKeysInLds ? keys[j] : order_key(row[j]);
@@ -152,17 +178,135 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix(const float* __restri
   }
 }
 
+// Single-wave selection for up to 64 * M candidates, keys in registers.
+// Lane l owns candidates [l M, l M + M).  Four 8-bit MSB-first radix passes
+// over a histogram in LDS (one wave: LDS operations complete in order, so no
+// barriers); the digit holding the (K-1)-th largest key is found from a wave
+// prefix sum over the per-lane bin sums.
+template <int M>
+__global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores, KvView kv,
+                                                QView Q, int top_k, int32_t* __restrict__ out_idx,
+                                                int32_t* __restrict__ out_cnt) {
+  __shared__ uint4 hist4[64];  // 256 bins, lane l owns bins 4l .. 4l+3
+  uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
+  const int lane = threadIdx.x;
+  const int qi = blockIdx.x;
+  const int s = query_seq(Q, qi);
+  const int len = kv.seq_lens[s];
+  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  const int local = pos / kBlockSize;
+  const int n = local;
+  const int need = top_k - 1;
+  const float* row = scores + (size_t)qi * kv.maxb;
+  int32_t* out = out_idx + (size_t)qi * top_k;
+  if (n <= need) {
+    for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
+    if (lane == 0) out_cnt[qi] = local + 1;
+    return;
+  }
+  // Unconditional loads from clamped (in-row) indices, so all M are in flight
+  // at once; candidates past n are masked afterwards.
+  float v[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) v[m] = row[min(lane * M + m, kv.maxb - 1)];
+  uint32_t k[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int j = lane * M + m;
+    k[m] = j < n ? order_key(v[m]) : 0u;  // key 0 is below every finite score
+  }
+  uint32_t T = 0u, mask = 0u, remaining = (uint32_t)need;
+#pragma unroll
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist4[lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int j = lane * M + m;
+      if (j < n && (k[m] & mask) == T) atomicAdd(&hist[(k[m] >> shift) & 0xFFu], 1u);
+    }
+    const uint4 h = hist4[lane];
+    const uint32_t mine = h.x + h.y + h.z + h.w;
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t above = total - incl;  // keys in digits above this lane's four
+    // the digit holding the remaining-th largest key lies in the lane where
+    // above < remaining <= above + mine; find it among the lane's four digits
+    uint32_t c = above;
+    int d = 3;
+    const uint32_t hs[4] = {h.x, h.y, h.z, h.w};
+    for (; d > 0; --d) {
+      if (c + hs[d] >= remaining) break;
+      c += hs[d];
+    }
+    const bool hit = above < remaining && remaining <= above + mine;
+    const int L = __builtin_ffsll((long long)__ballot(hit)) - 1;
+    const int dig = __builtin_amdgcn_readlane(4 * lane + d, L);
+    const uint32_t cut = (uint32_t)__builtin_amdgcn_readlane((int)c, L);
+    T |= (uint32_t)dig << shift;
+    remaining -= cut;
+    mask |= 0xFFu << shift;
+  }
+  // T is the (K-1)-th largest key; keep keys > T and the first `remaining` keys == T.
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int j = lane * M + m;
+    if (j < n) {
+      n_gt += k[m] > T;
+      n_eq += k[m] == T;
+    }
+  }
+  const uint32_t eq_before = wave_incl_scan(n_eq) - n_eq;
+  const uint32_t eq_take = eq_before >= remaining ? 0u : min(n_eq, remaining - eq_before);
+  const uint32_t mine_out = n_gt + eq_take;
+  uint32_t o = wave_incl_scan(mine_out) - mine_out, eq_seen = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int j = lane * M + m;
+    if (j < n) {
+      bool keep = k[m] > T;
+      if (k[m] == T) {
+        keep = eq_seen < eq_take;
+        ++eq_seen;
+      }
+      if (keep && o < (uint32_t)need) out[o++] = j;
+    }
+  }
+  if (lane == 0) {
+    out[need] = local;
+    out_cnt[qi] = top_k;
+  }
+}
+
+template <int kThreads>
+hipError_t launch_t(const float* scores, const KvView& kv, const QView& Q, int top_k,
+                    int32_t* idx, int32_t* cnt, hipStream_t st) {
+  const int nmax = kv.maxb - 1;  // candidates per query at most
+  if (nmax <= kTopkLdsKeys) {
+    hipLaunchKernelGGL((topk_radix<kThreads, true>), dim3(Q.nq), dim3(kThreads), 0, st, scores,
+                       kv, Q, top_k, idx, cnt);
+  } else {
+    hipLaunchKernelGGL((topk_radix<kThreads, false>), dim3(Q.nq), dim3(kThreads), 0, st, scores,
+                       kv, Q, top_k, idx, cnt);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, const KvView& kv, const QView& Q, int top_k,
                        int32_t* idx, int32_t* cnt, hipStream_t st) {
-  if (kv.maxb - 1 <= kTopkLdsKeys) {
-    hipLaunchKernelGGL(topk_radix<true>, dim3(Q.nq), dim3(kTopkThreads),
-                       (size_t)(kv.maxb - 1) * sizeof(uint32_t), st, scores, kv, Q, top_k, idx,
-                       cnt);
+  const int nmax = kv.maxb - 1;  // candidates per query at most
+  const dim3 g(Q.nq);
+  if (nmax <= 64 * 2) {
+    hipLaunchKernelGGL(topk_wave<2>, g, dim3(64), 0, st, scores, kv, Q, top_k, idx, cnt);
+  } else if (nmax <= 64 * 8) {
+    hipLaunchKernelGGL(topk_wave<8>, g, dim3(64), 0, st, scores, kv, Q, top_k, idx, cnt);
+  } else if (nmax <= 64 * 32) {
+    hipLaunchKernelGGL(topk_wave<32>, g, dim3(64), 0, st, scores, kv, Q, top_k, idx, cnt);
   } else {
-    hipLaunchKernelGGL(topk_radix<false>, dim3(Q.nq), dim3(kTopkThreads), 0, st, scores, kv, Q,
-                       top_k, idx, cnt);
+    // long candidate lists: a 1024-thread workgroup per query, 8-bit radix passes in LDS
+    return launch_t<1024>(scores, kv, Q, top_k, idx, cnt, st);
   }
   return hipGetLastError();
 }

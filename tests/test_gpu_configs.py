@@ -1,0 +1,115 @@
+"""GPU parity at the five benchmark-shaped workloads, in the launch
+configuration bench.py times (fused decode; index_score -> topk -> prefill
+attention for the chunked prefill), on queries the oracle can check one by
+one.  Also exercises every Top-K variant (up to 128, 512, 2048 candidates, and
+longer lists)."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from dsa_synth import workload
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as m
+    m._lib.load()
+    return m
+
+
+def _check(w, qis, idx, cnt, out, lse, label):
+    worst = (0.0, 0.0)
+    swaps = 0
+    for qi in qis:
+        r = parity.oracle_query(w, int(qi))
+        ok, nsw = parity.check_indices(idx[qi], cnt[qi], r, w.top_k)
+        assert ok, f"{label} q{qi}: indices {idx[qi][:8]}.. cnt {cnt[qi]} vs {r['idx'][:8]}.. {r['cnt']}"
+        swaps += nsw
+        ref = r if nsw == 0 else parity.oracle_query(w, int(qi), sel_override=idx[qi][:cnt[qi]])
+        good, a, rel = parity.attn_ok(out[qi], ref["out"])
+        assert good, f"{label} q{qi}: attention max-abs {a:.3e} max-rel {rel:.3e}"
+        la, _ = parity.attn_errors(lse[qi], ref["lse"])
+        assert la <= 1e-3, f"{label} q{qi}: lse {la:.3e}"
+        worst = (max(worst[0], a), max(worst[1], rel))
+    _say(f"{label}: {len(qis)} queries ok, {swaps} near-tie swaps, worst max-abs {worst[0]:.2e} "
+         f"max-rel {worst[1]:.2e}")
+
+
+def _fused(dsa, w):
+    kv, qs = parity.to_device(w)
+    nq, K = w.num_queries, w.top_k
+    bi = torch.empty(nq, K, dtype=torch.int32, device="cuda")
+    bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, K, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    torch.cuda.synchronize()
+    res = bi.cpu().numpy(), bc.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    del kv, qs, out, lse, bi, bc
+    torch.cuda.empty_cache()
+    return res
+
+
+@pytest.mark.parametrize("lens,top_k", [((64 * 1500 - 3, 64 * 700, 64 * 513 + 1), 40),
+                                         ((64 * 2500, 64 * 2049 - 1, 64 * 5000 + 7), 24)])
+def test_topk_variants_long_lists(dsa, lens, top_k):
+    w = workload.small_decode(seed=2201 + len(lens) + top_k, lens=lens, hq=16, hkv=2, hi=8,
+                              top_k=top_k)
+    _say(f"long lists {lens} K={top_k}")
+    idx, cnt, out, lse = _fused(dsa, w)
+    _check(w, range(w.num_queries), idx, cnt, out, lse, "long lists")
+
+
+def test_batched_decode_full(dsa):
+    w = workload.batched_decode()
+    _say("batched decode 32 x 32768, all queries")
+    idx, cnt, out, lse = _fused(dsa, w)
+    _check(w, range(w.num_queries), idx, cnt, out, lse, "batched_decode")
+
+
+def test_million_decode_full(dsa):
+    w = workload.million_decode()
+    _say("million-token decode 4 x 1048576, all queries")
+    idx, cnt, out, lse = _fused(dsa, w)
+    _check(w, range(w.num_queries), idx, cnt, out, lse, "million_decode")
+
+
+def test_ragged_decode_sampled(dsa):
+    w = workload.ragged_decode()
+    _say(f"ragged decode 128 seqs, pool {w.num_blocks} blocks, 16 sampled queries")
+    idx, cnt, out, lse = _fused(dsa, w)
+    order = np.argsort(w.seq_lens)
+    qis = sorted(set(order[:4].tolist() + order[-4:].tolist() + list(range(0, 128, 16))))
+    _check(w, qis, idx, cnt, out, lse, "ragged_decode")
+
+
+def test_chunked_prefill_sampled(dsa):
+    w = workload.chunked_prefill()
+    _say("chunked prefill 8192 queries, 20 sampled")
+    kv, qs = parity.to_device(w)
+    K = w.top_k
+    scores = dsa.index_score(kv, qs)
+    idx, cnt = dsa.topk_blocks(scores, kv, qs, K)
+    out, lse = dsa.sparse_attn_prefill(kv, qs, idx, cnt, K, w.softmax_scale)
+    torch.cuda.synchronize()
+    qis = [0, 1, 63, 64, 65, 127, 128, 4095, 4096, 8190, 8191] + list(range(700, 8192, 1013))
+    _check(w, qis, idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy(),
+           "chunked_prefill")
+    # the scores themselves are the oracle's float64 score rounded to fp32, bit for bit
+    sh = scores.cpu().numpy()
+    for qi in qis[:6]:
+        r = parity.oracle_query(w, qi)
+        assert parity.check_scores_exact(sh[qi], r, w.block_table.shape[1]).size == 0
+    del kv, qs, scores, idx, cnt, out, lse
+    torch.cuda.empty_cache()
