@@ -96,7 +96,7 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
                                              float scale2, int tok0, int pos, int len,
                                              const uint16_t* vs, WaveState& st) {
   const int lane = threadIdx.x & 63;
-  const int r = lane & 15, gq = lane >> 4;
+  const int gq = lane >> 4;
 
   f32x4 sc[4];
 #pragma unroll

@@ -20,31 +20,12 @@
 #include <hip/hip_runtime.h>
 
 #include "dsa_internal.h"
+#include "select_common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kTopkLdsKeys = 16384;  // candidates cached in LDS (64 KiB)
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  if (f == 0.0f) f = 0.0f;  // -0.0 and +0.0 compare equal
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave with DPP:
-// Hillis-Steele within each 16-lane row (row_shr 1, 2, 4, 8), then the row
-// totals are broadcast forward (row_bcast:15 into rows 1 and 3, row_bcast:31
-// into rows 2 and 3).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
 
 // Exclusive prefix sum over the workgroup (wave scans + one cross-wave step).
 // Returns this thread's prefix; *total receives the workgroup sum.
@@ -91,6 +72,13 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const float* __restrict__
   if (n <= need) {  // everything visible is kept
     for (int i = tid; i < top_k; i += kThreads) out[i] = i <= local ? i : -1;
     if (tid == 0) out_cnt[qi] = local + 1;
+    return;
+  }
+  if (need == 0) {  // K = 1: the local block alone
+    if (tid == 0) {
+      out[0] = local;
+      out_cnt[qi] = 1;
+    }
     return;
   }
   if (kKeysInLds) {
@@ -179,16 +167,12 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const float* __restrict__
 }
 
 // Single-wave selection for up to 64 * M candidates, keys in registers.
-// Lane l owns candidates [l M, l M + M).  Four 8-bit MSB-first radix passes
-// over a histogram in LDS (one wave: LDS operations complete in order, so no
-// barriers); the digit holding the (K-1)-th largest key is found from a wave
-// prefix sum over the per-lane bin sums.
+// Lane l owns candidates [l M, l M + M).
 template <int M>
 __global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores, KvView kv,
                                                 QView Q, int top_k, int32_t* __restrict__ out_idx,
                                                 int32_t* __restrict__ out_cnt) {
-  __shared__ uint4 hist4[64];  // 256 bins, lane l owns bins 4l .. 4l+3
-  uint32_t* hist = reinterpret_cast<uint32_t*>(hist4);
+  __shared__ uint4 hist4[64];
   const int lane = threadIdx.x;
   const int qi = blockIdx.x;
   const int s = query_seq(Q, qi);
@@ -204,74 +188,125 @@ __global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores
     if (lane == 0) out_cnt[qi] = local + 1;
     return;
   }
+  if (need == 0) {  // K = 1: the local block alone
+    if (lane == 0) {
+      out[0] = local;
+      out_cnt[qi] = 1;
+    }
+    return;
+  }
   // Unconditional loads from clamped (in-row) indices, so all M are in flight
-  // at once; candidates past n are masked afterwards.
+  // at once; candidates past n are masked.
   float v[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) v[m] = row[min(lane * M + m, kv.maxb - 1)];
-  uint32_t k[M];
+  uint32_t k[M], valid = 0u;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int j = lane * M + m;
-    k[m] = j < n ? order_key(v[m]) : 0u;  // key 0 is below every finite score
+    k[m] = order_key(v[m]);
+    valid |= (lane * M + m < n) ? (1u << m) : 0u;
   }
-  uint32_t T = 0u, mask = 0u, remaining = (uint32_t)need;
+  uint32_t T, take_eq, o;
+  wave_select<M>(k, valid, (uint32_t)need, hist4, T, take_eq);
+  const uint32_t keep = wave_keep<M>(k, valid, T, take_eq, &o);
 #pragma unroll
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist4[lane] = make_uint4(0u, 0u, 0u, 0u);
+  for (int m = 0; m < M; ++m)
+    if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = lane * M + m;
+  if (lane == 0) {
+    out[need] = local;  // largest visible id: last in ascending order
+    out_cnt[qi] = top_k;
+  }
+}
+
+// Two-level selection for long candidate lists (up to 16 * 64 * M, with
+// K - 1 <= kTreeMaxNeed): each of the 16 waves selects the K-1 best of its
+// contiguous range into LDS (in increasing position), then wave 0 selects
+// the K-1 best of those candidates, which are already in increasing order.
+constexpr int kTreeWaves = 16;
+constexpr int kTreeMaxNeed = 128;
+
+template <int M>
+__global__ __launch_bounds__(64 * kTreeWaves) void topk_tree(
+    const float* __restrict__ scores, KvView kv, QView Q, int top_k,
+    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
+  constexpr int M2 = kTreeWaves * kTreeMaxNeed / 64;  // second-level slots per lane
+  __shared__ uint4 hist4[kTreeWaves][64];
+  __shared__ uint32_t ck[kTreeWaves * kTreeMaxNeed];
+  __shared__ int32_t cj[kTreeWaves * kTreeMaxNeed];
+  __shared__ uint32_t wcnt[kTreeWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qi = blockIdx.x;
+  const int s = query_seq(Q, qi);
+  const int len = kv.seq_lens[s];
+  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  const int local = pos / kBlockSize;
+  const int n = local;
+  const int need = top_k - 1;
+  const float* row = scores + (size_t)qi * kv.maxb;
+  int32_t* out = out_idx + (size_t)qi * top_k;
+  if (n <= need) {
+    for (int i = threadIdx.x; i < top_k; i += 64 * kTreeWaves) out[i] = i <= local ? i : -1;
+    if (threadIdx.x == 0) out_cnt[qi] = local + 1;
+    return;
+  }
+  if (need == 0) {  // K = 1: the local block alone
+    if (threadIdx.x == 0) {
+      out[0] = local;
+      out_cnt[qi] = 1;
+    }
+    return;
+  }
+  // level 1: wave w owns positions [w R, w R + R), R = 64 M
+  {
+    const int base = wave * 64 * M + lane * M;
+    float v[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] = row[min(base + m, kv.maxb - 1)];
+    uint32_t k[M], valid = 0u;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const int j = lane * M + m;
-      if (j < n && (k[m] & mask) == T) atomicAdd(&hist[(k[m] >> shift) & 0xFFu], 1u);
+      k[m] = order_key(v[m]);
+      valid |= (base + m < n) ? (1u << m) : 0u;
     }
-    const uint4 h = hist4[lane];
-    const uint32_t mine = h.x + h.y + h.z + h.w;
-    const uint32_t incl = wave_incl_scan(mine);
-    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    const uint32_t above = total - incl;  // keys in digits above this lane's four
-    // the digit holding the remaining-th largest key lies in the lane where
-    // above < remaining <= above + mine; find it among the lane's four digits
-    uint32_t c = above;
-    int d = 3;
-    const uint32_t hs[4] = {h.x, h.y, h.z, h.w};
-    for (; d > 0; --d) {
-      if (c + hs[d] >= remaining) break;
-      c += hs[d];
+    const int nw = min(max(n - wave * 64 * M, 0), 64 * M);
+    uint32_t keep, o;
+    if (nw <= need) {  // keep the whole range
+      keep = valid;
+      const uint32_t c = (uint32_t)__builtin_popcount(valid);
+      o = wave_incl_scan(c) - c;
+    } else {
+      uint32_t T, take_eq;
+      wave_select<M>(k, valid, (uint32_t)need, hist4[wave], T, take_eq);
+      keep = wave_keep<M>(k, valid, T, take_eq, &o);
     }
-    const bool hit = above < remaining && remaining <= above + mine;
-    const int L = __builtin_ffsll((long long)__ballot(hit)) - 1;
-    const int dig = __builtin_amdgcn_readlane(4 * lane + d, L);
-    const uint32_t cut = (uint32_t)__builtin_amdgcn_readlane((int)c, L);
-    T |= (uint32_t)dig << shift;
-    remaining -= cut;
-    mask |= 0xFFu << shift;
-  }
-  // T is the (K-1)-th largest key; keep keys > T and the first `remaining` keys == T.
-  uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int j = lane * M + m;
-    if (j < n) {
-      n_gt += k[m] > T;
-      n_eq += k[m] == T;
-    }
-  }
-  const uint32_t eq_before = wave_incl_scan(n_eq) - n_eq;
-  const uint32_t eq_take = eq_before >= remaining ? 0u : min(n_eq, remaining - eq_before);
-  const uint32_t mine_out = n_gt + eq_take;
-  uint32_t o = wave_incl_scan(mine_out) - mine_out, eq_seen = 0;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int j = lane * M + m;
-    if (j < n) {
-      bool keep = k[m] > T;
-      if (k[m] == T) {
-        keep = eq_seen < eq_take;
-        ++eq_seen;
+    for (int m = 0; m < M; ++m) {
+      if (((keep >> m) & 1u) && o < (uint32_t)need) {
+        ck[wave * kTreeMaxNeed + o] = k[m];
+        cj[wave * kTreeMaxNeed + o] = base + m;
+        ++o;
       }
-      if (keep && o < (uint32_t)need) out[o++] = j;
     }
+    if (lane == 0) wcnt[wave] = (uint32_t)min(nw, need);
   }
+  __syncthreads();
+  if (wave != 0) return;
+  // level 2: candidate c = w * need + i (i < wcnt[w]) in increasing position
+  uint32_t k2[M2], valid2 = 0u;
+#pragma unroll
+  for (int m = 0; m < M2; ++m) {
+    const int c = lane * M2 + m;
+    const int w = c / kTreeMaxNeed, i = c % kTreeMaxNeed;
+    const bool ok = w < kTreeWaves && i < need && (uint32_t)i < wcnt[min(w, kTreeWaves - 1)];
+    k2[m] = ok ? ck[c] : 0u;
+    valid2 |= ok ? (1u << m) : 0u;
+  }
+  uint32_t T, take_eq, o;
+  wave_select<M2>(k2, valid2, (uint32_t)need, hist4[0], T, take_eq);
+  const uint32_t keep = wave_keep<M2>(k2, valid2, T, take_eq, &o);
+#pragma unroll
+  for (int m = 0; m < M2; ++m)
+    if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = cj[lane * M2 + m];
   if (lane == 0) {
     out[need] = local;
     out_cnt[qi] = top_k;
@@ -304,8 +339,11 @@ hipError_t launch_topk(const float* scores, const KvView& kv, const QView& Q, in
     hipLaunchKernelGGL(topk_wave<8>, g, dim3(64), 0, st, scores, kv, Q, top_k, idx, cnt);
   } else if (nmax <= 64 * 32) {
     hipLaunchKernelGGL(topk_wave<32>, g, dim3(64), 0, st, scores, kv, Q, top_k, idx, cnt);
+  } else if (nmax <= kTreeWaves * 64 * 16 && top_k - 1 <= kTreeMaxNeed) {
+    hipLaunchKernelGGL(topk_tree<16>, g, dim3(64 * kTreeWaves), 0, st, scores, kv, Q, top_k, idx,
+                       cnt);
   } else {
-    // long candidate lists: a 1024-thread workgroup per query, 8-bit radix passes in LDS
+    // long lists with large K: 8-bit radix passes over an LDS histogram
     return launch_t<1024>(scores, kv, Q, top_k, idx, cnt, st);
   }
   return hipGetLastError();

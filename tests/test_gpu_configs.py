@@ -1,8 +1,9 @@
 """GPU parity at the five benchmark-shaped workloads, in the launch
 configuration bench.py times (fused decode; index_score -> topk -> prefill
 attention for the chunked prefill), on queries the oracle can check one by
-one.  Also exercises every Top-K variant (up to 128, 512, 2048 candidates, and
-longer lists)."""
+one.  Also exercises every Top-K variant: one wave for up to 128, 512 and 2048
+candidates, the two-level selection for longer lists, and the LDS radix for
+long lists with a large K."""
 
 import sys
 
@@ -62,7 +63,9 @@ def _fused(dsa, w):
 
 
 @pytest.mark.parametrize("lens,top_k", [((64 * 1500 - 3, 64 * 700, 64 * 513 + 1), 40),
-                                         ((64 * 2500, 64 * 2049 - 1, 64 * 5000 + 7), 24)])
+                                         ((64 * 2500, 64 * 2049 - 1, 64 * 5000 + 7), 24),
+                                         ((64 * 3000 + 9, 64 * 2100), 200),
+                                         ((64 * 17000, 64 * 900), 33)])
 def test_topk_variants_long_lists(dsa, lens, top_k):
     w = workload.small_decode(seed=2201 + len(lens) + top_k, lens=lens, hq=16, hkv=2, hi=8,
                               top_k=top_k)
