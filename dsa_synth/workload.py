@@ -110,17 +110,22 @@ def build(name, seed, seq_lens, table, num_blocks, hq, hkv, hi, di, top_k,
 
     seq_lens: tokens per sequence; table: int [B, max_blocks] physical ids;
     prefill: None for decode (one query per sequence at L-1), else
-    (seq, first_pos, count) for a chunk of consecutive query positions.
+    (seq, first_pos, count) for a chunk of consecutive query positions, or a
+    list of such chunks (their queries concatenated in order), or a pair of
+    int arrays (q_seq, q_pos) giving every query's sequence and position.
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     table = np.asarray(table, dtype=np.int32)
     if prefill is None:
         q_seq = np.arange(seq_lens.size, dtype=np.int32)
         q_pos = (seq_lens - 1).astype(np.int32)
+    elif isinstance(prefill, tuple) and len(prefill) == 2:
+        q_seq = np.asarray(prefill[0], dtype=np.int32)
+        q_pos = np.asarray(prefill[1], dtype=np.int32)
     else:
-        s, first, count = prefill
-        q_seq = np.full(count, s, dtype=np.int32)
-        q_pos = np.arange(first, first + count, dtype=np.int32)
+        chunks = [prefill] if isinstance(prefill, tuple) else list(prefill)
+        q_seq = np.concatenate([np.full(c, s, dtype=np.int32) for s, _, c in chunks])
+        q_pos = np.concatenate([np.arange(f, f + c, dtype=np.int32) for _, f, c in chunks])
     nq = q_pos.size
     q, qi, w = _queries(seed, nq, hq, d, hi, di)
     plant = None
@@ -236,6 +241,37 @@ def small_prefill(seed=2101, L=64 * 20 - 5, count=200, hq=16, hkv=2, hi=4, di=12
     perm = gen.permutation(seed, gen.TAG_TABLE, P)
     return build(f"small_prefill_s{seed}", seed, [L], perm[None, :nb], P, hq=hq, hkv=hkv,
                  hi=hi, di=di, top_k=top_k, prefill=(0, L - count, count))
+
+
+def multi_prefill(seed=2121, lens=(64 * 30 + 7, 64 * 12, 64 * 21 - 1), counts=(120, 90, 70),
+                  interleave=False, hq=16, hkv=2, hi=8, di=128, top_k=8):
+    """Prefill chunks of several sequences in one batch: the last counts[s]
+    positions of sequence s, concatenated, or with ``interleave`` taken
+    round-robin across the sequences (so neighbouring queries differ in
+    sequence)."""
+    lens = [int(x) for x in lens]
+    nbs = [-(-L // 64) for L in lens]
+    maxb = max(nbs)
+    P = sum(nbs) + 5
+    perm = gen.permutation(seed, gen.TAG_TABLE, P)
+    table = np.zeros((len(lens), maxb), dtype=np.int32)
+    o = 0
+    for s, nb in enumerate(nbs):
+        table[s, :nb] = perm[o:o + nb]
+        o += nb
+    per = [np.arange(L - c, L, dtype=np.int32) for L, c in zip(lens, counts)]
+    if interleave:
+        qs, qp = [], []
+        for i in range(max(counts)):
+            for s, pos in enumerate(per):
+                if i < len(pos):
+                    qs.append(s)
+                    qp.append(int(pos[i]))
+        pre = (np.asarray(qs), np.asarray(qp))
+    else:
+        pre = [(s, L - c, c) for s, (L, c) in enumerate(zip(lens, counts))]
+    return build(f"multi_prefill_s{seed}", seed, lens, table, P, hq=hq, hkv=hkv, hi=hi, di=di,
+                 top_k=top_k, prefill=pre)
 
 
 def with_query_seed(w, qseed):

@@ -37,6 +37,9 @@ struct QView {
 __host__ __device__ inline int query_seq(const QView& q, int i) { return q.q_seq ? q.q_seq[i] : i; }
 
 hipError_t launch_index_score(const KvView& kv, const QView& q, float* scores, hipStream_t s);
+// Exact scoring of many queries on the int8 matrix cores (same results).
+bool index_score_mfma_supported(const KvView& kv, const QView& q);
+hipError_t launch_index_score_mfma(const KvView& kv, const QView& q, float* scores, hipStream_t s);
 hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, int top_k,
                        int32_t* idx, int32_t* cnt, hipStream_t s);
 

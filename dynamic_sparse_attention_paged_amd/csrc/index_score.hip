@@ -120,6 +120,8 @@ hipError_t launch_di(const KvView& kv, const QView& Q, float* scores, hipStream_
 }  // namespace
 
 hipError_t launch_index_score(const KvView& kv, const QView& Q, float* scores, hipStream_t st) {
+  // many queries at once: the same scores from the int8 matrix cores
+  if (index_score_mfma_supported(kv, Q)) return launch_index_score_mfma(kv, Q, scores, st);
   if (kv.idx_dim == 64) return launch_di<64>(kv, Q, scores, st);
   return launch_di<128>(kv, Q, scores, st);
 }

@@ -117,6 +117,32 @@ def test_small_prefill_stages(dsa, seed, count, L, top_k):
     _run_all_stages(dsa, w, f"small_prefill[{seed}]")
 
 
+# Batches of 256+ prefill queries of one sequence are scored on the int8
+# matrix cores: HI 4 / 8 x dI 64 / 128, several 512-block column ranges, a
+# ragged tail of queries and of blocks.
+MANY_QUERY_PREFILL_CASES = [
+    dict(seed=2111, L=64 * 700 + 13, count=300, hi=8, di=64, top_k=16),
+    dict(seed=2112, L=64 * 520, count=256, hi=4, di=64, top_k=8),
+    dict(seed=2113, L=64 * 300 - 9, count=333, hi=8, di=128, top_k=24),
+]
+
+
+@pytest.mark.parametrize("case", MANY_QUERY_PREFILL_CASES,
+                         ids=[str(c["seed"]) for c in MANY_QUERY_PREFILL_CASES])
+def test_many_query_prefill_stages(dsa, case):
+    w = workload.small_prefill(**case)
+    _say(f"many-query prefill {case}")
+    _run_all_stages(dsa, w, f"prefill[{case['seed']}]")
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_multi_sequence_prefill_stages(dsa, interleave):
+    # neighbouring queries of different sequences share waves of the scorer
+    w = workload.multi_prefill(interleave=interleave)
+    _say(f"multi-sequence prefill interleave={interleave} ({w.num_queries} queries)")
+    _run_all_stages(dsa, w, f"multi_prefill[{interleave}]")
+
+
 def test_tiny_decode_config(dsa):
     w = workload.tiny_decode()
     _say("tiny_decode (1 x 4096, K 8)")

@@ -51,3 +51,18 @@ def test_workload_shapes():
     assert np.unique(used).size == used.size and used.max() < s.num_blocks
     p = workload.small_prefill()
     assert p.q_pos[-1] == p.seq_lens[0] - 1 and not p.decode
+
+
+def test_multi_prefill_queries():
+    for inter in (False, True):
+        w = workload.multi_prefill(interleave=inter)
+        assert w.num_queries == 280 and not w.decode
+        assert (w.q_pos < w.seq_lens[w.q_seq]).all() and (w.q_pos >= 0).all()
+        for s, c in enumerate((120, 90, 70)):
+            pos = np.sort(w.q_pos[w.q_seq == s])
+            assert np.array_equal(pos, np.arange(w.seq_lens[s] - c, w.seq_lens[s]))
+        nb = -(-w.seq_lens // 64)
+        used = np.concatenate([w.block_table[s, :nb[s]] for s in range(3)])
+        assert np.unique(used).size == used.size and used.max() < w.num_blocks
+    w = workload.multi_prefill(interleave=True)
+    assert list(w.q_seq[:6]) == [0, 1, 2, 0, 1, 2]
