@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 METRIC = "decode queries/sec + achieved HBM GB/s (% roofline); prefill indexer MFMA %"
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+INT8_PEAK_TOPS = 5000.0
 ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", "attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_split_batched_decode.json")
 
@@ -257,8 +258,12 @@ def prefill_indexer_extra(steps):
                algorithmic_gflop=round(fl / 1e9, 3),
                tflops=round(fl / (ms * 1e-3) / 1e12, 2),
                frac_of_fp8_mfma_peak=round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-               note="scoring runs exact float64 FMAs (FP8 MFMA accumulation is inexact on "
-                    "gfx950); fraction is against the FP8 dense peak",
+               int8_digit_tops=round(9 * fl / (ms * 1e-3) / 1e12, 2),
+               frac_of_int8_mfma_peak=round(9 * fl / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+               note="exact scoring on the int8 matrix cores: each E4M3 product is nine "
+                    "base-128 digit products (the FP8 MFMA accumulation is inexact on gfx950); "
+                    "frac_of_fp8_mfma_peak counts the algorithmic FP8 flops, "
+                    "frac_of_int8_mfma_peak the digit products issued for them",
                topk_ms=round(tk_ms, 4), attention_ms=round(at_ms, 3))
     del D
     torch.cuda.empty_cache()
@@ -278,6 +283,9 @@ def main():
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--extra", choices=["tiny_decode", "million_decode", "ragged_decode",
+                                        "chunked_prefill"],
+                    help="run only this secondary workload (for profiling) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -290,6 +298,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.extra:
+        if args.extra == "chunked_prefill":
+            res = prefill_indexer_extra(args.steps)
+        else:
+            fn = getattr(workload, args.extra)
+            res = decode_extra(fn(), args.steps, 4 if args.extra != "tiny_decode" else 8)
+        print(json.dumps(res), flush=True)
+        return
     w = workload.batched_decode()
     log(f"workload {w.name}: pool {w.num_blocks} blocks, {args.query_sets} query sets")
     D = Device(w, args.query_sets)
