@@ -91,14 +91,9 @@ __device__ __forceinline__ void load_k(const uint16_t* __restrict__ kbase, size_
                                                  32 * c + 8 * gq);
 }
 
-// One selected block for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-__device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x8 (&qf)[4],
-                                             float scale2, int tok0, int pos, int len,
-                                             const uint16_t* vs, WaveState& st) {
-  const int lane = threadIdx.x & 63;
-  const int gq = lane >> 4;
-
-  f32x4 sc[4];
+// S^T = K Q^T for one block: sc[T][i] is token 16T + 4gq + i of head r.
+__device__ __forceinline__ void block_logits(const i16x8 (&kf)[4][4], const i16x8 (&qf)[4],
+                                             f32x4 (&sc)[4]) {
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -106,6 +101,13 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
     for (int c = 0; c < 4; ++c) acc = mfma_bf16(kf[T][c], qf[c], acc);
     sc[T] = acc;
   }
+}
+
+// Online softmax over one block's logits and O^T += V^T P^T.
+__device__ __forceinline__ void block_softmax_pv(f32x4 (&sc)[4], float scale2, int tok0, int pos,
+                                                 int len, const uint16_t* vs, WaveState& st) {
+  const int lane = threadIdx.x & 63;
+  const int gq = lane >> 4;
   // mask + scale (base 2); sc[T][i] is token 16T + 4gq + i of head r
   float mx = -INFINITY;
 #pragma unroll
@@ -170,13 +172,25 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
   }
 }
 
+// One selected block for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+__device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x8 (&qf)[4],
+                                             float scale2, int tok0, int pos, int len,
+                                             const uint16_t* vs, WaveState& st) {
+  f32x4 sc[4];
+  block_logits(kf, qf, sc);
+  block_softmax_pv(sc, scale2, tok0, pos, len, vs, st);
+}
+
 // grid (splits, Hkv, Nq), block 64 W.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
-template <int kAttnWaves>
+// kVBufs = 2: each wave double-buffers V in LDS, and the next block's K and V
+// are requested as soon as the current block's K has gone through the
+// logits MFMAs, so they arrive while the softmax and P V run.
+template <int kAttnWaves, int kVBufs>
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ partials) {
-  __shared__ uint16_t vs_all[kAttnWaves][64 * kHeadDim];
+  __shared__ uint16_t vs_all[kAttnWaves][kVBufs][64 * kHeadDim];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
 
   const int sp = blockIdx.x, g = blockIdx.y, qi = blockIdx.z;
@@ -207,7 +221,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* vs = vs_all[wave];
+  uint16_t* vs = vs_all[wave][0];
   const int32_t* sel = idx + (size_t)qi * top_k;
   const int32_t* trow = kv.table + (size_t)s * kv.maxb;
   const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
@@ -224,25 +238,56 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       my_j = sel[b0 + wave + kAttnWaves * (c0 + lane)];
       my_p = trow[my_j];
     }
-    for (int i = 0; i < cn; ++i) {
-      const int j = __builtin_amdgcn_readlane(my_j, i);
-      const int p = __builtin_amdgcn_readlane(my_p, i);
-      const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
-      // previous block's LDS reads are complete before the DMA overwrites vs
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
-      dma_v(kv.v + base, tok_stride, lane, vs);
+    if (kVBufs == 1) {
+      for (int i = 0; i < cn; ++i) {
+        const int j = __builtin_amdgcn_readlane(my_j, i);
+        const int p = __builtin_amdgcn_readlane(my_p, i);
+        const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
+        // previous block's LDS reads are complete before the DMA overwrites vs
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        dma_v(kv.v + base, tok_stride, lane, vs);
+        i16x8 kf[4][4];
+        load_k(kv.k + base, tok_stride, r, gq, kf);
+        __builtin_amdgcn_s_waitcnt(0);  // V in LDS and K in registers
+        __builtin_amdgcn_wave_barrier();
+        attend_block(kf, qf, scale2, j * kBlockSize, pos, len, vs, st);
+      }
+    } else {
+      // block i's K sits in kf and its V in buffer i & 1 (requested during
+      // block i - 1); only block i's loads are outstanding at the top.
       i16x8 kf[4][4];
-      load_k(kv.k + base, tok_stride, r, gq, kf);
-      __builtin_amdgcn_s_waitcnt(0);  // V in LDS and K in registers
-      __builtin_amdgcn_wave_barrier();
-      attend_block(kf, qf, scale2, j * kBlockSize, pos, len, vs, st);
+      {
+        const int p = __builtin_amdgcn_readlane(my_p, 0);
+        const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier LDS reads of the buffers done
+        __builtin_amdgcn_wave_barrier();
+        dma_v(kv.v + base, tok_stride, lane, vs_all[wave][0]);
+        load_k(kv.k + base, tok_stride, r, gq, kf);
+      }
+      for (int i = 0; i < cn; ++i) {
+        const int j = __builtin_amdgcn_readlane(my_j, i);
+        __builtin_amdgcn_s_waitcnt(0);  // block i: V in LDS, K in registers
+        __builtin_amdgcn_wave_barrier();
+        f32x4 sc[4];
+        block_logits(kf, qf, sc);
+        if (i + 1 < cn) {
+          const int pn = __builtin_amdgcn_readlane(my_p, i + 1);
+          const size_t nb = (size_t)pn * blk_elems + (size_t)g * kHeadDim;
+          // block i - 1's reads of the other buffer finished in its P V step
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+          __builtin_amdgcn_wave_barrier();
+          dma_v(kv.v + nb, tok_stride, lane, vs_all[wave][(i + 1) & 1]);
+          load_k(kv.k + nb, tok_stride, r, gq, kf);
+        }
+        block_softmax_pv(sc, scale2, j * kBlockSize, pos, len, vs_all[wave][i & 1], st);
+      }
     }
   }
 
   // ---- merge the four waves through LDS (reusing the V staging area)
   __syncthreads();
-  float* wo = reinterpret_cast<float*>(&vs_all[0][0]);  // [wave][16 heads][128]
+  float* wo = reinterpret_cast<float*>(&vs_all[0][0][0]);  // [wave][16 heads][128]
   if (gq == 0) {
     wm[wave][r] = st.m;
     wl[wave][r] = st.l;
@@ -339,10 +384,10 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   const float scale2 = scale * kLog2e;
   const dim3 grid(plan.splits, kv.num_kv_heads, Q.nq);
   if (plan.waves == 8) {
-    hipLaunchKernelGGL(sparse_attn_split<8>, grid, dim3(512), 0, st, kv, Q, idx, cnt, top_k,
+    hipLaunchKernelGGL((sparse_attn_split<8, 1>), grid, dim3(512), 0, st, kv, Q, idx, cnt, top_k,
                        scale2, plan.splits, out, lse, partials);
   } else {
-    hipLaunchKernelGGL(sparse_attn_split<4>, grid, dim3(256), 0, st, kv, Q, idx, cnt, top_k,
+    hipLaunchKernelGGL((sparse_attn_split<4, 2>), grid, dim3(256), 0, st, kv, Q, idx, cnt, top_k,
                        scale2, plan.splits, out, lse, partials);
   }
   hipError_t e = hipGetLastError();
