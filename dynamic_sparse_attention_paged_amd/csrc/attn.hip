@@ -35,6 +35,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kNumCUs = 256;   // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
@@ -43,15 +45,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ f32x4 mfma_bf16(i16x8 a, i16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs: round to nearest even
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
-  return __builtin_bit_cast(float, b << 16);
 }
 
 struct WaveState {
@@ -70,25 +63,35 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 // Loaded straight from global memory into LDS (16 B per lane, lane l of a
 // load landing at LDS offset 16 l), so V takes no registers.
 __device__ __forceinline__ void dma_v(const uint16_t* __restrict__ vbase, size_t tok_stride,
-                                      int lane, uint16_t* vs) {
-  const int row_in = lane >> 4;                 // token within the 4-row group
-  const int chunk = (lane & 15) ^ (2 * row_in);  // data chunk this lane fetches
+                                      uint32_t lane_off, uint16_t* vs) {
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    const uint16_t* src = vbase + (size_t)(4 * u + row_in) * tok_stride + 8 * chunk;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(vs + 512 * u), 16, 0, 0);
+    // uniform part (rows 4u ..) in scalar registers, lane part loop-invariant
+    const char* rows = reinterpret_cast<const char*>(vbase + (size_t)(4 * u) * tok_stride);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(rows + lane_off),
+                                     (lds_void_t*)(vs + 512 * u), 16, 0, 0);
   }
 }
 
-// K tile as MFMA A operands: k[T][c] = K[token 16T + r][dims 32c + 8gq .. +8]
+// Byte offset of lane l's 16 B of a V row group: token row l / 16 of the
+// group, chunk (l % 16) ^ 2 (row), the swizzle the transposed reads expect.
+__device__ __forceinline__ uint32_t dma_v_lane_offset(size_t tok_stride, int lane) {
+  const int row_in = lane >> 4;
+  const int chunk = (lane & 15) ^ (2 * row_in);
+  return (uint32_t)(((size_t)row_in * tok_stride + 8 * chunk) * 2);
+}
+
+// K tile as MFMA A operands: k[T][c] = K[token 16T + r][dims 32c + 8gq .. +8];
+// lane_off = (r * tok_stride + 8 gq) * 2 bytes.
 __device__ __forceinline__ void load_k(const uint16_t* __restrict__ kbase, size_t tok_stride,
-                                       int r, int gq, i16x8 (&kf)[4][4]) {
+                                       uint32_t lane_off, i16x8 (&kf)[4][4]) {
 #pragma unroll
-  for (int T = 0; T < 4; ++T)
+  for (int T = 0; T < 4; ++T) {
+    const char* rows = reinterpret_cast<const char*>(kbase + (size_t)(16 * T) * tok_stride);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      kf[T][c] = *reinterpret_cast<const i16x8*>(kbase + (size_t)(16 * T + r) * tok_stride +
-                                                 32 * c + 8 * gq);
+      kf[T][c] = *reinterpret_cast<const i16x8*>(rows + lane_off + 64 * c);
+  }
 }
 
 // S^T = K Q^T for one block: sc[T][i] is token 16T + 4gq + i of head r.
@@ -103,9 +106,10 @@ __device__ __forceinline__ void block_logits(const i16x8 (&kf)[4][4], const i16x
   }
 }
 
-// Online softmax over one block's logits and O^T += V^T P^T.
-__device__ __forceinline__ void block_softmax_pv(f32x4 (&sc)[4], float scale2, int tok0, int pos,
-                                                 int len, const uint16_t* vs, WaveState& st) {
+// Online softmax over one block's logits and O^T += V^T P^T.  Tokens a > lim
+// (past the query position or the sequence) are masked.
+__device__ __forceinline__ void block_softmax_pv(f32x4 (&sc)[4], float scale2, int tok0, int lim,
+                                                 const uint16_t* vs, WaveState& st) {
   const int lane = threadIdx.x & 63;
   const int gq = lane >> 4;
   // mask + scale (base 2); sc[T][i] is token 16T + 4gq + i of head r
@@ -115,27 +119,34 @@ __device__ __forceinline__ void block_softmax_pv(f32x4 (&sc)[4], float scale2, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int a = tok0 + 16 * T + 4 * gq + i;
-      const float x = (a <= pos && a < len) ? sc[T][i] * scale2 : -INFINITY;
+      const float x = (a <= lim) ? sc[T][i] * scale2 : -INFINITY;
       sc[T][i] = x;
       mx = fmaxf(mx, x);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // a block with no visible token leaves the state unchanged (-inf stays -inf)
   const float m_new = fmaxf(st.m, mx);
-  const float alpha = (st.m == -INFINITY) ? 0.f : exp2f(st.m - m_new);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);  // 0 while st.m = -inf
   float rs = 0.f;
   i16x8 ph[2], pl[2];
 #pragma unroll
   for (int T = 0; T < 4; ++T)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = sc[T][i];
-      const float p = (x == -INFINITY) ? 0.f : exp2f(x - m_new);
-      rs += p;
-      const uint32_t hb = f32_to_bf16_bits(p);
-      const uint32_t lb = f32_to_bf16_bits(p - bf16_bits_to_f32(hb));
-      ph[T >> 1][(T & 1) * 4 + i] = (short)hb;
-      pl[T >> 1][(T & 1) * 4 + i] = (short)lb;
+    for (int i = 0; i < 4; i += 2) {
+      // p = 2^(x - m) (0 for masked tokens), split p = hi + lo into two bf16
+      const f32x2 p = {__builtin_amdgcn_exp2f(sc[T][i] - m_use),
+                       __builtin_amdgcn_exp2f(sc[T][i + 1] - m_use)};
+      rs += p[0] + p[1];
+      const bf16x2 hb = __builtin_convertvector(p, bf16x2);  // round to nearest even
+      const f32x2 hf = __builtin_convertvector(hb, f32x2);
+      const bf16x2 lb = __builtin_convertvector(p - hf, bf16x2);
+      const uint32_t hw = __builtin_bit_cast(uint32_t, hb), lw = __builtin_bit_cast(uint32_t, lb);
+      ph[T >> 1][(T & 1) * 4 + i] = (short)(hw & 0xFFFFu);
+      ph[T >> 1][(T & 1) * 4 + i + 1] = (short)(hw >> 16);
+      pl[T >> 1][(T & 1) * 4 + i] = (short)(lw & 0xFFFFu);
+      pl[T >> 1][(T & 1) * 4 + i + 1] = (short)(lw >> 16);
     }
   rs += __shfl_xor(rs, 16, 64);
   rs += __shfl_xor(rs, 32, 64);
@@ -174,14 +185,14 @@ __device__ __forceinline__ void block_softmax_pv(f32x4 (&sc)[4], float scale2, i
 
 // One selected block for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x8 (&qf)[4],
-                                             float scale2, int tok0, int pos, int len,
-                                             const uint16_t* vs, WaveState& st) {
+                                             float scale2, int tok0, int lim, const uint16_t* vs,
+                                             WaveState& st) {
   f32x4 sc[4];
   block_logits(kf, qf, sc);
-  block_softmax_pv(sc, scale2, tok0, pos, len, vs, st);
+  block_softmax_pv(sc, scale2, tok0, lim, vs, st);
 }
 
-// grid (splits, Hkv, Nq), block 64 W.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
+// grid (splits, Nq, Hkv), block 64 W.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
 // kVBufs = 2: each wave double-buffers V in LDS, and the next block's K and V
 // are requested as soon as the current block's K has gone through the
 // logits MFMAs, so they arrive while the softmax and P V run.
@@ -193,8 +204,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   __shared__ uint16_t vs_all[kAttnWaves][kVBufs][64 * kHeadDim];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
 
-  const int sp = blockIdx.x, g = blockIdx.y, qi = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sp = blockIdx.x, qi = blockIdx.y, g = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform addresses
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15, gq = lane >> 4;
   const int G = Q.hq / kv.num_kv_heads;
   const int s = query_seq(Q, qi);
@@ -226,6 +238,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   const int32_t* trow = kv.table + (size_t)s * kv.maxb;
   const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
   const size_t blk_elems = (size_t)kBlockSize * tok_stride;
+  const int lim = min(pos, len - 1);  // last attended token
+  const uint32_t v_off = dma_v_lane_offset(tok_stride, lane);
+  const uint32_t k_off = (uint32_t)(((size_t)r * tok_stride + 8 * gq) * 2);
 
   // The wave's blocks are b0 + wave + 4 i.  Their logical ids and physical
   // blocks are fetched up front, one per lane (64 at a time), so that the
@@ -246,12 +261,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
         // previous block's LDS reads are complete before the DMA overwrites vs
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
-        dma_v(kv.v + base, tok_stride, lane, vs);
+        dma_v(kv.v + base, tok_stride, v_off, vs);
         i16x8 kf[4][4];
-        load_k(kv.k + base, tok_stride, r, gq, kf);
+        load_k(kv.k + base, tok_stride, k_off, kf);
         __builtin_amdgcn_s_waitcnt(0);  // V in LDS and K in registers
         __builtin_amdgcn_wave_barrier();
-        attend_block(kf, qf, scale2, j * kBlockSize, pos, len, vs, st);
+        attend_block(kf, qf, scale2, j * kBlockSize, lim, vs, st);
       }
     } else {
       // block i's K sits in kf and its V in buffer i & 1 (requested during
@@ -262,8 +277,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
         const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier LDS reads of the buffers done
         __builtin_amdgcn_wave_barrier();
-        dma_v(kv.v + base, tok_stride, lane, vs_all[wave][0]);
-        load_k(kv.k + base, tok_stride, r, gq, kf);
+        dma_v(kv.v + base, tok_stride, v_off, vs_all[wave][0]);
+        load_k(kv.k + base, tok_stride, k_off, kf);
       }
       for (int i = 0; i < cn; ++i) {
         const int j = __builtin_amdgcn_readlane(my_j, i);
@@ -277,10 +292,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
           // block i - 1's reads of the other buffer finished in its P V step
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
           __builtin_amdgcn_wave_barrier();
-          dma_v(kv.v + nb, tok_stride, lane, vs_all[wave][(i + 1) & 1]);
-          load_k(kv.k + nb, tok_stride, r, gq, kf);
+          dma_v(kv.v + nb, tok_stride, v_off, vs_all[wave][(i + 1) & 1]);
+          load_k(kv.k + nb, tok_stride, k_off, kf);
         }
-        block_softmax_pv(sc, scale2, j * kBlockSize, pos, len, vs_all[wave][i & 1], st);
+        block_softmax_pv(sc, scale2, j * kBlockSize, lim, vs_all[wave][i & 1], st);
       }
     }
   }
@@ -382,7 +397,9 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
                               const int32_t* cnt, int top_k, float scale, float* out, float* lse,
                               float* partials, AttnPlan plan, hipStream_t st) {
   const float scale2 = scale * kLog2e;
-  const dim3 grid(plan.splits, kv.num_kv_heads, Q.nq);
+  // KV head slowest: workgroups in flight together work on one head's blocks,
+  // so the blocks that many queries select stay in the last-level cache.
+  const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
   if (plan.waves == 8) {
     hipLaunchKernelGGL((sparse_attn_split<8, 1>), grid, dim3(512), 0, st, kv, Q, idx, cnt, top_k,
                        scale2, plan.splits, out, lse, partials);

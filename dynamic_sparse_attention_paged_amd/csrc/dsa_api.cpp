@@ -40,6 +40,9 @@ enum Need : unsigned {
 dsa_status check_common(const dsa_paged_kv* kv, const dsa_queries* qs, unsigned need) {
   if (!kv || !qs) return fail(DSA_ERR_NULL, "kv and qs must not be NULL");
   if (qs->num_queries < 0) return fail(DSA_ERR_SHAPE, "num_queries < 0");
+  if (qs->num_queries > 65535)
+    return fail(DSA_ERR_UNSUPPORTED, "num_queries %d: at most 65535 per call (one grid row per query)",
+                qs->num_queries);
   if (kv->block_size != dsa::kBlockSize)
     return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
   if (kv->head_dim != dsa::kHeadDim)

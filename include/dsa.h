@@ -85,7 +85,7 @@ typedef struct {
  * of every query; the chunk's K/V must already be in the cache.
  */
 typedef struct {
-  int32_t num_queries;         /* Nq >= 0 (0: every call is a no-op)                                */
+  int32_t num_queries;         /* 0 <= Nq <= 65535 (0: every call is a no-op)                       */
   int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads, Hq / Hkv <= 16                     */
   int32_t idx_heads;           /* indexer heads HI, 1..16                                            */
   const int32_t* q_seq;        /* int32 [Nq] or NULL                                                 */

@@ -74,6 +74,7 @@ def test_validation_errors(lib):
     assert _score(lib, _kv(), _qs(), scores=None) == E["DSA_ERR_NULL"]
     assert _score(lib, _kv(), _qs(num_queries=3)) == E["DSA_ERR_SHAPE"]  # decode: Nq > seqs
     assert _score(lib, _kv(num_blocks=0), _qs()) == E["DSA_ERR_SHAPE"]
+    assert _score(lib, _kv(), _qs(num_queries=65536)) == E["DSA_ERR_UNSUPPORTED"]  # grid rows
     assert _attn(lib, _kv(), _qs(num_q_heads=7)) == E["DSA_ERR_SHAPE"]  # Hq % Hkv
     assert _attn(lib, _kv(num_kv_heads=1), _qs(num_q_heads=32)) == E["DSA_ERR_UNSUPPORTED"]
     assert _attn(lib, _kv(), _qs(), top_k=0) == E["DSA_ERR_SHAPE"]
