@@ -293,10 +293,16 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
   int32_t* cnt = block_cnt_out ? block_cnt_out : reinterpret_cast<int32_t*>(ws + f.cnt);
   const dsa::KvView kvv = kv_view(kv);
   const dsa::QView qv = q_view(qs);
-  hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
-  if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
-  e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
-  if (e != hipSuccess) return hip_status(e, "fused: topk launch");
+  hipError_t e;
+  if (dsa::index_topk_fused_supported(kvv, qv)) {
+    e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
+  } else {
+    e = dsa::launch_index_score(kvv, qv, scores, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
+    e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: topk launch");
+  }
   const bool split = f.attn.plan.splits > 1;
   e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse,
                               split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr,
@@ -321,6 +327,9 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
   float* scores = static_cast<float*>(workspace);
   const dsa::KvView kvv = kv_view(kv);
   const dsa::QView qv = q_view(qs);
+  if (dsa::index_topk_fused_supported(kvv, qv))
+    return hip_status(dsa::launch_index_topk_fused(kvv, qv, top_k, block_idx, block_cnt, stream),
+                      "index_topk: fused launch");
   hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
   if (e != hipSuccess) return hip_status(e, "index_topk: score launch");
   return hip_status(dsa::launch_topk(scores, kvv, qv, top_k, block_idx, block_cnt, stream),

@@ -40,6 +40,11 @@ hipError_t launch_index_score(const KvView& kv, const QView& q, float* scores, h
 // Exact scoring of many queries on the int8 matrix cores (same results).
 bool index_score_mfma_supported(const KvView& kv, const QView& q);
 hipError_t launch_index_score_mfma(const KvView& kv, const QView& q, float* scores, hipStream_t s);
+// Scoring and Top-K of one query per workgroup, scores kept on chip (same
+// results as launch_index_score followed by launch_topk).
+bool index_topk_fused_supported(const KvView& kv, const QView& q);
+hipError_t launch_index_topk_fused(const KvView& kv, const QView& q, int top_k, int32_t* idx,
+                                   int32_t* cnt, hipStream_t s);
 hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, int top_k,
                        int32_t* idx, int32_t* cnt, hipStream_t s);
 

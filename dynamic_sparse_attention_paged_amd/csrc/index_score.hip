@@ -50,10 +50,26 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   const int gq = lane >> 4;
   const int j0 = blockIdx.x * kBlocksPerWg + wave * 16 * NB + (lane & 15);
   const int s = query_seq(Q, qi);
+  float* row = scores + (size_t)qi * kv.maxb;
+
+  // Block-table entries, key quarters and scales are requested first, before
+  // the query position is known (physical ids clamped into the pool, so the
+  // speculative reads stay in bounds), so that the table -> key chain
+  // overlaps the position read and the query prologue.
+  KeyQuarter<DI> kq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = min(j0 + 16 * b, kv.maxb - 1);
+    kq[b].p = min(max(kv.table[(size_t)s * kv.maxb + j], 0), kv.num_blocks - 1);
+    const uint4* krow =
+        reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)kq[b].p * DI + gq * (DI / 4));
+#pragma unroll
+    for (int i = 0; i < DI / 64; ++i) kq[b].w[i] = krow[i];
+    kq[b].ks = gq == 0 ? kv.idx_scale[kq[b].p] : 0.f;
+  }
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
   const int local = pos / kBlockSize;
-  float* row = scores + (size_t)qi * kv.maxb;
 
   // Workgroups whose blocks are all invisible only write -inf.
   if (blockIdx.x * kBlocksPerWg > local) {
@@ -64,17 +80,13 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
     }
     return;
   }
-  // Block-table entries, key quarters and scales are requested before the
-  // query prologue so that their latency overlaps it.
-  KeyQuarter<DI> kq[NB];
+  // invisible blocks score zero key words (their result is replaced by -inf)
   bool visible[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int j = j0 + 16 * b;
     visible[b] = j <= local && j < kv.maxb;
-    if (visible[b]) {
-      fetch_key_quarter<DI>(kv, s, j, gq, kq[b]);
-    } else {
+    if (!visible[b]) {
 #pragma unroll
       for (int i = 0; i < DI / 64; ++i) kq[b].w[i] = make_uint4(0u, 0u, 0u, 0u);
       kq[b].ks = 0.f;

@@ -97,9 +97,18 @@ __device__ __forceinline__ void wave_select(const uint32_t (&k)[M], uint32_t val
     const int L = __builtin_ffsll((long long)__ballot(hit)) - 1;
     const int dig = __builtin_amdgcn_readlane(4 * lane + d, L);
     const uint32_t cut = (uint32_t)__builtin_amdgcn_readlane((int)c, L);
+    const uint32_t in_bucket = (uint32_t)__builtin_amdgcn_readlane((int)hs[d], L);
     T |= (uint32_t)dig << sh;
     remaining -= cut;
     mask |= wmask;
+    if (in_bucket == remaining) {
+      // The whole digit bucket is kept: every key with this prefix is at
+      // least T (low bits zero), keys above it exceed T, keys below are
+      // under it.  Keep all keys equal to T.
+      T_out = T;
+      take_eq = 0xFFFFFFFFu;
+      return;
+    }
   }
   T_out = T;
   take_eq = remaining;

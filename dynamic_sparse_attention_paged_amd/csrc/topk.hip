@@ -176,12 +176,18 @@ __global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores
   const int lane = threadIdx.x;
   const int qi = blockIdx.x;
   const int s = query_seq(Q, qi);
+  const float* row = scores + (size_t)qi * kv.maxb;
+  // Unconditional loads from clamped (in-row) indices, issued before the
+  // query position is known, so all M are in flight with it; candidates past
+  // n are masked.
+  float v[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) v[m] = row[min(lane * M + m, kv.maxb - 1)];
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
   const int local = pos / kBlockSize;
   const int n = local;
   const int need = top_k - 1;
-  const float* row = scores + (size_t)qi * kv.maxb;
   int32_t* out = out_idx + (size_t)qi * top_k;
   if (n <= need) {
     for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
@@ -195,11 +201,6 @@ __global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores
     }
     return;
   }
-  // Unconditional loads from clamped (in-row) indices, so all M are in flight
-  // at once; candidates past n are masked.
-  float v[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) v[m] = row[min(lane * M + m, kv.maxb - 1)];
   uint32_t k[M], valid = 0u;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
