@@ -28,6 +28,7 @@
 #include <stdlib.h>
 
 #include "dsa_internal.h"
+#include "select_common.h"
 
 namespace dsa {
 namespace {
@@ -39,6 +40,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kNumCUs = 256;   // MI355X
+constexpr int kMaxSelectBlocks = 2048;  // selection inside attention: up to 2048 blocks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -196,13 +198,22 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
 // kVBufs = 2: each wave double-buffers V in LDS, and the next block's K and V
 // are requested as soon as the current block's K has gone through the
 // logits MFMAs, so they arrive while the softmax and P V run.
-template <int kAttnWaves, int kVBufs>
+//
+// kSelect: the selected blocks are not given but chosen here from the
+// query's scores (one wave, into LDS; the same rule as topk.hip), each
+// workgroup of the query repeating the cheap selection; workgroup (0, q, 0)
+// also writes them to idx_out / cnt_out when those are given.
+template <int kAttnWaves, int kVBufs, bool kSelect>
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    const float* __restrict__ scores, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
     int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ partials) {
   __shared__ uint16_t vs_all[kAttnWaves][kVBufs][64 * kHeadDim];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
+  __shared__ int32_t sel_lds[kSelect ? kMaxSelectBlocks : 1];
+  __shared__ uint4 hist4[kSelect ? 64 : 1];
+  __shared__ int cnt_lds;
 
   const int sp = blockIdx.x, qi = blockIdx.y, g = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform addresses
@@ -212,7 +223,34 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   const int s = query_seq(Q, qi);
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int n_sel = cnt[qi];
+  int n_sel;
+  const int32_t* sel;
+  if (kSelect) {
+    if (wave == 0) {
+      const int local = pos / kBlockSize;  // <= maxb - 1 < kMaxSelectBlocks
+      const float* row = scores + (size_t)qi * kv.maxb;
+      int c;
+      if (local <= 64 * 2) {
+        c = select_query_blocks<2>(row, kv.maxb, local, top_k, hist4, sel_lds);
+      } else if (local <= 64 * 8) {
+        c = select_query_blocks<8>(row, kv.maxb, local, top_k, hist4, sel_lds);
+      } else {
+        c = select_query_blocks<32>(row, kv.maxb, local, top_k, hist4, sel_lds);
+      }
+      if (lane == 0) cnt_lds = c;
+    }
+    __syncthreads();
+    n_sel = cnt_lds;
+    sel = sel_lds;
+    if (idx_out && sp == 0 && g == 0) {
+      for (int i = threadIdx.x; i < top_k; i += 64 * kAttnWaves)
+        idx_out[(size_t)qi * top_k + i] = sel_lds[i];
+      if (threadIdx.x == 0) cnt_out[qi] = n_sel;
+    }
+  } else {
+    n_sel = cnt[qi];
+    sel = idx + (size_t)qi * top_k;
+  }
   const int per = (top_k + splits - 1) / splits;
   const int b0 = sp * per, b1 = min(n_sel, b0 + per);
 
@@ -234,7 +272,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint16_t* vs = vs_all[wave][0];
-  const int32_t* sel = idx + (size_t)qi * top_k;
   const int32_t* trow = kv.table + (size_t)s * kv.maxb;
   const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
   const size_t blk_elems = (size_t)kBlockSize * tok_stride;
@@ -393,6 +430,13 @@ size_t attn_partials_bytes(int nq, int hq, int splits) {
   return (size_t)nq * hq * splits * (kHeadDim + 2) * sizeof(float);
 }
 
+hipError_t launch_merge(const QView& Q, const float* partials, int splits, float* out, float* lse,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(merge_splits, dim3(Q.nq * Q.hq), dim3(kHeadDim), 0, st, partials, splits, out,
+                     lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* idx,
                               const int32_t* cnt, int top_k, float scale, float* out, float* lse,
                               float* partials, AttnPlan plan, hipStream_t st) {
@@ -401,17 +445,33 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   // so the blocks that many queries select stay in the last-level cache.
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
   if (plan.waves == 8) {
-    hipLaunchKernelGGL((sparse_attn_split<8, 1>), grid, dim3(512), 0, st, kv, Q, idx, cnt, top_k,
-                       scale2, plan.splits, out, lse, partials);
+    hipLaunchKernelGGL((sparse_attn_split<8, 1, false>), grid, dim3(512), 0, st, kv, Q, idx, cnt,
+                       nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse, partials);
   } else {
-    hipLaunchKernelGGL((sparse_attn_split<4, 2>), grid, dim3(256), 0, st, kv, Q, idx, cnt, top_k,
-                       scale2, plan.splits, out, lse, partials);
+    hipLaunchKernelGGL((sparse_attn_split<4, 2, false>), grid, dim3(256), 0, st, kv, Q, idx, cnt,
+                       nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse, partials);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(merge_splits, dim3(Q.nq * Q.hq), dim3(kHeadDim), 0, st, partials,
-                     plan.splits, out, lse);
-  return hipGetLastError();
+  return launch_merge(Q, partials, plan.splits, out, lse, st);
+}
+
+bool attn_select_supported(const KvView& kv, const QView& Q, const AttnPlan& plan) {
+  return plan.waves == 4 && kv.maxb <= kMaxSelectBlocks && Q.nq >= 1;
+}
+
+hipError_t launch_sparse_attn_select(const KvView& kv, const QView& Q, const float* scores,
+                                     int top_k, float scale, float* out, float* lse,
+                                     float* partials, AttnPlan plan, int32_t* idx_out,
+                                     int32_t* cnt_out, hipStream_t st) {
+  const float scale2 = scale * kLog2e;
+  const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
+  hipLaunchKernelGGL((sparse_attn_split<4, 2, true>), grid, dim3(256), 0, st, kv, Q, nullptr,
+                     nullptr, scores, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
+                     partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  return launch_merge(Q, partials, plan.splits, out, lse, st);
 }
 
 }  // namespace dsa

@@ -293,19 +293,26 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
   int32_t* cnt = block_cnt_out ? block_cnt_out : reinterpret_cast<int32_t*>(ws + f.cnt);
   const dsa::KvView kvv = kv_view(kv);
   const dsa::QView qv = q_view(qs);
+  const bool split = f.attn.plan.splits > 1;
+  float* partials = split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr;
   hipError_t e;
   if (dsa::index_topk_fused_supported(kvv, qv)) {
+    // short contexts: scoring and selection in one kernel
     e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
   } else {
     e = dsa::launch_index_score(kvv, qv, scores, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
+    if (dsa::attn_select_supported(kvv, qv, f.attn.plan)) {
+      // the attention workgroups select their query's blocks themselves
+      e = dsa::launch_sparse_attn_select(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
+                                         f.attn.plan, block_idx_out, block_cnt_out, stream);
+      return hip_status(e, "fused: select + attention launch");
+    }
     e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
     if (e != hipSuccess) return hip_status(e, "fused: topk launch");
   }
-  const bool split = f.attn.plan.splits > 1;
-  e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse,
-                              split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr,
+  e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse, partials,
                               f.attn.plan, stream);
   return hip_status(e, "fused: attention launch");
 }

@@ -177,46 +177,11 @@ __global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores
   const int qi = blockIdx.x;
   const int s = query_seq(Q, qi);
   const float* row = scores + (size_t)qi * kv.maxb;
-  // Unconditional loads from clamped (in-row) indices, issued before the
-  // query position is known, so all M are in flight with it; candidates past
-  // n are masked.
-  float v[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) v[m] = row[min(lane * M + m, kv.maxb - 1)];
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos / kBlockSize;
-  const int n = local;
-  const int need = top_k - 1;
-  int32_t* out = out_idx + (size_t)qi * top_k;
-  if (n <= need) {
-    for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
-    if (lane == 0) out_cnt[qi] = local + 1;
-    return;
-  }
-  if (need == 0) {  // K = 1: the local block alone
-    if (lane == 0) {
-      out[0] = local;
-      out_cnt[qi] = 1;
-    }
-    return;
-  }
-  uint32_t k[M], valid = 0u;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    k[m] = order_key(v[m]);
-    valid |= (lane * M + m < n) ? (1u << m) : 0u;
-  }
-  uint32_t T, take_eq, o;
-  wave_select<M>(k, valid, (uint32_t)need, hist4, T, take_eq);
-  const uint32_t keep = wave_keep<M>(k, valid, T, take_eq, &o);
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-    if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = lane * M + m;
-  if (lane == 0) {
-    out[need] = local;  // largest visible id: last in ascending order
-    out_cnt[qi] = top_k;
-  }
+  const int c = select_query_blocks<M>(row, kv.maxb, pos / kBlockSize, top_k, hist4,
+                                       out_idx + (size_t)qi * top_k);
+  if (lane == 0) out_cnt[qi] = c;
 }
 
 // Two-level selection for long candidate lists (up to 16 * 64 * M, with
