@@ -143,6 +143,59 @@ def test_multi_sequence_prefill_stages(dsa, interleave):
     _run_all_stages(dsa, w, f"multi_prefill[{interleave}]")
 
 
+def _with(base, **fields):
+    import copy
+    v = copy.copy(base)
+    for k, val in fields.items():
+        setattr(v, k, val)
+    return v
+
+
+@pytest.mark.parametrize("lens,top_k", [((64 * 40 - 3, 64 * 9), 8),          # fused short-context path
+                                         ((64 * 700, 64 * 300 + 5), 16),     # selection inside attention
+                                         ((64 * 2600, 64 * 2100), 24)])      # separate Top-K kernel
+def test_ties_all_equal_scores(dsa, lens, top_k):
+    # every coarse key and scale equal: all visible blocks tie, so the lowest
+    # ids win (and the local block)
+    w = workload.small_decode(seed=2301, lens=lens, hq=16, hkv=2, hi=8, di=128, top_k=top_k)
+    keys = np.repeat(w.idx_keys[:1], w.idx_keys.shape[0], axis=0)
+    w = _with(w, idx_keys=keys, idx_scale=np.full_like(w.idx_scale, w.idx_scale[0]))
+    _say(f"ties: lens {lens} K={top_k}")
+    kv, qs, refs = _run_all_stages(dsa, w, "ties")
+    for r in refs:
+        n = r["cnt"]
+        loc = int(r["idx"][n - 1])
+        assert list(r["idx"][:n - 1]) == list(range(min(n - 1, loc)))  # oracle: lowest ids
+    out, lse, bi, bc = dsa.decode_fused(kv, qs, top_k, w.softmax_scale,
+                                        block_idx=torch.empty(w.num_queries, top_k, dtype=torch.int32,
+                                                              device="cuda"),
+                                        block_cnt=torch.empty(w.num_queries, dtype=torch.int32,
+                                                              device="cuda"))
+    torch.cuda.synchronize()
+    for qi, r in enumerate(refs):
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+
+
+def test_negative_head_weights(dsa):
+    # w of any sign: scores can be negative (ReLU is per head, before the weights)
+    w = workload.small_decode(seed=2302, lens=(64 * 300 + 17, 64 * 33), hq=16, hkv=2, hi=8,
+                              di=128, top_k=12)
+    ww = w.w.copy()
+    ww[:, ::2] *= -1.0
+    w = _with(w, w=ww)
+    _say("negative head weights")
+    _run_all_stages(dsa, w, "negative_w")
+
+
+def test_max_top_k(dsa):
+    # K = 2048 (the largest accepted): padding below 2048 visible blocks, a full
+    # selection above it
+    w = workload.small_decode(seed=2303, lens=(64 * 2048, 64 * 2400 - 7, 64 * 100), hq=8, hkv=1,
+                              hi=4, di=64, top_k=2048)
+    _say("K = 2048")
+    _run_all_stages(dsa, w, "max_top_k")
+
+
 def test_tiny_decode_config(dsa):
     w = workload.tiny_decode()
     _say("tiny_decode (1 x 4096, K 8)")
