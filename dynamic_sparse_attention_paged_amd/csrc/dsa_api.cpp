@@ -300,6 +300,10 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
     // short contexts: scoring and selection in one kernel
     e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
+  } else if (dsa::index_cand_topk_supported(kvv, qv, top_k)) {
+    // long contexts, small K: per-workgroup candidates, then a merge
+    e = dsa::launch_index_cand_topk(kvv, qv, top_k, scores, idx, cnt, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: index_cand_topk launch");
   } else {
     e = dsa::launch_index_score(kvv, qv, scores, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
@@ -337,6 +341,10 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
   if (dsa::index_topk_fused_supported(kvv, qv))
     return hip_status(dsa::launch_index_topk_fused(kvv, qv, top_k, block_idx, block_cnt, stream),
                       "index_topk: fused launch");
+  if (dsa::index_cand_topk_supported(kvv, qv, top_k))
+    return hip_status(dsa::launch_index_cand_topk(kvv, qv, top_k, scores, block_idx, block_cnt,
+                                                  stream),
+                      "index_topk: candidate launch");
   hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
   if (e != hipSuccess) return hip_status(e, "index_topk: score launch");
   return hip_status(dsa::launch_topk(scores, kvv, qv, top_k, block_idx, block_cnt, stream),

@@ -40,6 +40,12 @@ hipError_t launch_index_score(const KvView& kv, const QView& q, float* scores, h
 // Exact scoring of many queries on the int8 matrix cores (same results).
 bool index_score_mfma_supported(const KvView& kv, const QView& q);
 hipError_t launch_index_score_mfma(const KvView& kv, const QView& q, float* scores, hipStream_t s);
+// Scoring that keeps only each workgroup's Top-K candidates (in the score
+// workspace), then one merging wave per query: the same indices as
+// launch_index_score followed by launch_topk, for long lists and small K.
+bool index_cand_topk_supported(const KvView& kv, const QView& q, int top_k);
+hipError_t launch_index_cand_topk(const KvView& kv, const QView& q, int top_k, float* ws,
+                                  int32_t* idx, int32_t* cnt, hipStream_t s);
 // Scoring and Top-K of one query per workgroup, scores kept on chip (same
 // results as launch_index_score followed by launch_topk).
 bool index_topk_fused_supported(const KvView& kv, const QView& q);

@@ -28,18 +28,112 @@
 
 #include "dsa_internal.h"
 #include "score_common.h"
+#include "select_common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kScoreThreads = 256;
+constexpr int kMergeMaxCand = 2048;  // candidates the merging wave holds (32 per lane)
+
+// Candidate lists in the score workspace, per query q (nwg workgroups of
+// 256 blocks each): int32 counts [nwg], uint32 keys [nwg][need], int32 ids
+// [nwg][need].
+__host__ __device__ inline size_t cand_query_words(int nwg, int need) {
+  return (size_t)nwg * (1 + 2 * (size_t)need);
+}
+__device__ inline int32_t* cand_count(float* ws, int nwg, int need, int q) {
+  return reinterpret_cast<int32_t*>(ws) + (size_t)q * cand_query_words(nwg, need);
+}
+__device__ inline uint32_t* cand_keys(float* ws, int nwg, int need, int q) {
+  return reinterpret_cast<uint32_t*>(cand_count(ws, nwg, need, q) + nwg);
+}
+__device__ inline int32_t* cand_ids(float* ws, int nwg, int need, int q) {
+  return reinterpret_cast<int32_t*>(cand_keys(ws, nwg, need, q) + (size_t)nwg * need);
+}
+
+// One wave per query: the final need best of the workgroups' candidate lists
+// (concatenated in workgroup order, so in increasing id order), plus the
+// local block; the same rule as topk.hip.
+__global__ __launch_bounds__(64) void topk_merge_candidates(float* __restrict__ ws, KvView kv,
+                                                            QView Q, int top_k, int nwg,
+                                                            int32_t* __restrict__ out_idx,
+                                                            int32_t* __restrict__ out_cnt) {
+  constexpr int M = kMergeMaxCand / 64;
+  __shared__ uint32_t ck[kMergeMaxCand];
+  __shared__ int32_t cj[kMergeMaxCand];
+  __shared__ uint4 hist4[64];
+  const int lane = threadIdx.x;
+  const int qi = blockIdx.x;
+  const int s = query_seq(Q, qi);
+  const int len = kv.seq_lens[s];
+  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  const int local = pos / kBlockSize;
+  const int need = top_k - 1;
+  int32_t* out = out_idx + (size_t)qi * top_k;
+  if (local <= need) {
+    for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
+    if (lane == 0) out_cnt[qi] = local + 1;
+    return;
+  }
+  if (need == 0) {
+    if (lane == 0) {
+      out[0] = local;
+      out_cnt[qi] = 1;
+    }
+    return;
+  }
+  // compact the lists into LDS (lane w copies workgroup w's list)
+  int total = 0;
+  for (int w0 = 0; w0 < nwg; w0 += 64) {
+    const int w = w0 + lane;
+    const int cw = w < nwg ? cand_count(ws, nwg, need, qi)[w] : 0;
+    const uint32_t incl = wave_incl_scan((uint32_t)cw);
+    const int off = total + (int)incl - cw;
+    if (w < nwg) {
+      const uint32_t* kk = cand_keys(ws, nwg, need, qi) + (size_t)w * need;
+      const int32_t* jj = cand_ids(ws, nwg, need, qi) + (size_t)w * need;
+      for (int i = 0; i < cw; ++i) {
+        ck[off + i] = kk[i];
+        cj[off + i] = jj[i];
+      }
+    }
+    total += __builtin_amdgcn_readlane((int)incl, 63);
+  }
+  __syncthreads();
+  uint32_t k[M], valid = 0u;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int p = lane * M + m;
+    k[m] = p < total ? ck[p] : 0u;
+    valid |= (p < total) ? (1u << m) : 0u;
+  }
+  uint32_t T, take_eq, o;
+  wave_select<M>(k, valid, (uint32_t)need, hist4, T, take_eq);
+  const uint32_t keep = wave_keep<M>(k, valid, T, take_eq, &o);
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = cj[lane * M + m];
+  if (lane == 0) {
+    out[need] = local;
+    out_cnt[qi] = top_k;
+  }
+}
 
 // Lanes: 4 per block (dims DI/4 each); a lane holds NB blocks (16 apart), so a
 // wave covers 16 NB blocks and a workgroup 64 NB.
-template <int DI, int HP, int NB>
+//
+// kCand: instead of the score row, the workgroup writes its Top-K
+// candidates: the need best of its blocks below the local block (equal
+// scores to the lower id), as order-preserving keys and ids in increasing id
+// order, with their count (layout: cand_layout below).
+template <int DI, int HP, int NB, bool kCand>
 __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QView Q,
-                                                                   float* __restrict__ scores) {
+                                                                   float* __restrict__ scores,
+                                                                   int need) {
   __shared__ double qv[DI * HP];
+  __shared__ float scw[kCand ? 64 * NB : 1];
+  __shared__ uint4 hist4[kCand ? 64 : 1];
   __shared__ double sq[HP], wq[HP];
   __shared__ uint32_t amax_bits[HP];
   __shared__ int expo[HP];
@@ -71,8 +165,12 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
   const int local = pos / kBlockSize;
 
-  // Workgroups whose blocks are all invisible only write -inf.
+  // Workgroups whose blocks are all invisible only write -inf (or no candidates).
   if (blockIdx.x * kBlocksPerWg > local) {
+    if (kCand) {
+      if (threadIdx.x == 0) cand_count(scores, gridDim.x, need, qi)[blockIdx.x] = 0;
+      return;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int j = j0 + 16 * b;
@@ -95,11 +193,56 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   load_query<DI, HP>(Q, qi, qv, sq, wq, amax_bits, expo);
   float S[NB];
   score_quarters<DI, HP, NB>(kq, gq, qv, sq, wq, S);
+  if (!kCand) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int j = j0 + 16 * b;
-    if (gq == 0 && j < kv.maxb) row[j] = visible[b] ? S[b] : -INFINITY;
+    for (int b = 0; b < NB; ++b) {
+      const int j = j0 + 16 * b;
+      if (gq == 0 && j < kv.maxb) row[j] = visible[b] ? S[b] : -INFINITY;
+    }
+    return;
   }
+  // ---- candidates of this workgroup: blocks jbase + o, o < c (below local)
+  if (gq == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) scw[wave * 16 * NB + (lane & 15) + 16 * b] = S[b];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int jbase = blockIdx.x * kBlocksPerWg;
+  const int c = min(max(local - jbase, 0), kBlocksPerWg);
+  int32_t* cnt_out = cand_count(scores, gridDim.x, need, qi);
+  uint32_t* keys_out = cand_keys(scores, gridDim.x, need, qi) + (size_t)blockIdx.x * need;
+  int32_t* ids_out = cand_ids(scores, gridDim.x, need, qi) + (size_t)blockIdx.x * need;
+  uint32_t k[NB], valid = 0u;
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int o = lane * NB + m;
+    k[m] = order_key(scw[o]);
+    valid |= (o < c) ? (1u << m) : 0u;
+  }
+  if (c <= need) {  // all of them
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int o = lane * NB + m;
+      if (o < c) {
+        keys_out[o] = k[m];
+        ids_out[o] = jbase + o;
+      }
+    }
+    if (lane == 0) cnt_out[blockIdx.x] = c;
+    return;
+  }
+  uint32_t T, take_eq, o;
+  wave_select<NB>(k, valid, (uint32_t)need, hist4, T, take_eq);
+  const uint32_t keep = wave_keep<NB>(k, valid, T, take_eq, &o);
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+    if (((keep >> m) & 1u) && o < (uint32_t)need) {
+      keys_out[o] = k[m];
+      ids_out[o] = jbase + lane * NB + m;
+      ++o;
+    }
+  if (lane == 0) cnt_out[blockIdx.x] = need;
 }
 
 template <int DI, int HP>
@@ -110,14 +253,31 @@ hipError_t launch_t(const KvView& kv, const QView& Q, float* scores, hipStream_t
   const long pairs = (long)Q.nq * kv.maxb;
   if (pairs >= 256L * 256) {
     dim3 grid((kv.maxb + 255) / 256, Q.nq);
-    hipLaunchKernelGGL((index_score_exact<DI, HP, 4>), grid, dim3(kScoreThreads), 0, st, kv, Q,
-                       scores);
+    hipLaunchKernelGGL((index_score_exact<DI, HP, 4, false>), grid, dim3(kScoreThreads), 0, st, kv,
+                       Q, scores, 0);
   } else {
     dim3 grid((kv.maxb + 63) / 64, Q.nq);
-    hipLaunchKernelGGL((index_score_exact<DI, HP, 1>), grid, dim3(kScoreThreads), 0, st, kv, Q,
-                       scores);
+    hipLaunchKernelGGL((index_score_exact<DI, HP, 1, false>), grid, dim3(kScoreThreads), 0, st, kv,
+                       Q, scores, 0);
   }
   return hipGetLastError();
+}
+
+template <int DI, int HP>
+hipError_t launch_cand_t(const KvView& kv, const QView& Q, int need, float* ws, hipStream_t st) {
+  dim3 grid((kv.maxb + 255) / 256, Q.nq);
+  hipLaunchKernelGGL((index_score_exact<DI, HP, 4, true>), grid, dim3(kScoreThreads), 0, st, kv, Q,
+                     ws, need);
+  return hipGetLastError();
+}
+
+template <int DI>
+hipError_t launch_cand_di(const KvView& kv, const QView& Q, int need, float* ws, hipStream_t st) {
+  if (Q.hi <= 1) return launch_cand_t<DI, 1>(kv, Q, need, ws, st);
+  if (Q.hi <= 2) return launch_cand_t<DI, 2>(kv, Q, need, ws, st);
+  if (Q.hi <= 4) return launch_cand_t<DI, 4>(kv, Q, need, ws, st);
+  if (Q.hi <= 8) return launch_cand_t<DI, 8>(kv, Q, need, ws, st);
+  return launch_cand_t<DI, 16>(kv, Q, need, ws, st);
 }
 
 template <int DI>
@@ -130,6 +290,28 @@ hipError_t launch_di(const KvView& kv, const QView& Q, float* scores, hipStream_
 }
 
 }  // namespace
+
+bool index_cand_topk_supported(const KvView& kv, const QView& Q, int top_k) {
+  // long candidate lists (past what a selecting attention workgroup holds),
+  // few queries, and the candidate lists fit the score workspace and one
+  // merging wave
+  const int need = top_k - 1;
+  const int nwg = (kv.maxb + 255) / 256;
+  return kv.maxb > 2048 && need >= 1 && !index_score_mfma_supported(kv, Q) &&
+         (long)nwg * need <= kMergeMaxCand && cand_query_words(nwg, need) <= (size_t)kv.maxb;
+}
+
+hipError_t launch_index_cand_topk(const KvView& kv, const QView& Q, int top_k, float* ws,
+                                  int32_t* idx, int32_t* cnt, hipStream_t st) {
+  const int need = top_k - 1;
+  const int nwg = (kv.maxb + 255) / 256;
+  hipError_t e = kv.idx_dim == 64 ? launch_cand_di<64>(kv, Q, need, ws, st)
+                                  : launch_cand_di<128>(kv, Q, need, ws, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_candidates, dim3(Q.nq), dim3(64), 0, st, ws, kv, Q, top_k, nwg, idx,
+                     cnt);
+  return hipGetLastError();
+}
 
 hipError_t launch_index_score(const KvView& kv, const QView& Q, float* scores, hipStream_t st) {
   // many queries at once: the same scores from the int8 matrix cores
