@@ -244,7 +244,9 @@ def decode_extra(w, steps, nsets):
                path_gbps=round(byts / (ms * 1e-3) / 1e9, 1),
                path_frac_of_hbm=round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                attn_kernel_ms=round(attn_ms, 5),
-               attn_kernel_gbps=round(attn_bytes(w, cnt) / (attn_ms * 1e-3) / 1e9, 1))
+               attn_kernel_gbps=round(attn_bytes(w, cnt) / (attn_ms * 1e-3) / 1e9, 1),
+               attn_kernel_frac_of_hbm=round(attn_bytes(w, cnt) / (attn_ms * 1e-3) / 1e9 /
+                                             HBM_PEAK_GBPS, 4))
     del D
     torch.cuda.empty_cache()
     return res

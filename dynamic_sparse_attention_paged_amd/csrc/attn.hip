@@ -409,6 +409,12 @@ AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill) {
   // (eight waves per workgroup measured no faster than four for batched decode)
   a.waves = prefill ? 8 : 4;
   a.splits = 1;
+  if (!prefill && top_k <= 8 && units < kNumCUs) {
+    // at most eight blocks: one per wave of one eight-wave workgroup, with
+    // no split partials and no merge launch
+    a.waves = 8;
+    return a;
+  }
   if (!prefill && units > 0 && units < kNumCUs) {
     int splits = (int)((kNumCUs + units - 1) / units);
     const int max_splits = (top_k + a.waves - 1) / a.waves;  // >= one block per wave
