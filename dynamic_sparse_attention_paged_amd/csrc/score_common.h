@@ -35,35 +35,38 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 }
 
 // Quantize the query's indexer heads into LDS.  qv[d * HP + h] holds the
-// float64 value of the E4M3 code (zero for padded heads h >= hi).
+// float64 value of the E4M3 code (zero for padded heads h >= hi).  Each
+// head's max |q| is reduced by one wave (shuffles, no LDS atomics).
 template <int DI, int HP>
 __device__ void load_query(const QView& Q, int qi, double* qv, double* sq, double* w,
-                           uint32_t* amax_bits, int* expo) {
-  const int tid = threadIdx.x;
+                           uint32_t* /*unused*/, int* expo) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int hi = Q.hi;
   const uint16_t* src = Q.q_idx + (size_t)qi * hi * DI;
-  if (tid < HP) amax_bits[tid] = 0u;
-  __syncthreads();
-  for (int e = tid; e < hi * DI; e += blockDim.x) {
-    const float x = fabsf(bf16_to_f32(src[e]));
-    atomicMax(&amax_bits[e / DI], __builtin_bit_cast(uint32_t, x));
-  }
-  __syncthreads();
-  if (tid < HP) {
-    int e = 0;
-    double wh = 0.0;
-    if (tid < hi) {
-      const float a = __builtin_bit_cast(float, amax_bits[tid]);
-      if (a != 0.0f) {
-        int E;
-        const float f = frexpf(a, &E);  // a = f 2^E, f in [0.5, 1)
-        e = (f <= 0.875f) ? E - 9 : E - 8;
-      }
-      wh = (double)Q.w[(size_t)qi * hi + tid];
+  for (int h = wave; h < HP; h += nwaves) {
+    float a = 0.f;
+    if (h < hi) {
+#pragma unroll
+      for (int e = lane; e < DI; e += 64) a = fmaxf(a, fabsf(bf16_to_f32(src[h * DI + e])));
     }
-    expo[tid] = e;
-    sq[tid] = ldexp(1.0, e);
-    w[tid] = wh;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if (lane == 0) {
+      int e = 0;
+      double wh = 0.0;
+      if (h < hi) {
+        if (a != 0.0f) {
+          int E;
+          const float f = frexpf(a, &E);  // a = f 2^E, f in [0.5, 1)
+          e = (f <= 0.875f) ? E - 9 : E - 8;
+        }
+        wh = (double)Q.w[(size_t)qi * hi + h];
+      }
+      expo[h] = e;
+      sq[h] = ldexp(1.0, e);
+      w[h] = wh;
+    }
   }
   __syncthreads();
   for (int e = tid; e < DI * HP; e += blockDim.x) {
