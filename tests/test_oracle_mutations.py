@@ -1,0 +1,199 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of an oracle function (on the CPU,
+patched into every module that holds a reference to it) and checks that at
+least one of the pins in tests/test_oracle_*.py then fails.  The pins
+themselves pass on the real oracle (the rest of the suite).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.dsa as D
+import oracle.fp8 as F
+import oracle.pipeline as P
+from tests import test_oracle_attention as TA
+from tests import test_oracle_fp8 as TF
+from tests import test_oracle_score as TS
+from tests import test_oracle_select as TSEL
+
+_MODULES = (oracle, D, F, P, TA, TF, TS, TSEL)
+_real = {name: getattr(D, name, None) or getattr(F, name, None) or getattr(P, name)
+         for name in ("e4m3_decode", "e4m3_encode", "quantize_q_idx", "index_scores",
+                      "select_blocks", "visible_blocks", "_gather_tokens",
+                      "attention_partial", "merge_partials", "sparse_attention",
+                      "dense_attention", "score_query")}
+
+
+def _patch(monkeypatch, name, fn):
+    for m in _MODULES:
+        if hasattr(m, name):
+            monkeypatch.setattr(m, name, fn)
+
+
+# ---------------------------------------------------------------------------
+# mutants: each is the real function with one plausible mistake
+# ---------------------------------------------------------------------------
+def decode_wrong_bias(codes):
+    return _real["e4m3_decode"](codes) * 0.5  # exponent bias 8 instead of 7
+
+
+def encode_ties_away(x):
+    # nearest representable magnitude, ties to the larger one (not to even)
+    x = np.asarray(x, dtype=np.float64)
+    vals = _real["e4m3_decode"](np.arange(0x7F, dtype=np.uint8))  # +0 .. 448
+    a = np.minimum(np.abs(x), 448.0)
+    dist = np.abs(a[..., None] - vals)
+    best = dist.min(axis=-1, keepdims=True)
+    code = (np.where(dist == best, np.arange(0x7F), -1)).max(axis=-1)  # larger on ties
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def q_scale_not_power_of_two(q_idx):
+    q = np.asarray(q_idx, dtype=np.float64)
+    amax = np.max(np.abs(q), axis=-1)
+    scale = np.where(amax == 0.0, 1.0, amax / 448.0)
+    return _real["e4m3_encode"](q / scale[..., None]), scale
+
+
+def scores_without_relu(qc, sq, w, kc, ks, activation="relu"):
+    return _real["index_scores"](qc, sq, w, kc, ks, activation="identity")
+
+
+def scores_relu_after_head_sum(qc, sq, w, kc, ks, activation="relu"):
+    s = _real["index_scores"](qc, sq, w, kc, ks, activation="identity")
+    return np.where(s > 0.0, s, 0.0)
+
+
+def scores_ignore_key_scale(qc, sq, w, kc, ks, activation="relu"):
+    return _real["index_scores"](qc, sq, w, kc, np.ones_like(np.asarray(ks, np.float64)),
+                                 activation=activation)
+
+
+def select_ties_to_higher_id(cand, scores, local, top_k):
+    cand = np.asarray(cand, dtype=np.int64)
+    if cand.size <= top_k:
+        sel = np.sort(cand)
+    else:
+        others = [(j, s) for j, s in zip(cand.tolist(), np.asarray(scores).tolist()) if j != local]
+        others.sort(key=lambda js: (-js[1], -js[0]))
+        sel = np.sort(np.asarray([j for j, _ in others[:top_k - 1]] + [int(local)]))
+    out = np.full(top_k, -1, dtype=np.int32)
+    out[:sel.size] = sel
+    return out, int(sel.size)
+
+
+def select_local_not_forced(cand, scores, local, top_k):
+    cand = np.asarray(cand, dtype=np.int64)
+    order = sorted(zip(cand.tolist(), np.asarray(scores).tolist()), key=lambda js: (-js[1], js[0]))
+    sel = np.sort(np.asarray([j for j, _ in order[:top_k]], dtype=np.int64))
+    out = np.full(top_k, -1, dtype=np.int32)
+    out[:sel.size] = sel
+    return out, int(sel.size)
+
+
+def select_in_score_order(cand, scores, local, top_k):
+    idx, cnt = _real["select_blocks"](cand, scores, local, top_k)
+    pos = {int(j): i for i, j in enumerate(np.asarray(cand).tolist())}
+    s = np.asarray(scores)
+    head = sorted(idx[:cnt].tolist(), key=lambda j: (-s[pos[j]], j))
+    out = idx.copy()
+    out[:cnt] = head
+    return out, cnt
+
+
+def visible_off_by_one(pos, seq_len, block_size):
+    nb = -(-int(seq_len) // int(block_size))
+    j = np.arange(nb, dtype=np.int64)
+    return j[j * int(block_size) < int(pos)]  # drops a local block starting at pos
+
+
+def gather_ignores_causality(block_ids, table_row, pos, seq_len, block_size, k_block, v_block):
+    # tokens after the query inside its own block are not masked
+    return _real["_gather_tokens"](block_ids, table_row, seq_len - 1, seq_len, block_size, k_block,
+                                   v_block)
+
+
+def partial_wrong_gqa_grouping(q, K, V, softmax_scale, num_kv_heads):
+    q = np.asarray(q, dtype=np.float64)
+    hq = q.shape[0]
+    m, l, o = np.empty(hq), np.empty(hq), np.empty_like(q)
+    for h in range(hq):
+        g = h % num_kv_heads  # interleaved instead of contiguous groups
+        x = float(softmax_scale) * (K[:, g, :] @ q[h])
+        m[h] = x.max()
+        p = np.exp(x - m[h])
+        l[h] = p.sum()
+        o[h] = (p @ V[:, g, :]) / l[h]
+    return m, l, o
+
+
+def partial_without_scale(q, K, V, softmax_scale, num_kv_heads):
+    return _real["attention_partial"](q, K, V, 1.0, num_kv_heads)
+
+
+def merge_unweighted(parts):
+    o = sum(p[2] for p in parts) / len(parts)
+    m = np.max(np.stack([p[0] for p in parts]), axis=0)
+    return o, m + np.log(sum(p[1] * np.exp(p[0] - m) for p in parts))
+
+
+def sparse_lse_in_log2(q, block_ids, table_row, pos, seq_len, block_size, k_block, v_block,
+                       softmax_scale, num_kv_heads):
+    K, V, _ = D._gather_tokens(block_ids, table_row, pos, seq_len, block_size, k_block, v_block)
+    m, l, o = D.attention_partial(q, K, V, softmax_scale, num_kv_heads)
+    return o, m + np.log2(l)
+
+
+def dense_not_causal(q, table_row, pos, seq_len, block_size, k_block, v_block, softmax_scale,
+                     num_kv_heads):
+    return _real["dense_attention"](q, table_row, seq_len - 1, seq_len, block_size, k_block,
+                                    v_block, softmax_scale, num_kv_heads)
+
+
+def score_query_skips_table(q_idx, w, table_row, pos, seq_len, block_size, key_codes, key_scale,
+                            activation="relu"):
+    ident = np.arange(len(table_row))  # logical id used as the physical one
+    return _real["score_query"](q_idx, w, ident, pos, seq_len, block_size, key_codes, key_scale,
+                                activation=activation)
+
+
+CASES = [
+    ("e4m3_decode", decode_wrong_bias, ["TF.test_spot_codes"]),
+    ("e4m3_encode", encode_ties_away, ["TF.test_encode_ties_to_even",
+                                       "TF.test_encode_matches_brute_force_all_bf16"]),
+    ("quantize_q_idx", q_scale_not_power_of_two, ["TS.test_q_scale_closed_form_and_invariant"]),
+    ("index_scores", scores_without_relu, ["TS.test_scores_exact_integer_recomputation"]),
+    ("index_scores", scores_relu_after_head_sum, ["TS.test_scores_exact_integer_recomputation"]),
+    ("index_scores", scores_ignore_key_scale, ["TS.test_scores_exact_integer_recomputation"]),
+    ("select_blocks", select_ties_to_higher_id, ["TSEL.test_select_brute_force_random"]),
+    ("select_blocks", select_local_not_forced, ["TSEL.test_select_brute_force_random",
+                                                "TSEL.test_hand_examples_select"]),
+    ("select_blocks", select_in_score_order, ["TSEL.test_select_brute_force_random"]),
+    ("visible_blocks", visible_off_by_one, ["TSEL.test_visible_blocks_are_the_causal_prefix"]),
+    ("_gather_tokens", gather_ignores_causality,
+     ["TA.test_all_blocks_equals_dense_and_torch", "TA.test_hand_examples_attention"]),
+    ("attention_partial", partial_wrong_gqa_grouping, ["TA.test_all_blocks_equals_dense_and_torch"]),
+    ("attention_partial", partial_without_scale, ["TA.test_all_blocks_equals_dense_and_torch"]),
+    ("merge_partials", merge_unweighted, ["TA.test_merge_identity"]),
+    ("sparse_attention", sparse_lse_in_log2, ["TA.test_hand_examples_attention",
+                                              "TA.test_all_blocks_equals_dense_and_torch"]),
+    ("dense_attention", dense_not_causal, ["TA.test_all_blocks_equals_dense_and_torch"]),
+    ("score_query", score_query_skips_table, ["TS.test_scores_use_the_block_table"]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", CASES, ids=[c[1].__name__ for c in CASES])
+def test_pins_catch_mutant(monkeypatch, golden, name, mutant, pins):
+    _patch(monkeypatch, name, mutant)
+    mods = {"TA": TA, "TF": TF, "TS": TS, "TSEL": TSEL}
+    failures = 0
+    for pin in pins:
+        mod, fn = pin.split(".")
+        f = getattr(mods[mod], fn)
+        try:
+            f(golden) if "golden" in f.__code__.co_varnames[:f.__code__.co_argcount] else f()
+        except AssertionError:  # a pin's check failed (not a crash of the mutant)
+            failures += 1
+    assert failures > 0, f"no pin caught the mutant {mutant.__name__} of {name}"
