@@ -462,8 +462,10 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   return launch_merge(Q, partials, plan.splits, out, lse, st);
 }
 
-bool attn_select_supported(const KvView& kv, const QView& Q, const AttnPlan& plan) {
-  return plan.waves == 4 && kv.maxb <= kMaxSelectBlocks && Q.nq >= 1;
+bool attn_select_supported(const KvView& kv, const QView& Q, int top_k, const AttnPlan& plan) {
+  // the selection (top_k entries, -1 padded) and the candidates live in LDS
+  return plan.waves == 4 && kv.maxb <= kMaxSelectBlocks && top_k <= kMaxSelectBlocks &&
+         Q.nq >= 1;
 }
 
 hipError_t launch_sparse_attn_select(const KvView& kv, const QView& Q, const float* scores,

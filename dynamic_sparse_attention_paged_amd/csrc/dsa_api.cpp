@@ -307,7 +307,7 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
   } else {
     e = dsa::launch_index_score(kvv, qv, scores, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
-    if (dsa::attn_select_supported(kvv, qv, f.attn.plan)) {
+    if (dsa::attn_select_supported(kvv, qv, top_k, f.attn.plan)) {
       // the attention workgroups select their query's blocks themselves
       e = dsa::launch_sparse_attn_select(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
                                          f.attn.plan, block_idx_out, block_cnt_out, stream);

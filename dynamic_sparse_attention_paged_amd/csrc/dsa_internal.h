@@ -68,9 +68,9 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& q, const int32_t* i
                               float* partials, AttnPlan plan, hipStream_t s);
 // Decode attention that first selects each query's blocks from its scores
 // (scores as written by launch_index_score; the same selection as
-// launch_topk), for sequences of at most 2048 blocks.  idx_out / cnt_out may
-// be null.
-bool attn_select_supported(const KvView& kv, const QView& q, const AttnPlan& plan);
+// launch_topk), for sequences of at most 2048 blocks and top_k <= 2048.
+// idx_out / cnt_out may be null.
+bool attn_select_supported(const KvView& kv, const QView& q, int top_k, const AttnPlan& plan);
 hipError_t launch_sparse_attn_select(const KvView& kv, const QView& q, const float* scores,
                                      int top_k, float scale, float* out, float* lse,
                                      float* partials, AttnPlan plan, int32_t* idx_out,

@@ -187,13 +187,27 @@ def test_negative_head_weights(dsa):
     _run_all_stages(dsa, w, "negative_w")
 
 
-def test_max_top_k(dsa):
-    # K = 2048 (the largest accepted): padding below 2048 visible blocks, a full
-    # selection above it
-    w = workload.small_decode(seed=2303, lens=(64 * 2048, 64 * 2400 - 7, 64 * 100), hq=8, hkv=1,
-                              hi=4, di=64, top_k=2048)
-    _say("K = 2048")
-    _run_all_stages(dsa, w, "max_top_k")
+@pytest.mark.parametrize("lens,top_k", [((64 * 2048, 64 * 2400 - 7, 64 * 100), 2048),
+                                         ((64 * 2048 - 5, 64 * 1000), 2048),  # in-attention selection
+                                         ((64 * 2048, 64 * 1500 + 3, 64 * 90), 4096),
+                                         ((64 * 4200 + 1, 64 * 300), 4096)])
+def test_large_top_k(dsa, lens, top_k):
+    # large K up to 4096 (the largest accepted): padding below K visible blocks
+    # (every path, including the fused ones), a full selection above it
+    w = workload.small_decode(seed=2303, lens=lens, hq=8, hkv=1, hi=4, di=64, top_k=top_k)
+    _say(f"K = {top_k}, lens {lens}")
+    kv, qs, refs = _run_all_stages(dsa, w, "large_top_k")
+    nq = w.num_queries
+    bi = torch.empty(nq, top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, top_k, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    bi2, bc2 = dsa.index_topk(kv, qs, top_k)
+    torch.cuda.synchronize()
+    for qi, r in enumerate(refs):
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        assert np.array_equal(bi2[qi].cpu().numpy(), r["idx"]) and int(bc2[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"fused q{qi}: {a:.3e} {rel:.3e}"
 
 
 def test_tiny_decode_config(dsa):
