@@ -387,9 +387,12 @@ hipError_t launch_t(const KvView& kv, const QView& Q, float* scores, hipStream_t
 }  // namespace
 
 bool index_score_mfma_supported(const KvView& kv, const QView& Q) {
-  // many queries of one sequence (a prefill chunk); 4 or 8 indexer heads
-  return Q.q_seq != nullptr && Q.nq >= 256 && (Q.hi == 4 || Q.hi == 8) &&
-         (kv.idx_dim == 64 || kv.idx_dim == 128);
+  // many queries with explicit sequences and positions (a prefill chunk; the
+  // kernel walks the blocks once per distinct sequence of a workgroup), 4 or
+  // 8 indexer heads; a wave's score rows must fit one buffer resource (32-bit
+  // byte range)
+  return Q.q_seq != nullptr && Q.q_pos != nullptr && Q.nq >= 256 && (Q.hi == 4 || Q.hi == 8) &&
+         (kv.idx_dim == 64 || kv.idx_dim == 128) && kv.maxb <= (1 << 24);
 }
 
 hipError_t launch_index_score_mfma(const KvView& kv, const QView& Q, float* scores,
