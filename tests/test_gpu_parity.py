@@ -265,3 +265,54 @@ def test_run_to_run_bit_determinism(dsa):
     b = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)[0].clone()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def _random_decode_case(seed):
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hi = int(rng.integers(1, 17))
+    di = int(rng.choice([64, 128]))
+    nseq = int(rng.integers(1, 6))
+    # each sequence short, medium or long (ragged tails), independently
+    ranges = [(1, 64 * 40), (64 * 200, 64 * 2100), (64 * 2000, 64 * 5000)]
+    lens = tuple(int(rng.integers(*ranges[int(rng.integers(0, 3))])) for _ in range(nseq))
+    kind = int(rng.integers(0, 5))
+    top_k = [1, int(rng.integers(2, 9)), int(rng.integers(9, 65)), int(rng.integers(65, 300)),
+             int(rng.integers(300, 700))][kind]
+    return dict(seed=3000 + seed, lens=lens, hq=hkv * G, hkv=hkv, hi=hi, di=di, top_k=top_k)
+
+
+@pytest.mark.parametrize("seed", list(range(10)))
+def test_random_decode_configs(dsa, seed):
+    case = _random_decode_case(seed)
+    w = workload.small_decode(**case)
+    _say(f"random decode {case}")
+    kv, qs, refs = _run_all_stages(dsa, w, f"random[{seed}]")
+    K, nq = w.top_k, w.num_queries
+    bi = torch.empty(nq, K, dtype=torch.int32, device="cuda")
+    bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, K, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    bi2, bc2 = dsa.index_topk(kv, qs, K)
+    torch.cuda.synchronize()
+    for qi, r in enumerate(refs):
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        assert np.array_equal(bi2[qi].cpu().numpy(), r["idx"]) and int(bc2[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"fused q{qi}: {a:.3e} {rel:.3e}"
+
+
+@pytest.mark.parametrize("seed", list(range(4)))
+def test_random_prefill_configs(dsa, seed):
+    rng = np.random.default_rng(100 + seed)
+    hkv = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 4, 8]))
+    hi = int(rng.choice([3, 4, 8, 16])) if seed % 2 else int(rng.choice([4, 8]))
+    di = int(rng.choice([64, 128]))
+    L = int(rng.integers(64 * 50, 64 * 900))
+    count = int(rng.integers(256, 400)) if seed % 2 == 0 else int(rng.integers(20, 300))
+    top_k = int(rng.choice([1, int(rng.integers(2, 20)), int(rng.integers(20, 120))]))
+    w = workload.small_prefill(seed=3100 + seed, L=L, count=count, hq=hkv * G, hkv=hkv, hi=hi,
+                               di=di, top_k=top_k)
+    _say(f"random prefill L={L} count={count} hq={hkv * G} hkv={hkv} hi={hi} di={di} K={top_k}")
+    _run_all_stages(dsa, w, f"random_prefill[{seed}]")
