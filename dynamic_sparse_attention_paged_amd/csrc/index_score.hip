@@ -135,7 +135,6 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   __shared__ float scw[kCand ? 64 * NB : 1];
   __shared__ uint4 hist4[kCand ? 64 : 1];
   __shared__ double sq[HP], wq[HP];
-  __shared__ uint32_t amax_bits[HP];
   __shared__ int expo[HP];
   constexpr int kBlocksPerWg = 64 * NB;
 
@@ -190,7 +189,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
       kq[b].ks = 0.f;
     }
   }
-  load_query<DI, HP>(Q, qi, qv, sq, wq, amax_bits, expo);
+  load_query<DI, HP>(Q, qi, qv, sq, wq, expo);
   float S[NB];
   score_quarters<DI, HP, NB>(kq, gq, qv, sq, wq, S);
   if (!kCand) {

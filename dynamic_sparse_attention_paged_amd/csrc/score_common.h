@@ -38,8 +38,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 // float64 value of the E4M3 code (zero for padded heads h >= hi).  Each
 // head's max |q| is reduced by one wave (shuffles, no LDS atomics).
 template <int DI, int HP>
-__device__ void load_query(const QView& Q, int qi, double* qv, double* sq, double* w,
-                           uint32_t* /*unused*/, int* expo) {
+__device__ void load_query(const QView& Q, int qi, double* qv, double* sq, double* w, int* expo) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int hi = Q.hi;
