@@ -28,6 +28,7 @@
 #include <stdlib.h>
 
 #include "dsa_internal.h"
+#include "score_i8_lds.h"
 #include "select_common.h"
 
 namespace dsa {
@@ -41,6 +42,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kNumCUs = 256;   // MI355X
 constexpr int kMaxSelectBlocks = 2048;  // selection inside attention: up to 2048 blocks
+constexpr int kMaxScoredBlocks = 256;  // scoring inside attention: up to 256 blocks
+// where the attention kernel gets its blocks from (see sparse_attn_split)
+constexpr int kAttnGiven = 0, kAttnSelect = 1, kAttnScore = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -199,20 +203,31 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
 // are requested as soon as the current block's K has gone through the
 // logits MFMAs, so they arrive while the softmax and P V run.
 //
-// kSelect: the selected blocks are not given but chosen here from the
-// query's scores (one wave, into LDS; the same rule as topk.hip), each
-// workgroup of the query repeating the cheap selection; workgroup (0, q, 0)
-// also writes them to idx_out / cnt_out when those are given.
-template <int kAttnWaves, int kVBufs, bool kSelect>
+// kMode says where the selected blocks come from:
+//   kAttnGiven  idx / cnt, as written by the Top-K kernels;
+//   kAttnSelect chosen here from the query's scores (one wave, into LDS; the
+//               same rule as topk.hip), each workgroup of the query repeating
+//               the cheap selection;
+//   kAttnScore  scored here as well: the workgroup computes its query's exact
+//               indexer scores into LDS on the int8 matrix cores (the same
+//               values as index_score.hip, score_i8_lds.h), then selects as
+//               above; the block-table row stays in LDS for the gather.
+// With kAttnSelect / kAttnScore, workgroup (0, q, 0) also writes the
+// selection to idx_out / cnt_out when those are given.  DI and HP (index
+// key length, indexer heads rounded up to 4, 8 or 16) matter for kAttnScore only.
+template <int kAttnWaves, int kVBufs, int kMode, int DI, int HP>
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     const float* __restrict__ scores, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
     int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ partials) {
+  constexpr bool kSelects = kMode != kAttnGiven;
+  constexpr bool kScores = kMode == kAttnScore;
   __shared__ uint16_t vs_all[kAttnWaves][kVBufs][64 * kHeadDim];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
-  __shared__ int32_t sel_lds[kSelect ? kMaxSelectBlocks : 1];
-  __shared__ uint4 hist4[kSelect ? 64 : 1];
+  __shared__ int32_t sel_lds[kSelects ? kMaxSelectBlocks : 1];
+  __shared__ uint4 hist4[kSelects ? 64 : 1];
+  __shared__ int tab[kScores ? kMaxScoredBlocks : 1];
   __shared__ int cnt_lds;
 
   const int sp = blockIdx.x, qi = blockIdx.y, g = blockIdx.z;
@@ -221,11 +236,38 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   const int r = lane & 15, gq = lane >> 4;
   const int G = Q.hq / kv.num_kv_heads;
   const int s = query_seq(Q, qi);
+  constexpr int kDI = DI > 0 ? DI : 64;
+  constexpr int kHP = HP > 0 ? HP : 4;
+  QueryRows<kDI> qr;
+  if (kScores) qr.fetch(Q, qi, lane);  // first: the longest chain starts here
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
   int n_sel;
   const int32_t* sel;
-  if (kSelect) {
+  const int32_t* trow = kv.table + (size_t)s * kv.maxb;
+  if (kScores) {
+    // Scoring scratch (digit table, scores, head weights) lives in the V
+    // staging area, which is free until the gather starts.
+    uint32_t* lut = reinterpret_cast<uint32_t*>(&vs_all[0][0][0]);
+    float* sc = reinterpret_cast<float*>(lut + 256);
+    double* wsq = reinterpret_cast<double*>(sc + kMaxScoredBlocks);
+    const int local = pos / kBlockSize;  // <= maxb - 1 < kMaxScoredBlocks (host check)
+    for (int c = threadIdx.x; c < 256; c += 64 * kAttnWaves) lut[c] = digits_of_code((uint32_t)c);
+    for (int j = threadIdx.x; j <= local; j += 64 * kAttnWaves) tab[j] = trow[j];
+    __syncthreads();
+    i32x4 qa[kDI / 64][3];
+    qr.build(lut, lane, wave == 0, wsq, qa);
+    __syncthreads();
+    score_tiles_i8<kDI, kHP, kAttnWaves>(kv, qa, wave, lane, local, lut, tab, wsq, sc);
+    __syncthreads();
+    if (wave == 0) {
+      const int c = local <= 64 * 2 ? select_lds_blocks<2>(sc, local, top_k, hist4, sel_lds)
+                                    : select_lds_blocks<4>(sc, local, top_k, hist4, sel_lds);
+      if (lane == 0) cnt_lds = c;
+    }
+    trow = tab;
+  }
+  if (kMode == kAttnSelect) {
     if (wave == 0) {
       const int local = pos / kBlockSize;  // <= maxb - 1 < kMaxSelectBlocks
       const float* row = scores + (size_t)qi * kv.maxb;
@@ -239,6 +281,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       }
       if (lane == 0) cnt_lds = c;
     }
+  }
+  if (kSelects) {
     __syncthreads();
     n_sel = cnt_lds;
     sel = sel_lds;
@@ -272,7 +316,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint16_t* vs = vs_all[wave][0];
-  const int32_t* trow = kv.table + (size_t)s * kv.maxb;
   const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
   const size_t blk_elems = (size_t)kBlockSize * tok_stride;
   const int lim = min(pos, len - 1);  // last attended token
@@ -451,10 +494,10 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   // so the blocks that many queries select stay in the last-level cache.
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
   if (plan.waves == 8) {
-    hipLaunchKernelGGL((sparse_attn_split<8, 1, false>), grid, dim3(512), 0, st, kv, Q, idx, cnt,
+    hipLaunchKernelGGL((sparse_attn_split<8, 1, kAttnGiven, 0, 0>), grid, dim3(512), 0, st, kv, Q, idx, cnt,
                        nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse, partials);
   } else {
-    hipLaunchKernelGGL((sparse_attn_split<4, 2, false>), grid, dim3(256), 0, st, kv, Q, idx, cnt,
+    hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnGiven, 0, 0>), grid, dim3(256), 0, st, kv, Q, idx, cnt,
                        nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse, partials);
   }
   hipError_t e = hipGetLastError();
@@ -474,10 +517,70 @@ hipError_t launch_sparse_attn_select(const KvView& kv, const QView& Q, const flo
                                      int32_t* cnt_out, hipStream_t st) {
   const float scale2 = scale * kLog2e;
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
-  hipLaunchKernelGGL((sparse_attn_split<4, 2, true>), grid, dim3(256), 0, st, kv, Q, nullptr,
+  hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnSelect, 0, 0>), grid, dim3(256), 0, st, kv, Q, nullptr,
                      nullptr, scores, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
                      partials);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  return launch_merge(Q, partials, plan.splits, out, lse, st);
+}
+
+namespace {
+
+template <int kWaves, int kVBufs, int DI>
+hipError_t launch_scored_di(const KvView& kv, const QView& Q, int top_k, float scale2,
+                            float* out, float* lse, float* partials, int splits,
+                            int32_t* idx_out, int32_t* cnt_out, hipStream_t st) {
+  const dim3 grid(splits, Q.nq, kv.num_kv_heads), block(64 * kWaves);
+  if (Q.hi <= 4) {
+    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 4>), grid, block, 0, st,
+                       kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2, splits,
+                       out, lse, partials);
+  } else if (Q.hi <= 8) {
+    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 8>), grid, block, 0, st,
+                       kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2, splits,
+                       out, lse, partials);
+  } else {
+    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 16>), grid, block, 0,
+                       st, kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2,
+                       splits, out, lse, partials);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_score_supported(const KvView& kv, const QView& Q, int top_k, const AttnPlan& plan) {
+  // Every workgroup of a query repeats the query's scoring, so this pays only
+  // while that work is small and the grid is a single round of workgroups
+  // (measured: 32 queries x 64-256 blocks 3-4 us faster per step than a
+  // separate scoring launch; 512 blocks, or four rounds of workgroups, slower).
+  // The block-table row, the scores (in the V staging area) and the selection
+  // live in LDS.
+  const long wgs = (long)Q.nq * kv.num_kv_heads * plan.splits;
+  return (plan.waves == 4 || plan.waves == 8) && kv.maxb <= kMaxScoredBlocks && wgs <= kNumCUs &&
+         top_k <= kMaxSelectBlocks && (kv.idx_dim == 64 || kv.idx_dim == 128) && Q.hi >= 1 &&
+         Q.hi <= 16 && Q.nq >= 1 && !index_score_mfma_supported(kv, Q);
+}
+
+hipError_t launch_sparse_attn_score(const KvView& kv, const QView& Q, int top_k, float scale,
+                                    float* out, float* lse, float* partials, AttnPlan plan,
+                                    int32_t* idx_out, int32_t* cnt_out, hipStream_t st) {
+  const float scale2 = scale * kLog2e;
+  hipError_t e;
+  if (plan.waves == 8) {
+    e = kv.idx_dim == 64
+            ? launch_scored_di<8, 1, 64>(kv, Q, top_k, scale2, out, lse, partials, plan.splits,
+                                         idx_out, cnt_out, st)
+            : launch_scored_di<8, 1, 128>(kv, Q, top_k, scale2, out, lse, partials, plan.splits,
+                                          idx_out, cnt_out, st);
+  } else {
+    e = kv.idx_dim == 64
+            ? launch_scored_di<4, 2, 64>(kv, Q, top_k, scale2, out, lse, partials, plan.splits,
+                                         idx_out, cnt_out, st)
+            : launch_scored_di<4, 2, 128>(kv, Q, top_k, scale2, out, lse, partials, plan.splits,
+                                          idx_out, cnt_out, st);
+  }
   if (e != hipSuccess || plan.splits == 1) return e;
   return launch_merge(Q, partials, plan.splits, out, lse, st);
 }

@@ -296,6 +296,13 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
   const bool split = f.attn.plan.splits > 1;
   float* partials = split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr;
   hipError_t e;
+  if (dsa::attn_score_supported(kvv, qv, top_k, f.attn.plan)) {
+    // short contexts, small grids: every attention workgroup scores and
+    // selects its query's blocks itself, in one launch
+    e = dsa::launch_sparse_attn_score(kvv, qv, top_k, softmax_scale, out, lse, partials,
+                                      f.attn.plan, block_idx_out, block_cnt_out, stream);
+    return hip_status(e, "fused: score + select + attention launch");
+  }
   if (dsa::index_topk_fused_supported(kvv, qv)) {
     // short contexts: scoring and selection in one kernel
     e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);

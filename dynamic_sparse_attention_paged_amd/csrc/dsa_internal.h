@@ -75,5 +75,14 @@ hipError_t launch_sparse_attn_select(const KvView& kv, const QView& q, const flo
                                      int top_k, float scale, float* out, float* lse,
                                      float* partials, AttnPlan plan, int32_t* idx_out,
                                      int32_t* cnt_out, hipStream_t s);
+// Decode attention that first scores (exactly, on chip) and selects each
+// query's blocks itself: the same scores, selection and attention as
+// launch_index_score, launch_topk and launch_sparse_attn, in one launch, for
+// sequences of at most 256 blocks and grids of at most one workgroup per CU.
+// idx_out / cnt_out may be null.
+bool attn_score_supported(const KvView& kv, const QView& q, int top_k, const AttnPlan& plan);
+hipError_t launch_sparse_attn_score(const KvView& kv, const QView& q, int top_k, float scale,
+                                    float* out, float* lse, float* partials, AttnPlan plan,
+                                    int32_t* idx_out, int32_t* cnt_out, hipStream_t s);
 
 }  // namespace dsa

@@ -151,7 +151,7 @@ __device__ __forceinline__ uint32_t wave_keep(const uint32_t (&k)[M], uint32_t v
 // top_k - 1 best of candidates 0 .. local - 1 (fp32 scores row[0 .. local)),
 // equal scores going to the lower id; ids in increasing order to out[0 ..
 // cnt) (the local block last) and -1 up to top_k.  out may point to global
-// memory or LDS.  Requires local < 64 M when more than need candidates
+// memory or LDS.  Requires local <= 64 M when more than need candidates
 // exist.  Returns cnt.
 template <int M>
 __device__ __forceinline__ int select_query_blocks(const float* row, int maxb, int local,
@@ -184,6 +184,45 @@ __device__ __forceinline__ int select_query_blocks(const float* row, int maxb, i
   for (int m = 0; m < M; ++m)
     if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = lane * M + m;
   if (lane == 0) out[need] = local;  // largest visible id: last in ascending order
+  return top_k;
+}
+
+// LDS slot of candidate j's score when a query's scores are kept in LDS:
+// XOR-swizzled within each group of 32, so that one lane's reads of M
+// consecutive scores and the wave's reads of a row hit distinct banks.
+__device__ __forceinline__ int sc_slot(int j) { return j ^ ((j >> 5) & 31); }
+
+// select_query_blocks with the scores in LDS (slot sc_slot(j) of candidate
+// j): the same rule, output and return value.  Requires local <= 64 M when
+// more than top_k - 1 candidates exist.
+template <int M>
+__device__ __forceinline__ int select_lds_blocks(const float* sc, int local, int top_k,
+                                                 uint4* hist4, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int n = local;
+  const int need = top_k - 1;
+  if (n <= need) {
+    for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
+    return local + 1;
+  }
+  if (need == 0) {
+    if (lane == 0) out[0] = local;
+    return 1;
+  }
+  uint32_t k[M], valid = 0u;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = lane * M + m;
+    k[m] = c < n ? order_key(sc[sc_slot(c)]) : 0u;
+    valid |= (c < n) ? (1u << m) : 0u;
+  }
+  uint32_t T, take_eq, o;
+  wave_select<M>(k, valid, (uint32_t)need, hist4, T, take_eq);
+  const uint32_t keep = wave_keep<M>(k, valid, T, take_eq, &o);
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = lane * M + m;
+  if (lane == 0) out[need] = local;
   return top_k;
 }
 

@@ -302,6 +302,34 @@ def test_random_decode_configs(dsa, seed):
         assert good, f"fused q{qi}: {a:.3e} {rel:.3e}"
 
 
+@pytest.mark.parametrize("nq,hkv,top_k", [(40, 8, 16),   # 320 (query, KV head) workgroups
+                                           (24, 8, 32),   # 192 pairs x 2 splits: 384 workgroups
+                                           (3, 2, 9)])    # 6 pairs x 3 splits, in-attention scoring
+def test_fused_decode_short_context_paths(dsa, nq, hkv, top_k):
+    """Short contexts (<= 256 blocks) through the fused entry point: with at
+    most one workgroup per CU the attention workgroups score and select their
+    blocks themselves; with more, one workgroup per query scores and selects
+    first.  Both must give the oracle's indices and attention."""
+    rng = np.random.default_rng(nq * 7 + hkv)
+    lens = tuple(int(x) for x in rng.integers(1, 64 * 256 + 1, size=nq))
+    w = workload.small_decode(seed=2300 + nq, lens=lens, hq=8 * hkv, hkv=hkv, hi=8, di=128,
+                              top_k=top_k)
+    _say(f"fused short contexts nq={nq} hkv={hkv} K={top_k} maxb={w.block_table.shape[1]}")
+    kv, qs = parity.to_device(w)
+    bi = torch.empty(nq, top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, top_k, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    torch.cuda.synchronize()
+    for qi in range(nq):
+        r = parity.oracle_query(w, qi)
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"], \
+            f"q{qi}: {bi[qi].cpu().numpy()[:8]} vs {r['idx'][:8]}"
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"q{qi}: attention {a:.3e} {rel:.3e}"
+        la, _ = parity.attn_errors(lse[qi].cpu().numpy(), r["lse"])
+        assert la <= 1e-3, f"q{qi}: lse {la:.3e}"
+
+
 @pytest.mark.parametrize("seed", list(range(4)))
 def test_random_prefill_configs(dsa, seed):
     rng = np.random.default_rng(100 + seed)
