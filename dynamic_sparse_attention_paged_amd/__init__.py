@@ -20,7 +20,7 @@ from . import _lib
 
 __all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
            "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "index_topk",
-           "workspace_size", "make_workspace", "abi_version"]
+           "workspace_size", "make_workspace", "abi_version", "check_inputs"]
 
 
 class DSAError(RuntimeError):
@@ -60,8 +60,10 @@ class Queries:
 
     @property
     def num_queries(self):
-        t = self.q if self.q is not None else self.q_idx
-        return t.shape[0]
+        for t in (self.q, self.q_idx, self.q_pos, self.q_seq):
+            if t is not None:
+                return t.shape[0]
+        raise ValueError("Queries needs q, q_idx, q_pos or q_seq to know its size")
 
     def struct(self):
         def ptr(t):
@@ -226,3 +228,29 @@ def index_topk(kv, qs, top_k, block_idx=None, block_cnt=None, workspace=None):
                               block_cnt.data_ptr(), workspace.data_ptr(), workspace.numel(),
                               _stream(dev)))
     return block_idx, block_cnt
+
+
+def check_inputs(kv, qs, block_idx=None, block_cnt=None, top_k=0):
+    """Check the device-side contract (tables, lengths, positions and, when
+    given, a selection).  Returns the sorted names of the violated rules
+    (empty if none); waits for the check to finish."""
+    lib = _lib.load()
+    _check_tensors(kv.block_table, kv.seq_lens, qs.q_seq, qs.q_pos, block_idx, block_cnt)
+    dev = kv.block_table.device
+    flags = torch.empty(1, dtype=torch.int32, device=dev)
+    kvs, qss = _check_struct(kv), qs.struct()
+    _check(lib.dsa_check_inputs(ctypes.byref(kvs), ctypes.byref(qss),
+                                block_idx.data_ptr() if block_idx is not None else None,
+                                block_cnt.data_ptr() if block_cnt is not None else None,
+                                int(top_k), flags.data_ptr(), _stream(dev)))
+    f = int(flags.item()) & 0xFFFFFFFF
+    return sorted(name for bit, name in _lib.CHECK_FLAGS.items() if f & bit)
+
+
+def _check_struct(kv):
+    """PagedKV struct for the check: only the table, lengths and pool size matter."""
+    num_blocks = (kv.k_cache.shape[0] if kv.k_cache is not None else
+                  kv.idx_keys.shape[0] if kv.idx_keys is not None else 1)
+    return _lib.PagedKVStruct(None, None, None, None, kv.block_table.data_ptr(),
+                              kv.seq_lens.data_ptr(), num_blocks, 64, 1, 128, 64,
+                              kv.block_table.shape[0], kv.block_table.shape[1])

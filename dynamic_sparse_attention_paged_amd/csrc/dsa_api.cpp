@@ -358,4 +358,31 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
                     "index_topk: topk launch");
 }
 
+dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
+                            const int32_t* block_idx, const int32_t* block_cnt, int32_t top_k,
+                            uint32_t* flags, hipStream_t stream) {
+  if (!kv || !qs || !flags) return fail(DSA_ERR_NULL, "kv, qs and flags must not be NULL");
+  if (!aligned(flags, 4)) return fail(DSA_ERR_ALIGN, "flags needs 4 B alignment");
+  if (qs->num_queries < 0) return fail(DSA_ERR_SHAPE, "num_queries < 0");
+  if (kv->block_size != dsa::kBlockSize)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
+  if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1)
+    return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq must be >= 1");
+  if (!kv->block_table || !kv->seq_lens) return fail(DSA_ERR_NULL, "block_table/seq_lens NULL");
+  if (!qs->q_seq && qs->num_queries > kv->num_seqs)
+    return fail(DSA_ERR_SHAPE, "decode batch (q_seq NULL) needs num_queries <= num_seqs");
+  if ((block_idx == nullptr) != (block_cnt == nullptr))
+    return fail(DSA_ERR_NULL, "block_idx and block_cnt go together");
+  if (block_idx) {
+    dsa_status st = check_topk(top_k);
+    if (st != DSA_OK) return st;
+    if (!aligned(block_idx, 4) || !aligned(block_cnt, 4))
+      return fail(DSA_ERR_ALIGN, "block_idx/block_cnt need 4 B alignment");
+  }
+  dsa::KvView kvv = kv_view(kv);
+  dsa::QView qv = q_view(qs);
+  return hip_status(dsa::launch_check_inputs(kvv, qv, block_idx, block_cnt, top_k, flags, stream),
+                    "check_inputs launch");
+}
+
 }  // extern "C"

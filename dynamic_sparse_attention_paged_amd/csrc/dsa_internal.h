@@ -85,4 +85,10 @@ hipError_t launch_sparse_attn_score(const KvView& kv, const QView& q, int top_k,
                                     float* out, float* lse, float* partials, AttnPlan plan,
                                     int32_t* idx_out, int32_t* cnt_out, hipStream_t s);
 
+// Device-data check (check.hip): zeroes *flags, then ORs in the
+// DSA_CHECK_* bits of every violation.
+hipError_t launch_check_inputs(const KvView& kv, const QView& q, const int32_t* block_idx,
+                               const int32_t* block_cnt, int top_k, uint32_t* flags,
+                               hipStream_t s);
+
 }  // namespace dsa

@@ -192,6 +192,43 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
                           int32_t* block_idx, int32_t* block_cnt, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Device-data check.  The entry points above trust the device-side contract
+ * (conventions at the top of this file); this one checks it and is meant for
+ * debugging and for callers that receive tables or block lists from
+ * elsewhere.  It reads block_table, seq_lens, q_seq / q_pos when given, and
+ * block_idx / block_cnt when given, all within their declared shapes, and
+ * dereferences none of their values, so it is safe on any data.  It enqueues
+ * two small kernels on `stream`; once the stream reaches them, *flags (a
+ * device uint32, 4 B aligned) holds the OR of the DSA_CHECK_* bits of every
+ * violation found, 0 if none:
+ *   DSA_CHECK_SEQ_LEN    seq_lens[s] < 1 or > max_blocks_per_seq * block_size
+ *   DSA_CHECK_TABLE      a block holding tokens (j * block_size < seq_lens[s])
+ *                        has a table entry outside [0, num_blocks)
+ *   DSA_CHECK_Q_SEQ      q_seq[i] outside [0, num_seqs)
+ *   DSA_CHECK_Q_POS      the query position is outside [0, seq_lens[s])
+ *   DSA_CHECK_BLOCK_LIST a selection (as dsa_sparse_attn_decode / _prefill
+ *                        take it) breaks the rule of dsa_topk_blocks ([P1]
+ *                        section 4(1)): block_cnt[i] in 1..top_k, ids
+ *                        ascending and visible (j * block_size <= pos),
+ *                        the last one the local block pos / block_size,
+ *                        then -1 up to top_k
+ * block_idx / block_cnt: NULL to skip the list check (then top_k is unused),
+ * else int32 [Nq, top_k] / [Nq] with 1 <= top_k <= 4096.  Only block_table,
+ * seq_lens (and the queries' q_seq / q_pos) are required of kv / qs; no
+ * K/V, index keys or query vectors are read.
+ */
+enum {
+  DSA_CHECK_SEQ_LEN = 1,
+  DSA_CHECK_TABLE = 2,
+  DSA_CHECK_Q_SEQ = 4,
+  DSA_CHECK_Q_POS = 8,
+  DSA_CHECK_BLOCK_LIST = 16
+};
+dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
+                            const int32_t* block_idx, const int32_t* block_cnt, int32_t top_k,
+                            uint32_t* flags, hipStream_t stream);
+
 /* Workspace sizes.  op: one of the DSA_OP_* values. */
 enum { DSA_OP_ATTN_DECODE = 1, DSA_OP_DECODE_FUSED = 2, DSA_OP_INDEX_TOPK = 3 };
 dsa_status dsa_workspace_size(int op, const dsa_paged_kv* kv, const dsa_queries* qs,

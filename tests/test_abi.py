@@ -85,6 +85,24 @@ def test_validation_errors(lib):
                                        0.1, FAKE, None, None) == E["DSA_ERR_NULL"]  # q_seq/q_pos
 
 
+def test_check_inputs_validation(lib):
+    E = {v: k for k, v in _lib.STATUS.items()}
+
+    def chk(kv, qs, bi=None, bc=None, top_k=0, flags=FAKE):
+        return lib.dsa_check_inputs(ctypes.byref(kv) if kv is not None else None,
+                                    ctypes.byref(qs), bi, bc, top_k, flags, None)
+    assert chk(None, _qs()) == E["DSA_ERR_NULL"]
+    assert chk(_kv(), _qs(), flags=None) == E["DSA_ERR_NULL"]
+    assert chk(_kv(), _qs(), flags=FAKE + 2) == E["DSA_ERR_ALIGN"]
+    assert chk(_kv(block_table=None), _qs()) == E["DSA_ERR_NULL"]
+    assert chk(_kv(num_seqs=0), _qs()) == E["DSA_ERR_SHAPE"]
+    assert chk(_kv(block_size=32), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+    assert chk(_kv(), _qs(num_queries=3)) == E["DSA_ERR_SHAPE"]  # decode: Nq > seqs
+    assert chk(_kv(), _qs(), bi=FAKE) == E["DSA_ERR_NULL"]       # block_idx without block_cnt
+    assert chk(_kv(), _qs(), bi=FAKE, bc=FAKE, top_k=0) == E["DSA_ERR_SHAPE"]
+    assert chk(_kv(), _qs(), bi=FAKE + 1, bc=FAKE, top_k=4) == E["DSA_ERR_ALIGN"]
+
+
 def test_workspace_contract(lib):
     E = {v: k for k, v in _lib.STATUS.items()}
     kv, qs = _kv(), _qs()
