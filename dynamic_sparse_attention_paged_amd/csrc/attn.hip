@@ -223,7 +223,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     float* __restrict__ partials) {
   constexpr bool kSelects = kMode != kAttnGiven;
   constexpr bool kScores = kMode == kAttnScore;
-  __shared__ uint16_t vs_all[kAttnWaves][kVBufs][64 * kHeadDim];
+  // V staging: vs_a, and with kVBufs = 2 vs_b, one 16 KiB block per wave each
+  // (two arrays, so that the buffer being read and the one being filled are
+  // distinct objects)
+  __shared__ uint16_t vs_a[kAttnWaves][64 * kHeadDim];
+  __shared__ uint16_t vs_b[kVBufs == 2 ? kAttnWaves : 1][kVBufs == 2 ? 64 * kHeadDim : 8];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
   __shared__ int32_t sel_lds[kSelects ? kMaxSelectBlocks : 1];
   __shared__ uint4 hist4[kSelects ? 64 : 1];
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   if (kScores) {
     // Scoring scratch (digit table, scores, head weights) lives in the V
     // staging area, which is free until the gather starts.
-    uint32_t* lut = reinterpret_cast<uint32_t*>(&vs_all[0][0][0]);
+    uint32_t* lut = reinterpret_cast<uint32_t*>(&vs_a[0][0]);
     float* sc = reinterpret_cast<float*>(lut + 256);
     double* wsq = reinterpret_cast<double*>(sc + kMaxScoredBlocks);
     const int local = pos / kBlockSize;  // <= maxb - 1 < kMaxScoredBlocks (host check)
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* vs = vs_all[wave][0];
+  uint16_t* vs = vs_a[wave];
   const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
   const size_t blk_elems = (size_t)kBlockSize * tok_stride;
   const int lim = min(pos, len - 1);  // last attended token
@@ -349,40 +353,80 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
         attend_block(kf, qf, scale2, j * kBlockSize, lim, vs, st);
       }
     } else {
-      // block i's K sits in kf and its V in buffer i & 1 (requested during
-      // block i - 1); only block i's loads are outstanding at the top.
-      i16x8 kf[4][4];
-      {
-        const int p = __builtin_amdgcn_readlane(my_p, 0);
-        const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier LDS reads of the buffers done
+      // K two blocks ahead in registers (ka / kb), V one block ahead in LDS
+      // (vs_a / vs_b).  Issue order: K_0, V_0, K_1, then per block t, after
+      // its logits: V_{t+1}, K_{t+2}.  So at the top of every block but the
+      // last, exactly K_{t+1}'s 16 loads were issued after V_t, and vmcnt(16)
+      // means K_t and V_t have landed (vector memory counts complete in
+      // order); the last block waits for everything.  The order of these
+      // issues is pinned (compiler and scheduling barriers), and the waits are
+      // explicit because the LDS written by global_load_lds is not a register
+      // the compiler can track.  The step's V buffers are __restrict__: the
+      // one being filled is never the one being read, which keeps the
+      // compiler from draining every load before the P V reads.
+      i16x8 ka[4][4], kb[4][4];
+      auto base_of = [&](int t) {
+        const int p = __builtin_amdgcn_readlane(my_p, t);
+        return (size_t)p * blk_elems + (size_t)g * kHeadDim;
+      };
+      auto pin_order = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier LDS reads of the buffers done
+      __builtin_amdgcn_wave_barrier();
+      auto prime = [&](uint16_t* __restrict__ v0) {
+        const size_t b = base_of(0);
+        load_k(kv.k + b, tok_stride, k_off, ka);
+        pin_order();
+        dma_v(kv.v + b, tok_stride, v_off, v0);
+        pin_order();
+        if (cn > 1) load_k(kv.k + base_of(1), tok_stride, k_off, kb);
+        pin_order();
+      };
+      // a block with a successor
+      auto step = [&](int t, i16x8 (&kcur)[4][4], uint16_t* __restrict__ vcur,
+                      uint16_t* __restrict__ vnext) {
+        const int j = __builtin_amdgcn_readlane(my_j, t);
+        __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) lgkmcnt(0): K_t, V_t landed
         __builtin_amdgcn_wave_barrier();
-        dma_v(kv.v + base, tok_stride, v_off, vs_all[wave][0]);
-        load_k(kv.k + base, tok_stride, k_off, kf);
-      }
-      for (int i = 0; i < cn; ++i) {
-        const int j = __builtin_amdgcn_readlane(my_j, i);
-        __builtin_amdgcn_s_waitcnt(0);  // block i: V in LDS, K in registers
-        __builtin_amdgcn_wave_barrier();
+        pin_order();
         f32x4 sc[4];
-        block_logits(kf, qf, sc);
-        if (i + 1 < cn) {
-          const int pn = __builtin_amdgcn_readlane(my_p, i + 1);
-          const size_t nb = (size_t)pn * blk_elems + (size_t)g * kHeadDim;
-          // block i - 1's reads of the other buffer finished in its P V step
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-          __builtin_amdgcn_wave_barrier();
-          dma_v(kv.v + nb, tok_stride, v_off, vs_all[wave][(i + 1) & 1]);
-          load_k(kv.k + nb, tok_stride, k_off, kf);
-        }
-        block_softmax_pv(sc, scale2, j * kBlockSize, lim, vs_all[wave][i & 1], st);
+        block_logits(kcur, qf, sc);
+        // vnext was last read by block t - 1's P V, finished at the wait above
+        dma_v(kv.v + base_of(t + 1), tok_stride, v_off, vnext);
+        pin_order();
+        if (t + 2 < cn) load_k(kv.k + base_of(t + 2), tok_stride, k_off, kcur);
+        pin_order();
+        block_softmax_pv(sc, scale2, j * kBlockSize, lim, vcur, st);
+      };
+      auto last = [&](int t, i16x8 (&kcur)[4][4], uint16_t* vcur) {
+        const int j = __builtin_amdgcn_readlane(my_j, t);
+        __builtin_amdgcn_s_waitcnt(0);  // everything landed
+        __builtin_amdgcn_wave_barrier();
+        pin_order();
+        f32x4 sc[4];
+        block_logits(kcur, qf, sc);
+        block_softmax_pv(sc, scale2, j * kBlockSize, lim, vcur, st);
+      };
+      prime(vs_a[wave]);
+      int t = 0;
+      for (; t + 2 < cn; t += 2) {
+        step(t, ka, vs_a[wave], vs_b[wave]);
+        step(t + 1, kb, vs_b[wave], vs_a[wave]);
+      }
+      if (t + 1 < cn) {  // two blocks left
+        step(t, ka, vs_a[wave], vs_b[wave]);
+        last(t + 1, kb, vs_b[wave]);
+      } else {  // one block left
+        last(t, ka, vs_a[wave]);
       }
     }
   }
 
   // ---- merge the four waves through LDS (reusing the V staging area)
   __syncthreads();
-  float* wo = reinterpret_cast<float*>(&vs_all[0][0][0]);  // [wave][16 heads][128]
+  float* wo = reinterpret_cast<float*>(&vs_a[0][0]);  // [wave][16 heads][128]
   if (gq == 0) {
     wm[wave][r] = st.m;
     wl[wave][r] = st.l;
@@ -449,8 +493,10 @@ AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill) {
   // Enough (query, KV head) pairs to give every CU a workgroup: no split.
   // Otherwise the selected blocks are split across workgroups until every
   // CU has one.
-  // (eight waves per workgroup measured no faster than four for batched decode)
-  a.waves = prefill ? 8 : 4;
+  // Four waves, each double-buffering V (eight single-buffered waves measured
+  // no faster for batched decode and 13% slower for a chunked prefill of 8192
+  // queries, whose gather is latency-bound).
+  a.waves = 4;
   a.splits = 1;
   if (!prefill && top_k <= 8 && units < kNumCUs) {
     // at most eight blocks: one per wave of one eight-wave workgroup, with
