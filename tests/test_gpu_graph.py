@@ -14,8 +14,12 @@ def test_fused_decode_graph_replays_match_eager():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import dynamic_sparse_attention_paged_amd as dsa
+    # short contexts (scoring inside attention), mid-length (selection inside
+    # attention, split partials), long (per-workgroup candidates and a merge)
     for seed, kw in ((2301, {}), (2302, dict(hq=64, hkv=8, hi=8, top_k=32,
-                                            lens=(64 * 300, 64 * 90 + 5, 64 * 2)))):
+                                            lens=(64 * 300, 64 * 90 + 5, 64 * 2))),
+                     (2303, dict(hq=16, hkv=2, hi=8, top_k=16,
+                                 lens=(64 * 2600, 64 * 2100 + 3)))):
         w = workload.small_decode(seed=seed, **kw)
         kv, qs = parity.to_device(w)
         other = workload.with_query_seed(w, seed + 50)
@@ -43,3 +47,32 @@ def test_fused_decode_graph_replays_match_eager():
             torch.cuda.synchronize()
             for a, b in zip((out, lse, bi, bc), ref):
                 assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (seed, rep)
+
+
+def test_calls_on_a_side_stream_match_the_default_stream():
+    """Every entry point enqueues on the stream it is given (torch's current
+    stream in the binding): the same calls on a side stream give the same bits."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as dsa
+    w = workload.small_decode(seed=2304, hq=32, hkv=4, hi=8, top_k=12,
+                              lens=(64 * 700 + 9, 64 * 40, 64 * 3))
+    kv, qs = parity.to_device(w)
+    K = w.top_k
+
+    def run():
+        sc = dsa.index_score(kv, qs)
+        i, c = dsa.topk_blocks(sc, kv, qs, K)
+        o, l = dsa.sparse_attn_decode(kv, qs, i, c, K, w.softmax_scale)
+        fo, fl, _, _ = dsa.decode_fused(kv, qs, K, w.softmax_scale)
+        return sc, i, c, o, l, fo, fl
+
+    ref = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run()
+    side.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
