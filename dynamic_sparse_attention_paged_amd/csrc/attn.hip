@@ -27,6 +27,7 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include "cand_common.h"
 #include "dsa_internal.h"
 #include "score_i8_lds.h"
 #include "select_common.h"
@@ -44,7 +45,7 @@ constexpr int kNumCUs = 256;   // MI355X
 constexpr int kMaxSelectBlocks = 2048;  // selection inside attention: up to 2048 blocks
 constexpr int kMaxScoredBlocks = 256;  // scoring inside attention: up to 256 blocks
 // where the attention kernel gets its blocks from (see sparse_attn_split)
-constexpr int kAttnGiven = 0, kAttnSelect = 1, kAttnScore = 2;
+constexpr int kAttnGiven = 0, kAttnSelect = 1, kAttnScore = 2, kAttnCand = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -211,7 +212,10 @@ __device__ __forceinline__ void attend_block(const i16x8 (&kf)[4][4], const i16x
 //   kAttnScore  scored here as well: the workgroup computes its query's exact
 //               indexer scores into LDS on the int8 matrix cores (the same
 //               values as index_score.hip, score_i8_lds.h), then selects as
-//               above; the block-table row stays in LDS for the gather.
+//               above; the block-table row stays in LDS for the gather;
+//   kAttnCand   chosen here from the per-workgroup candidate lists of a long
+//               context (cand_common.h; `scores` points at the lists), merged
+//               by all waves with the same rule.
 // With kAttnSelect / kAttnScore, workgroup (0, q, 0) also writes the
 // selection to idx_out / cnt_out when those are given.  DI and HP (index
 // key length, indexer heads rounded up to 4, 8 or 16) matter for kAttnScore only.
@@ -284,6 +288,41 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
         c = select_query_blocks<32>(row, kv.maxb, local, top_k, hist4, sel_lds);
       }
       if (lane == 0) cnt_lds = c;
+    }
+  }
+  if (kMode == kAttnCand) {
+    const int local = pos / kBlockSize;
+    const int need = top_k - 1;
+    if (local <= need || need == 0) {  // uniform over the workgroup
+      if (wave == 0) {
+        const int c = need == 0 ? 1 : local + 1;
+        for (int i = lane; i < top_k; i += 64)
+          sel_lds[i] = need == 0 ? (i == 0 ? local : -1) : (i <= local ? i : -1);
+        if (lane == 0) cnt_lds = c;
+      }
+    } else {
+      // merge scratch in the V staging area, free until the gather starts
+      uint32_t* ck = reinterpret_cast<uint32_t*>(&vs_a[0][0]);
+      int32_t* cj = reinterpret_cast<int32_t*>(ck + kMergeMaxCand);
+      int* off = cj + kMergeMaxCand;
+      uint32_t* k2 = reinterpret_cast<uint32_t*>(off + kMergeMaxCand + 4);
+      int32_t* j2 = reinterpret_cast<int32_t*>(k2 + kMergeMaxCand);
+      int32_t* cpos = j2 + kMergeMaxCand;
+      int* n2 = cpos + kMergeMaxCand;
+      uint4* h4 = reinterpret_cast<uint4*>(n2 + 16);
+      static_assert((6 * kMergeMaxCand + 4 + 16) * 4 + kAttnWaves * 64 * 16 <=
+                        (int)sizeof(vs_a), "merge scratch fits the V staging area");
+      const CandScratch S{ck, cj, off, k2, j2, cpos, n2, h4};
+      const int nwg = (kv.maxb + kCandBlocks - 1) / kCandBlocks;
+      const int c = merge_candidate_lists<kAttnWaves>(const_cast<float*>(scores), nwg, need, qi,
+                                                      S, sel_lds);
+      if (wave == 0) {  // c == need: the lists hold at least need candidates below local
+        if (lane == 0) {
+          sel_lds[c] = local;
+          cnt_lds = c + 1;
+        }
+        for (int i = c + 1 + lane; i < top_k; i += 64) sel_lds[i] = -1;
+      }
     }
   }
   if (kSelects) {
@@ -627,6 +666,26 @@ hipError_t launch_sparse_attn_score(const KvView& kv, const QView& Q, int top_k,
             : launch_scored_di<4, 2, 128>(kv, Q, top_k, scale2, out, lse, partials, plan.splits,
                                           idx_out, cnt_out, st);
   }
+  if (e != hipSuccess || plan.splits == 1) return e;
+  return launch_merge(Q, partials, plan.splits, out, lse, st);
+}
+
+bool attn_cand_supported(const KvView& kv, const QView& Q, int top_k, const AttnPlan& plan) {
+  // the merge scratch lives in the V staging area of the four-wave kernel and
+  // the selection (top_k entries) in LDS
+  return plan.waves == 4 && top_k <= kMaxSelectBlocks && index_cand_topk_supported(kv, Q, top_k);
+}
+
+hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& Q, float* ws, int top_k,
+                                   float scale, float* out, float* lse, float* partials,
+                                   AttnPlan plan, int32_t* idx_out, int32_t* cnt_out,
+                                   hipStream_t st) {
+  const float scale2 = scale * kLog2e;
+  const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
+  hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnCand, 0, 0>), grid, dim3(256), 0, st, kv, Q,
+                     nullptr, nullptr, ws, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
+                     partials);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   return launch_merge(Q, partials, plan.splits, out, lse, st);
 }

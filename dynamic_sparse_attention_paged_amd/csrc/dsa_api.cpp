@@ -308,7 +308,15 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
     e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
   } else if (dsa::index_cand_topk_supported(kvv, qv, top_k)) {
-    // long contexts, small K: per-workgroup candidates, then a merge
+    // long contexts, small K: per-workgroup candidates, merged by the
+    // attention workgroups themselves, or else by a merging kernel first
+    if (dsa::attn_cand_supported(kvv, qv, top_k, f.attn.plan)) {
+      e = dsa::launch_index_cand_scores(kvv, qv, top_k, scores, stream);
+      if (e != hipSuccess) return hip_status(e, "fused: candidate scoring launch");
+      e = dsa::launch_sparse_attn_cand(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
+                                       f.attn.plan, block_idx_out, block_cnt_out, stream);
+      return hip_status(e, "fused: candidate merge + attention launch");
+    }
     e = dsa::launch_index_cand_topk(kvv, qv, top_k, scores, idx, cnt, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_cand_topk launch");
   } else {

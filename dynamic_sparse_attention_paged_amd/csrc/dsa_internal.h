@@ -46,6 +46,9 @@ hipError_t launch_index_score_mfma(const KvView& kv, const QView& q, float* scor
 bool index_cand_topk_supported(const KvView& kv, const QView& q, int top_k);
 hipError_t launch_index_cand_topk(const KvView& kv, const QView& q, int top_k, float* ws,
                                   int32_t* idx, int32_t* cnt, hipStream_t s);
+// Only the scoring kernel of launch_index_cand_topk: the candidate lists in ws.
+hipError_t launch_index_cand_scores(const KvView& kv, const QView& q, int top_k, float* ws,
+                                    hipStream_t s);
 // Scoring and Top-K of one query per workgroup, scores kept on chip (same
 // results as launch_index_score followed by launch_topk).
 bool index_topk_fused_supported(const KvView& kv, const QView& q);
@@ -84,6 +87,14 @@ bool attn_score_supported(const KvView& kv, const QView& q, int top_k, const Att
 hipError_t launch_sparse_attn_score(const KvView& kv, const QView& q, int top_k, float scale,
                                     float* out, float* lse, float* partials, AttnPlan plan,
                                     int32_t* idx_out, int32_t* cnt_out, hipStream_t s);
+// Decode attention that first merges each query's candidate lists (as left
+// by launch_index_cand_scores in ws) into its selection, the same as
+// launch_index_cand_topk's; for the lists launch_index_cand_topk takes.
+bool attn_cand_supported(const KvView& kv, const QView& q, int top_k, const AttnPlan& plan);
+hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& q, float* ws, int top_k,
+                                   float scale, float* out, float* lse, float* partials,
+                                   AttnPlan plan, int32_t* idx_out, int32_t* cnt_out,
+                                   hipStream_t s);
 
 // Device-data check (check.hip): zeroes *flags, then ORs in the
 // DSA_CHECK_* bits of every violation.

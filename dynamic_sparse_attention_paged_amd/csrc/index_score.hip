@@ -28,96 +28,54 @@
 
 #include "dsa_internal.h"
 #include "score_common.h"
+#include "cand_common.h"
 #include "select_common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kMergeMaxCand = 2048;  // candidates the merging wave holds (32 per lane)
 
-// Candidate lists in the score workspace, per query q (nwg workgroups of
-// 256 blocks each): int32 counts [nwg], uint32 keys [nwg][need], int32 ids
-// [nwg][need].
-__host__ __device__ inline size_t cand_query_words(int nwg, int need) {
-  return (size_t)nwg * (1 + 2 * (size_t)need);
-}
-__device__ inline int32_t* cand_count(float* ws, int nwg, int need, int q) {
-  return reinterpret_cast<int32_t*>(ws) + (size_t)q * cand_query_words(nwg, need);
-}
-__device__ inline uint32_t* cand_keys(float* ws, int nwg, int need, int q) {
-  return reinterpret_cast<uint32_t*>(cand_count(ws, nwg, need, q) + nwg);
-}
-__device__ inline int32_t* cand_ids(float* ws, int nwg, int need, int q) {
-  return reinterpret_cast<int32_t*>(cand_keys(ws, nwg, need, q) + (size_t)nwg * need);
-}
+constexpr int kMergeWaves = 16;
 
-// One wave per query: the final need best of the workgroups' candidate lists
-// (concatenated in workgroup order, so in increasing id order), plus the
-// local block; the same rule as topk.hip.
-__global__ __launch_bounds__(64) void topk_merge_candidates(float* __restrict__ ws, KvView kv,
-                                                            QView Q, int top_k, int nwg,
-                                                            int32_t* __restrict__ out_idx,
-                                                            int32_t* __restrict__ out_cnt) {
-  constexpr int M = kMergeMaxCand / 64;
-  __shared__ uint32_t ck[kMergeMaxCand];
-  __shared__ int32_t cj[kMergeMaxCand];
-  __shared__ uint4 hist4[64];
-  const int lane = threadIdx.x;
+// One workgroup per query: the local block plus the need best of the
+// workgroups' candidate lists (cand_common.h); the same rule as topk.hip.
+__global__ __launch_bounds__(64 * kMergeWaves) void topk_merge_candidates(
+    float* __restrict__ ws, KvView kv, QView Q, int top_k, int nwg, int32_t* __restrict__ out_idx,
+    int32_t* __restrict__ out_cnt) {
+  __shared__ uint32_t ck[kMergeMaxCand], k2[kMergeMaxCand];
+  __shared__ int32_t cj[kMergeMaxCand], j2[kMergeMaxCand], pos[kMergeMaxCand];
+  __shared__ int off[kMergeMaxCand + 1];
+  __shared__ int n2[kMergeWaves];
+  __shared__ uint4 hist4[kMergeWaves * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int qi = blockIdx.x;
   const int s = query_seq(Q, qi);
   const int len = kv.seq_lens[s];
-  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos / kBlockSize;
+  const int pos_q = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  const int local = pos_q / kBlockSize;
   const int need = top_k - 1;
   int32_t* out = out_idx + (size_t)qi * top_k;
-  if (local <= need) {
-    for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
-    if (lane == 0) out_cnt[qi] = local + 1;
+  if (local <= need) {  // uniform over the workgroup
+    for (int i = tid; i < top_k; i += 64 * kMergeWaves) out[i] = i <= local ? i : -1;
+    if (tid == 0) out_cnt[qi] = local + 1;
     return;
   }
   if (need == 0) {
-    if (lane == 0) {
+    if (tid == 0) {
       out[0] = local;
       out_cnt[qi] = 1;
     }
     return;
   }
-  // compact the lists into LDS (lane w copies workgroup w's list)
-  int total = 0;
-  for (int w0 = 0; w0 < nwg; w0 += 64) {
-    const int w = w0 + lane;
-    const int cw = w < nwg ? cand_count(ws, nwg, need, qi)[w] : 0;
-    const uint32_t incl = wave_incl_scan((uint32_t)cw);
-    const int off = total + (int)incl - cw;
-    if (w < nwg) {
-      const uint32_t* kk = cand_keys(ws, nwg, need, qi) + (size_t)w * need;
-      const int32_t* jj = cand_ids(ws, nwg, need, qi) + (size_t)w * need;
-      for (int i = 0; i < cw; ++i) {
-        ck[off + i] = kk[i];
-        cj[off + i] = jj[i];
-      }
-    }
-    total += __builtin_amdgcn_readlane((int)incl, 63);
-  }
-  __syncthreads();
-  uint32_t k[M], valid = 0u;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int p = lane * M + m;
-    k[m] = p < total ? ck[p] : 0u;
-    valid |= (p < total) ? (1u << m) : 0u;
-  }
-  uint32_t T, take_eq, o;
-  wave_select<M>(k, valid, (uint32_t)need, hist4, T, take_eq);
-  const uint32_t keep = wave_keep<M>(k, valid, T, take_eq, &o);
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-    if (((keep >> m) & 1u) && o < (uint32_t)need) out[o++] = cj[lane * M + m];
+  const CandScratch S{ck, cj, off, k2, j2, pos, n2, hist4};
+  const int c = merge_candidate_lists<kMergeWaves>(ws, nwg, need, qi, S, out);
+  if (tid >= 64) return;
   if (lane == 0) {
-    out[need] = local;
-    out_cnt[qi] = top_k;
+    out[c] = local;  // c == need: the lists hold at least need candidates below local
+    out_cnt[qi] = c + 1;
   }
+  for (int i = c + 1 + lane; i < top_k; i += 64) out[i] = -1;
 }
 
 // Lanes: 4 per block (dims DI/4 each); a lane holds NB blocks (16 apart), so a
@@ -264,7 +222,8 @@ hipError_t launch_t(const KvView& kv, const QView& Q, float* scores, hipStream_t
 
 template <int DI, int HP>
 hipError_t launch_cand_t(const KvView& kv, const QView& Q, int need, float* ws, hipStream_t st) {
-  dim3 grid((kv.maxb + 255) / 256, Q.nq);
+  static_assert(64 * 4 == kCandBlocks, "NB = 4: one list per 256-block workgroup");
+  dim3 grid((kv.maxb + kCandBlocks - 1) / kCandBlocks, Q.nq);
   hipLaunchKernelGGL((index_score_exact<DI, HP, 4, true>), grid, dim3(kScoreThreads), 0, st, kv, Q,
                      ws, need);
   return hipGetLastError();
@@ -295,20 +254,25 @@ bool index_cand_topk_supported(const KvView& kv, const QView& Q, int top_k) {
   // few queries, and the candidate lists fit the score workspace and one
   // merging wave
   const int need = top_k - 1;
-  const int nwg = (kv.maxb + 255) / 256;
+  const int nwg = (kv.maxb + kCandBlocks - 1) / kCandBlocks;
   return kv.maxb > 2048 && need >= 1 && !index_score_mfma_supported(kv, Q) &&
          (long)nwg * need <= kMergeMaxCand && cand_query_words(nwg, need) <= (size_t)kv.maxb;
 }
 
+hipError_t launch_index_cand_scores(const KvView& kv, const QView& Q, int top_k, float* ws,
+                                    hipStream_t st) {
+  const int need = top_k - 1;
+  return kv.idx_dim == 64 ? launch_cand_di<64>(kv, Q, need, ws, st)
+                          : launch_cand_di<128>(kv, Q, need, ws, st);
+}
+
 hipError_t launch_index_cand_topk(const KvView& kv, const QView& Q, int top_k, float* ws,
                                   int32_t* idx, int32_t* cnt, hipStream_t st) {
-  const int need = top_k - 1;
-  const int nwg = (kv.maxb + 255) / 256;
-  hipError_t e = kv.idx_dim == 64 ? launch_cand_di<64>(kv, Q, need, ws, st)
-                                  : launch_cand_di<128>(kv, Q, need, ws, st);
+  const int nwg = (kv.maxb + kCandBlocks - 1) / kCandBlocks;
+  hipError_t e = launch_index_cand_scores(kv, Q, top_k, ws, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_candidates, dim3(Q.nq), dim3(64), 0, st, ws, kv, Q, top_k, nwg, idx,
-                     cnt);
+  hipLaunchKernelGGL(topk_merge_candidates, dim3(Q.nq), dim3(64 * kMergeWaves), 0, st, ws, kv, Q,
+                     top_k, nwg, idx, cnt);
   return hipGetLastError();
 }
 

@@ -72,6 +72,11 @@ def test_topk_variants_long_lists(dsa, lens, top_k):
     _say(f"long lists {lens} K={top_k}")
     idx, cnt, out, lse = _fused(dsa, w)
     _check(w, range(w.num_queries), idx, cnt, out, lse, "long lists")
+    # scoring + selection alone (dsa_index_topk): the same lists
+    kv, qs = parity.to_device(w)
+    bi, bc = dsa.index_topk(kv, qs, top_k)
+    torch.cuda.synchronize()
+    assert np.array_equal(bi.cpu().numpy(), idx) and np.array_equal(bc.cpu().numpy(), cnt)
 
 
 def test_batched_decode_full(dsa):
