@@ -112,12 +112,12 @@ def workspace_size(op, kv, qs, top_k):
 
 
 def _workspace(nbytes, device):
-    # zero-filled once: the library keeps its ticket counters at zero between calls
+    # (the library needs no particular contents; zero-filled for reproducibility)
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def make_workspace(op, kv, qs, top_k):
-    """A zero-filled workspace for ``op`` (reusable across calls with the same sizes)."""
+    """A workspace for ``op``, reusable by later calls (of any sizes it covers)."""
     return _workspace(workspace_size(op, kv, qs, top_k), kv.block_table.device)
 
 

@@ -76,3 +76,32 @@ def test_calls_on_a_side_stream_match_the_default_stream():
     side.synchronize()
     for a, b in zip(got, ref):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_fused_workspace_reused_across_shapes():
+    """One workspace serves fused calls of different sizes, split counts and
+    paths in any order: each call equals the same call on a fresh workspace."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as dsa
+    cases = [workload.small_decode(seed=2305, hq=64, hkv=8, hi=8, top_k=32,
+                                   lens=(64 * 60, 64 * 33 - 5, 64 * 31)),          # scoring in attention
+             workload.small_decode(seed=2306, hq=16, hkv=2, hi=8, top_k=16,
+                                   lens=(64 * 2600, 64 * 2100 + 3)),               # candidate lists
+             workload.small_decode(seed=2307, hq=32, hkv=4, hi=4, top_k=24,
+                                   lens=(64 * 700, 64 * 300 + 1, 64 * 5, 64 * 900))]  # selection
+    dev = [parity.to_device(w) for w in cases]
+    fresh = []
+    for w, (kv, qs) in zip(cases, dev):
+        out, lse, _, _ = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale)
+        fresh.append((out.clone(), lse.clone()))
+    size = max(dsa.workspace_size(dsa._lib.OP_DECODE_FUSED, kv, qs, w.top_k)
+               for w, (kv, qs) in zip(cases, dev))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for rnd in range(3):
+        for k in ((0, 1, 2), (2, 0, 1), (1, 2, 0))[rnd]:
+            w, (kv, qs) = cases[k], dev[k]
+            out, lse, _, _ = dsa.decode_fused(kv, qs, w.top_k, w.softmax_scale, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), fresh[k][0].view(torch.int32)), (rnd, k)
+            assert torch.equal(lse.view(torch.int32), fresh[k][1].view(torch.int32)), (rnd, k)
