@@ -25,7 +25,6 @@
 // with the usual max / rescale rule; logits are kept in base 2.
 #include <hip/hip_runtime.h>
 #include <math.h>
-#include <stdlib.h>
 
 #include "cand_common.h"
 #include "dsa_internal.h"
@@ -548,13 +547,6 @@ AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill) {
     const int max_splits = (top_k + a.waves - 1) / a.waves;  // >= one block per wave
     a.splits = splits < max_splits ? splits : max_splits;
     if (a.splits < 1) a.splits = 1;
-  }
-  // Tuning override (same results, different launch shape): DSA_ATTN_SPLITS=n
-  if (!prefill) {
-    if (const char* e = getenv("DSA_ATTN_SPLITS")) {
-      const int n = atoi(e);
-      if (n >= 1) a.splits = n < top_k ? n : top_k;
-    }
   }
   return a;
 }
