@@ -108,6 +108,36 @@ def test_small_decode_stages(dsa, case):
         assert good, f"fused q{qi}: {a:.3e} {rel:.3e}"
 
 
+def _tiny_sweep():
+    cases = []
+    for nb in (1, 2, 3, 7, 64, 65):
+        for k in sorted({1, nb - 1, nb, nb + 3}):
+            if k >= 1:
+                cases.append((nb, k))
+    return cases
+
+
+@pytest.mark.parametrize("nb,top_k", _tiny_sweep(), ids=[f"nb{n}-K{k}" for n, k in _tiny_sweep()])
+def test_tiny_sweep_stages(dsa, nb, top_k):
+    """Every stage in isolation and the fused entry points, for sequences of
+    nb blocks (full, a ragged last block, and one token into the last block)
+    and K below, at and above the number of visible blocks."""
+    lens = sorted({nb * 64, max(1, nb * 64 - 5), (nb - 1) * 64 + 1})
+    w = workload.small_decode(seed=2500 + 7 * nb + top_k, lens=tuple(lens), hq=16, hkv=2, hi=4,
+                              di=128, top_k=top_k)
+    kv, qs, refs = _run_all_stages(dsa, w, f"sweep nb={nb} K={top_k}")
+    bi = torch.empty(w.num_queries, top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, top_k, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    bi2, bc2 = dsa.index_topk(kv, qs, top_k)
+    torch.cuda.synchronize()
+    for qi, r in enumerate(refs):
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        assert np.array_equal(bi2[qi].cpu().numpy(), r["idx"]) and int(bc2[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"fused q{qi}: {a:.3e} {rel:.3e}"
+
+
 @pytest.mark.parametrize("seed,count,L,top_k", [(2101, 200, 64 * 20 - 5, 6),
                                                 (2102, 130, 64 * 3 + 1, 2),
                                                 (2103, 257, 64 * 40, 64)])
