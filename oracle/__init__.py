@@ -31,6 +31,9 @@ What the pages fix, and what the oracle follows:
   * sparse attention is full attention restricted to the index-selected pairs
     ([P4] "Deep Integration of Sparse Attention and Vision Computation", the
     full-vs-sparse table).
+  * the write path: tokens' K/V rows go to their blocks through the table,
+    and each block's coarse key is stored as E4M3 codes with a per-block
+    float32 scale ([P5] "KV Cache Layout"; [P1] section 4(2)); write.py.
 
 Where the pages are silent the oracle takes the plainest reading; each reading
 is named in the function that uses it.  Parity pins: every function in this
@@ -51,6 +54,7 @@ from .dsa import (
     merge_partials,
     attention_partial,
 )
+from .write import kv_write, quantize_coarse_key
 
 __all__ = [
     "e4m3_decode",
@@ -58,6 +62,8 @@ __all__ = [
     "bf16_bits_to_f64",
     "E4M3_MAX",
     "quantize_q_idx",
+    "kv_write",
+    "quantize_coarse_key",
     "visible_blocks",
     "local_block",
     "index_scores",

@@ -13,17 +13,20 @@ import oracle
 import oracle.dsa as D
 import oracle.fp8 as F
 import oracle.pipeline as P
+import oracle.write as W
 from tests import test_oracle_attention as TA
 from tests import test_oracle_fp8 as TF
 from tests import test_oracle_score as TS
 from tests import test_oracle_select as TSEL
+from tests import test_oracle_write as TW
 
-_MODULES = (oracle, D, F, P, TA, TF, TS, TSEL)
-_real = {name: getattr(D, name, None) or getattr(F, name, None) or getattr(P, name)
+_MODULES = (oracle, D, F, P, W, TA, TF, TS, TSEL, TW)
+_real = {name: getattr(D, name, None) or getattr(F, name, None) or getattr(P, name, None)
+         or getattr(W, name)
          for name in ("e4m3_decode", "e4m3_encode", "quantize_q_idx", "index_scores",
                       "select_blocks", "visible_blocks", "_gather_tokens",
                       "attention_partial", "merge_partials", "sparse_attention",
-                      "dense_attention", "score_query")}
+                      "dense_attention", "score_query", "quantize_coarse_key", "kv_write")}
 
 
 def _patch(monkeypatch, name, fn):
@@ -159,6 +162,39 @@ def score_query_skips_table(q_idx, w, table_row, pos, seq_len, block_size, key_c
                                 activation=activation)
 
 
+def coarse_key_scale_240(x):
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) or np.float32(1.0)
+    ks = np.float32(amax / np.float32(240.0))  # the E4M3 range taken as 240
+    y = np.clip((x / ks).astype(np.float32), -448.0, 448.0)
+    return F.e4m3_encode(y.astype(np.float64)), ks
+
+
+def coarse_key_power_of_two_scale(x):
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.max(np.abs(x))) or 1.0
+    ks = np.float32(2.0 ** np.ceil(np.log2(amax / 448.0)))  # the query's rule instead
+    y = np.clip((x / ks).astype(np.float32), -448.0, 448.0)
+    return F.e4m3_encode(y.astype(np.float64)), ks
+
+
+def coarse_key_truncated(x):
+    codes, ks = _real["quantize_coarse_key"](x)
+    y = np.clip((np.asarray(x, np.float32) / ks).astype(np.float32), -448.0, 448.0)
+    v = F.e4m3_decode(codes)
+    over = np.abs(v) > np.abs(y)  # round toward zero instead of to nearest
+    down = np.where(codes & 0x7F, codes - 1, codes).astype(np.uint8)
+    return np.where(over, down, codes).astype(np.uint8), ks
+
+
+def kv_write_position_off_by_one(k_pool, v_pool, table, seq_lens, tok_seq, tok_pos, k_new,
+                                 v_new, block_size):
+    pos = None if tok_pos is None else np.maximum(np.asarray(tok_pos) - 1, 0)
+    lens = np.asarray(seq_lens) - (1 if tok_pos is None else 0)
+    return _real["kv_write"](k_pool, v_pool, table, np.maximum(lens, 1), tok_seq, pos, k_new,
+                             v_new, block_size)
+
+
 CASES = [
     ("e4m3_decode", decode_wrong_bias, ["TF.test_spot_codes"]),
     ("e4m3_encode", encode_ties_away, ["TF.test_encode_ties_to_even",
@@ -181,13 +217,19 @@ CASES = [
                                               "TA.test_all_blocks_equals_dense_and_torch"]),
     ("dense_attention", dense_not_causal, ["TA.test_all_blocks_equals_dense_and_torch"]),
     ("score_query", score_query_skips_table, ["TS.test_scores_use_the_block_table"]),
+    ("quantize_coarse_key", coarse_key_scale_240, ["TW.test_hand_examples_coarse_key",
+                                                   "TW.test_largest_entry_and_error_bound"]),
+    ("quantize_coarse_key", coarse_key_power_of_two_scale, ["TW.test_hand_examples_coarse_key"]),
+    ("quantize_coarse_key", coarse_key_truncated, ["TW.test_codes_match_torch_float8_conversion",
+                                                   "TW.test_largest_entry_and_error_bound"]),
+    ("kv_write", kv_write_position_off_by_one, ["TW.test_kv_write_round_trip"]),
 ]
 
 
 @pytest.mark.parametrize("name,mutant,pins", CASES, ids=[c[1].__name__ for c in CASES])
 def test_pins_catch_mutant(monkeypatch, golden, name, mutant, pins):
     _patch(monkeypatch, name, mutant)
-    mods = {"TA": TA, "TF": TF, "TS": TS, "TSEL": TSEL}
+    mods = {"TA": TA, "TF": TF, "TS": TS, "TSEL": TSEL, "TW": TW}
     failures = 0
     for pin in pins:
         mod, fn = pin.split(".")
