@@ -20,7 +20,8 @@ from . import _lib
 
 __all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
            "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "index_topk",
-           "workspace_size", "make_workspace", "abi_version", "check_inputs"]
+           "workspace_size", "make_workspace", "abi_version", "check_inputs",
+           "kv_write", "index_key_write"]
 
 
 class DSAError(RuntimeError):
@@ -254,3 +255,28 @@ def _check_struct(kv):
     return _lib.PagedKVStruct(None, None, None, None, kv.block_table.data_ptr(),
                               kv.seq_lens.data_ptr(), num_blocks, 64, 1, 128, 64,
                               kv.block_table.shape[0], kv.block_table.shape[1])
+
+
+def kv_write(kv, k_new, v_new, tok_seq=None, tok_pos=None):
+    """Write tokens' K/V rows (bf16 [n, Hkv, 128]) into kv.k_cache / kv.v_cache
+    through the block table: token i goes to sequence tok_seq[i] (default i)
+    at position tok_pos[i] (default seq_lens[s] - 1)."""
+    lib = _lib.load()
+    _check_tensors(kv.k_cache, kv.v_cache, kv.block_table, kv.seq_lens, k_new, v_new, tok_seq,
+                   tok_pos)
+    kvs = kv.struct()
+    ptr = (lambda t: t.data_ptr() if t is not None else None)
+    _check(lib.dsa_kv_write(ctypes.byref(kvs), int(k_new.shape[0]), ptr(tok_seq), ptr(tok_pos),
+                            k_new.data_ptr(), v_new.data_ptr(), _stream(kv.k_cache.device)))
+
+
+def index_key_write(kv, block_ids, coarse):
+    """Store coarse keys (fp32 [n, idx_dim]) of physical blocks block_ids
+    (int32 [n]) as E4M3 codes with scale max|x| / 448 into kv.idx_keys /
+    kv.idx_scale."""
+    lib = _lib.load()
+    _check_tensors(kv.idx_keys, kv.idx_scale, block_ids, coarse)
+    kvs = kv.struct()
+    _check(lib.dsa_index_key_write(ctypes.byref(kvs), int(block_ids.shape[0]),
+                                   block_ids.data_ptr(), coarse.data_ptr(),
+                                   _stream(kv.idx_keys.device)))

@@ -15,8 +15,8 @@ OP_INDEX_TOPK = 3
 
 EXPORTS = ["dsa_index_score", "dsa_topk_blocks", "dsa_sparse_attn_decode",
            "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_index_topk",
-           "dsa_workspace_size", "dsa_check_inputs", "dsa_status_str", "dsa_last_error",
-           "dsa_abi_version"]
+           "dsa_workspace_size", "dsa_check_inputs", "dsa_kv_write", "dsa_index_key_write",
+           "dsa_status_str", "dsa_last_error", "dsa_abi_version"]
 CHECK_FLAGS = {1: "seq_len", 2: "table", 4: "q_seq", 8: "q_pos", 16: "block_list"}
 
 
@@ -75,6 +75,8 @@ def load():
         "dsa_index_topk": [kvp, qp, i32, vp, vp, vp, sz, vp],
         "dsa_workspace_size": [ctypes.c_int, kvp, qp, i32, P(sz)],
         "dsa_check_inputs": [kvp, qp, vp, vp, i32, vp, vp],
+        "dsa_kv_write": [kvp, i32, vp, vp, vp, vp, vp],
+        "dsa_index_key_write": [kvp, i32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

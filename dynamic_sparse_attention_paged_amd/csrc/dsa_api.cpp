@@ -366,6 +366,53 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
                     "index_topk: topk launch");
 }
 
+dsa_status dsa_kv_write(const dsa_paged_kv* kv, int32_t n_tokens, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const void* k_new, const void* v_new,
+                        hipStream_t stream) {
+  if (!kv) return fail(DSA_ERR_NULL, "kv must not be NULL");
+  if (n_tokens < 0) return fail(DSA_ERR_SHAPE, "n_tokens < 0");
+  if (kv->block_size != dsa::kBlockSize)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
+  if (kv->head_dim != dsa::kHeadDim)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: this build supports 128", kv->head_dim);
+  if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1 ||
+      kv->num_kv_heads < 1)
+    return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq, num_kv_heads must be >= 1");
+  if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens)
+    return fail(DSA_ERR_NULL, "k_cache/v_cache/block_table/seq_lens NULL");
+  if (n_tokens > 0 && (!k_new || !v_new)) return fail(DSA_ERR_NULL, "k_new/v_new NULL");
+  if (!aligned(kv->k_cache, 16) || !aligned(kv->v_cache, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16))
+    return fail(DSA_ERR_ALIGN, "k_cache/v_cache/k_new/v_new need 16 B alignment");
+  if (!tok_seq && n_tokens > kv->num_seqs)
+    return fail(DSA_ERR_SHAPE, "tok_seq NULL needs n_tokens <= num_seqs");
+  if (n_tokens == 0) return ok();
+  const dsa::KvView kvv = kv_view(kv);
+  return hip_status(dsa::launch_kv_write(kvv, n_tokens, tok_seq, tok_pos, k_new, v_new,
+                                         const_cast<void*>(kv->k_cache),
+                                         const_cast<void*>(kv->v_cache), stream),
+                    "kv_write launch");
+}
+
+dsa_status dsa_index_key_write(const dsa_paged_kv* kv, int32_t n_blocks, const int32_t* block_ids,
+                               const float* coarse, hipStream_t stream) {
+  if (!kv) return fail(DSA_ERR_NULL, "kv must not be NULL");
+  if (n_blocks < 0) return fail(DSA_ERR_SHAPE, "n_blocks < 0");
+  if (kv->num_blocks < 1) return fail(DSA_ERR_SHAPE, "num_blocks must be >= 1");
+  if (kv->idx_dim != 64 && kv->idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "idx_dim %d: supported 64, 128", kv->idx_dim);
+  if (!kv->idx_keys || !kv->idx_scale) return fail(DSA_ERR_NULL, "idx_keys/idx_scale NULL");
+  if (n_blocks > 0 && (!block_ids || !coarse)) return fail(DSA_ERR_NULL, "block_ids/coarse NULL");
+  if (!aligned(block_ids, 4) || !aligned(coarse, 4) || !aligned(kv->idx_scale, 4))
+    return fail(DSA_ERR_ALIGN, "block_ids/coarse/idx_scale need 4 B alignment");
+  if (n_blocks == 0) return ok();
+  const dsa::KvView kvv = kv_view(kv);
+  return hip_status(dsa::launch_index_key_write(kvv, n_blocks, block_ids, coarse,
+                                                const_cast<uint8_t*>(kv->idx_keys),
+                                                const_cast<float*>(kv->idx_scale), stream),
+                    "index_key_write launch");
+}
+
 dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
                             const int32_t* block_idx, const int32_t* block_cnt, int32_t top_k,
                             uint32_t* flags, hipStream_t stream) {

@@ -96,6 +96,14 @@ hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& q, float* ws, 
                                    AttnPlan plan, int32_t* idx_out, int32_t* cnt_out,
                                    hipStream_t s);
 
+// Paged write path (write.hip): token K/V rows into their blocks; per-block
+// coarse keys quantized to E4M3 with scale max|x| / 448.
+hipError_t launch_kv_write(const KvView& kv, int n, const int32_t* tok_seq, const int32_t* tok_pos,
+                           const void* k_new, const void* v_new, void* k_out, void* v_out,
+                           hipStream_t s);
+hipError_t launch_index_key_write(const KvView& kv, int n, const int32_t* blk, const float* x,
+                                  uint8_t* keys_out, float* scale_out, hipStream_t s);
+
 // Device-data check (check.hip): zeroes *flags, then ORs in the
 // DSA_CHECK_* bits of every violation.
 hipError_t launch_check_inputs(const KvView& kv, const QView& q, const int32_t* block_idx,

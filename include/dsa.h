@@ -193,6 +193,42 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Paged write path ([P5] "KV Cache Layout": prefill writes a chunk's tokens
+ * into their blocks in batch, decode appends the newest token, through the
+ * same block table the reads use).  Token i's K and V rows (bf16 [Hkv, 128]
+ * each, k_new / v_new: bf16 [n_tokens, Hkv, 128], 16 B aligned) are copied to
+ * block block_table[s][pos / block_size], row pos % block_size of
+ * kv->k_cache / kv->v_cache, which this call writes (the const qualifiers of
+ * dsa_paged_kv describe the other calls).  s = tok_seq[i] (NULL: s = i, which
+ * needs n_tokens <= num_seqs); pos = tok_pos[i] (NULL: seq_lens[s] - 1, the
+ * newest token of a decode step).  Block allocation and the table entries
+ * themselves are the caller's.  A token whose target falls outside the table
+ * row or the pool is skipped (nothing is written for it); rows of tokens that
+ * share a target are written in no particular order.  Needs k_cache, v_cache,
+ * block_table, seq_lens.
+ */
+dsa_status dsa_kv_write(const dsa_paged_kv* kv, int32_t n_tokens, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const void* k_new, const void* v_new,
+                        hipStream_t stream);
+
+/*
+ * Coarse index keys at low precision ([P1] section 4(2): a compressed
+ * representation per block, kept apart from the fine-grained KV; [P5] "Index
+ * Selection Path": low-precision scoring inputs).  How the representation is
+ * derived from a block is left open by the pages; it is given here as one
+ * float vector per block (coarse: fp32 [n_blocks, idx_dim], 4 B aligned) and
+ * stored for physical block p = block_ids[i] as
+ *   ks = max_d |x[d]| / 448 (1 / 448 for a zero vector),
+ *   idx_keys[p][d] = E4M3(clamp(x[d] / ks, -448, 448)), round to nearest even,
+ *   idx_scale[p] = ks,
+ * every division in float32, rounded once; this call writes kv->idx_keys and
+ * kv->idx_scale.  Ids outside [0, num_blocks) are skipped.  The result is
+ * exactly what dsa_index_score expects (key value = idx_scale * E4M3 value).
+ */
+dsa_status dsa_index_key_write(const dsa_paged_kv* kv, int32_t n_blocks, const int32_t* block_ids,
+                               const float* coarse, hipStream_t stream);
+
+/*
  * Device-data check.  The entry points above trust the device-side contract
  * (conventions at the top of this file); this one checks it and is meant for
  * debugging and for callers that receive tables or block lists from

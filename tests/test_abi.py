@@ -103,6 +103,33 @@ def test_check_inputs_validation(lib):
     assert chk(_kv(), _qs(), bi=FAKE + 1, bc=FAKE, top_k=4) == E["DSA_ERR_ALIGN"]
 
 
+def test_write_path_validation(lib):
+    E = {v: k for k, v in _lib.STATUS.items()}
+
+    def kvw(kv, n=2, ts=None, tp=None, kn=FAKE, vn=FAKE):
+        return lib.dsa_kv_write(ctypes.byref(kv) if kv is not None else None, n, ts, tp, kn, vn,
+                                None)
+    assert kvw(None) == E["DSA_ERR_NULL"]
+    assert kvw(_kv(), n=-1) == E["DSA_ERR_SHAPE"]
+    assert kvw(_kv(k_cache=None)) == E["DSA_ERR_NULL"]
+    assert kvw(_kv(), kn=None) == E["DSA_ERR_NULL"]
+    assert kvw(_kv(), kn=FAKE + 4) == E["DSA_ERR_ALIGN"]
+    assert kvw(_kv(head_dim=64)) == E["DSA_ERR_UNSUPPORTED"]
+    assert kvw(_kv(), n=3) == E["DSA_ERR_SHAPE"]  # tok_seq NULL: n <= num_seqs
+    assert kvw(_kv(), n=0) == 0                    # nothing to do, nothing launched
+
+    def ikw(kv, n=2, ids=FAKE, x=FAKE):
+        return lib.dsa_index_key_write(ctypes.byref(kv) if kv is not None else None, n, ids, x,
+                                       None)
+    assert ikw(None) == E["DSA_ERR_NULL"]
+    assert ikw(_kv(), n=-1) == E["DSA_ERR_SHAPE"]
+    assert ikw(_kv(idx_dim=96)) == E["DSA_ERR_UNSUPPORTED"]
+    assert ikw(_kv(idx_keys=None)) == E["DSA_ERR_NULL"]
+    assert ikw(_kv(), ids=None) == E["DSA_ERR_NULL"]
+    assert ikw(_kv(), x=FAKE + 2) == E["DSA_ERR_ALIGN"]
+    assert ikw(_kv(), n=0) == 0
+
+
 def test_workspace_contract(lib):
     E = {v: k for k, v in _lib.STATUS.items()}
     kv, qs = _kv(), _qs()

@@ -14,8 +14,10 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "dynamic_sparse_attention_paged_amd")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-KERNEL_OBJS = ["index_score.o", "index_score_mfma.o", "index_topk_fused.o", "topk.o", "attn.o",
-               "check.o"]
+sys.path.insert(0, ROOT)
+from dynamic_sparse_attention_paged_amd.build import SOURCES  # noqa: E402
+
+KERNEL_OBJS = [os.path.splitext(f)[0] + ".o" for f in SOURCES if f != "dsa_api.cpp"]
 
 
 def _asan_runtime():
