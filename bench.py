@@ -252,6 +252,48 @@ def decode_extra(w, steps, nsets):
     return res
 
 
+def write_path_extra(steps):
+    """The paged write path at the chunked-prefill shape: one chunk of 8192
+    tokens written into a 2048-block pool (HBM-bound copy through the block
+    table), the 128 coarse keys of the chunk's blocks, and a 32-token decode
+    append (latency)."""
+    import numpy as np
+    import torch
+    import dynamic_sparse_attention_paged_amd as dsa
+    from dsa_synth import gen
+    P, hkv, d, di, n = 2048, 8, 128, 128, 8192
+    k = torch.zeros((P, 64, hkv, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    keys = torch.zeros((P, di), dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(P, dtype=torch.float32, device="cuda")
+    perm = torch.from_numpy(gen.permutation(4242, gen.TAG_TABLE, P).astype(np.int32)).cuda()
+    table = perm.view(1, P)
+    seq_lens = torch.tensor([P * 64], dtype=torch.int32, device="cuda")
+    kv = dsa.PagedKV(k, v, keys, scale, table, seq_lens)
+    k_new = torch.randn((n, hkv, d), device="cuda").to(torch.bfloat16)
+    v_new = torch.randn((n, hkv, d), device="cuda").to(torch.bfloat16)
+    tok_seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+    tok_pos = torch.arange(P * 64 - n, P * 64, dtype=torch.int32, device="cuda")
+    ms = event_time_ms(lambda i: dsa.kv_write(kv, k_new, v_new, tok_seq, tok_pos), steps, 3)
+    moved = 2 * 2 * k_new.numel() * 2  # K and V, read and written
+    blocks = perm[P - n // 64:].contiguous()
+    coarse = torch.randn((n // 64, di), device="cuda")
+    key_ms = event_time_ms(lambda i: dsa.index_key_write(kv, blocks, coarse), steps, 3)
+    # decode append: 32 sequences, the newest token of each
+    tables = perm[:32 * 64].view(32, 64).contiguous()
+    kv32 = dsa.PagedKV(k, v, keys, scale, tables,
+                       torch.full((32,), 64 * 64, dtype=torch.int32, device="cuda"))
+    app_ms = event_time_ms(lambda i: dsa.kv_write(kv32, k_new[:32], v_new[:32]), steps, 3)
+    res = dict(workload="kv_write_8192_tokens_hkv8", kv_write_ms=round(ms, 4),
+               bytes_moved=moved, gbps=round(moved / (ms * 1e-3) / 1e9, 1),
+               frac_of_hbm=round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               index_key_write_128_blocks_us=round(key_ms * 1e3, 2),
+               decode_append_32_tokens_us=round(app_ms * 1e3, 2))
+    del kv, kv32, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_indexer_extra(steps):
     """Chunked-prefill indexer: TFLOP/s and fraction of the FP8 MFMA peak."""
     import torch
@@ -292,7 +334,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--extra", choices=["tiny_decode", "million_decode", "ragged_decode",
-                                        "chunked_prefill"],
+                                        "chunked_prefill", "write_path"],
                     help="run only this secondary workload (for profiling) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -309,6 +351,8 @@ def main():
     if args.extra:
         if args.extra == "chunked_prefill":
             res = prefill_indexer_extra(args.steps)
+        elif args.extra == "write_path":
+            res = write_path_extra(args.steps)
         else:
             fn = getattr(workload, args.extra)
             res = decode_extra(fn(), args.steps, 4 if args.extra != "tiny_decode" else 8)
@@ -394,6 +438,8 @@ def main():
             extras[name] = decode_extra(fn(), steps, 4 if name != "tiny_decode" else 8)
         log("extra: chunked_prefill indexer")
         extras["chunked_prefill"] = prefill_indexer_extra(5)
+        log("extra: write path")
+        extras["write_path"] = write_path_extra(20)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:
