@@ -252,6 +252,18 @@ def decode_extra(w, steps, nsets):
     return res
 
 
+def block_size_extra(steps):
+    """The batched decode shape at 64, 128, 256 and 512 tokens per block, with
+    top_k = 2048 / block_size (the same attended tokens): the pages' block-size
+    tuning sweep through the fused entry point."""
+    from dsa_synth import workload
+    res = {}
+    for bs in (64, 128, 256, 512):
+        log(f"extra: block size {bs}")
+        res[f"bs{bs}"] = decode_extra(workload.batched_decode_blocks(bs), steps, 4)
+    return res
+
+
 def write_path_extra(steps):
     """The paged write path at the chunked-prefill shape: one chunk of 8192
     tokens written into a 2048-block pool (HBM-bound copy through the block
@@ -334,7 +346,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--extra", choices=["tiny_decode", "million_decode", "ragged_decode",
-                                        "chunked_prefill", "write_path"],
+                                        "chunked_prefill", "write_path", "block_sizes"],
                     help="run only this secondary workload (for profiling) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -353,6 +365,8 @@ def main():
             res = prefill_indexer_extra(args.steps)
         elif args.extra == "write_path":
             res = write_path_extra(args.steps)
+        elif args.extra == "block_sizes":
+            res = block_size_extra(args.steps)
         else:
             fn = getattr(workload, args.extra)
             res = decode_extra(fn(), args.steps, 4 if args.extra != "tiny_decode" else 8)
@@ -440,6 +454,7 @@ def main():
         extras["chunked_prefill"] = prefill_indexer_extra(5)
         log("extra: write path")
         extras["write_path"] = write_path_extra(20)
+        extras["block_sizes"] = block_size_extra(20)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:

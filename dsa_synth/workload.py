@@ -173,6 +173,19 @@ def batched_decode():
                  hq=64, hkv=8, hi=8, di=128, top_k=32)
 
 
+def batched_decode_blocks(bs):
+    """The batched decode shape (32 sequences of 32768 tokens) with blocks of
+    bs tokens and top_k = 2048 / bs, so that every query attends the same
+    2048 tokens' worth of blocks at any block size."""
+    seed = 1002
+    B, nb = 32, 32768 // bs
+    perm = gen.permutation(seed, gen.TAG_TABLE, B * nb)
+    j = np.arange(nb)
+    table = np.stack([perm[j * B + s] for s in range(B)])
+    return build(f"batched_decode_32x32768_bs{bs}_k{2048 // bs}", seed, [32768] * B, table,
+                 B * nb, hq=64, hkv=8, hi=8, di=128, top_k=2048 // bs, bs=bs)
+
+
 def ragged_decode():
     seed = 1003
     B = 128
@@ -220,9 +233,9 @@ NAMED = {
 # small workloads for parity tests
 # ---------------------------------------------------------------------------
 def small_decode(seed=2001, lens=(64 * 7 - 17, 64 * 65, 64 * 130 - 63, 64, 1),
-                 hq=16, hkv=2, hi=4, di=128, top_k=8, extra=5):
+                 hq=16, hkv=2, hi=4, di=128, top_k=8, extra=5, bs=64):
     """Ragged decode over a shared permuted pool with a few unused blocks."""
-    nbs = [-(-L // 64) for L in lens]
+    nbs = [-(-L // bs) for L in lens]
     P = sum(nbs) + extra
     perm = gen.permutation(seed, gen.TAG_TABLE, P)
     table = np.zeros((len(lens), max(nbs)), dtype=np.int64)
@@ -230,17 +243,19 @@ def small_decode(seed=2001, lens=(64 * 7 - 17, 64 * 65, 64 * 130 - 63, 64, 1),
     for s, nb in enumerate(nbs):
         table[s, :nb] = perm[off: off + nb]
         off += nb
-    return build(f"small_decode_s{seed}", seed, list(lens), table, P, hq=hq, hkv=hkv,
-                 hi=hi, di=di, top_k=top_k)
+    name = f"small_decode_s{seed}" + ("" if bs == 64 else f"_bs{bs}")
+    return build(name, seed, list(lens), table, P, hq=hq, hkv=hkv, hi=hi, di=di,
+                 top_k=top_k, bs=bs)
 
 
 def small_prefill(seed=2101, L=64 * 20 - 5, count=200, hq=16, hkv=2, hi=4, di=128,
-                  top_k=6, extra=3):
-    nb = -(-L // 64)
+                  top_k=6, extra=3, bs=64):
+    nb = -(-L // bs)
     P = nb + extra
     perm = gen.permutation(seed, gen.TAG_TABLE, P)
-    return build(f"small_prefill_s{seed}", seed, [L], perm[None, :nb], P, hq=hq, hkv=hkv,
-                 hi=hi, di=di, top_k=top_k, prefill=(0, L - count, count))
+    name = f"small_prefill_s{seed}" + ("" if bs == 64 else f"_bs{bs}")
+    return build(name, seed, [L], perm[None, :nb], P, hq=hq, hkv=hkv, hi=hi, di=di,
+                 top_k=top_k, prefill=(0, L - count, count), bs=bs)
 
 
 def multi_prefill(seed=2121, lens=(64 * 30 + 7, 64 * 12, 64 * 21 - 1), counts=(120, 90, 70),

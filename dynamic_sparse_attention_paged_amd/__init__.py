@@ -32,18 +32,30 @@ class DSAError(RuntimeError):
 
 @dataclass
 class PagedKV:
-    k_cache: torch.Tensor      # bf16 [P, 64, Hkv, 128]
-    v_cache: torch.Tensor      # bf16 [P, 64, Hkv, 128]
+    k_cache: torch.Tensor      # bf16 [P, bs, Hkv, 128], bs = 64, 128, 256 or 512
+    v_cache: torch.Tensor      # bf16 [P, bs, Hkv, 128]
     idx_keys: torch.Tensor     # uint8 (E4M3 codes) [P, dI]
     idx_scale: torch.Tensor    # f32 [P]
     block_table: torch.Tensor  # int32 [B, max_blocks]
     seq_lens: torch.Tensor     # int32 [B]
+    block_size: Optional[int] = None  # tokens per block when k_cache is None (default 64)
+
+    @property
+    def tokens_per_block(self):
+        if self.k_cache is None:
+            return 64 if self.block_size is None else int(self.block_size)
+        bs = int(self.k_cache.shape[1])
+        if self.block_size is not None and int(self.block_size) != bs:
+            raise ValueError(f"block_size {self.block_size} != k_cache.shape[1] {bs}")
+        return bs
 
     def struct(self):
         def ptr(t):
             return t.data_ptr() if t is not None else None
         k = self.k_cache
-        P, bs, hkv, d = k.shape if k is not None else (self.idx_keys.shape[0], 64, 1, 128)
+        P, bs, hkv, d = (k.shape if k is not None else
+                         (self.idx_keys.shape[0], self.tokens_per_block, 1, 128))
+        bs = self.tokens_per_block
         return _lib.PagedKVStruct(
             ptr(self.k_cache), ptr(self.v_cache), ptr(self.idx_keys), ptr(self.idx_scale),
             ptr(self.block_table), ptr(self.seq_lens), P, bs, hkv, d,
@@ -253,7 +265,7 @@ def _check_struct(kv):
     num_blocks = (kv.k_cache.shape[0] if kv.k_cache is not None else
                   kv.idx_keys.shape[0] if kv.idx_keys is not None else 1)
     return _lib.PagedKVStruct(None, None, None, None, kv.block_table.data_ptr(),
-                              kv.seq_lens.data_ptr(), num_blocks, 64, 1, 128, 64,
+                              kv.seq_lens.data_ptr(), num_blocks, kv.tokens_per_block, 1, 128, 64,
                               kv.block_table.shape[0], kv.block_table.shape[1])
 
 

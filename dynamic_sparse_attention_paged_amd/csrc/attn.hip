@@ -6,14 +6,15 @@
 // index-selected pairs, otherwise the full-attention formula; [P5] "KV Cache
 // Layout": whole blocks read through the block table): for query head h with
 // KV head g = h / G (G = Hq / Hkv), over the tokens t of the selected blocks
-// with position j*64 + t <= pos and < seq_len,
+// with position j*block_size + t <= pos and < seq_len,
 //   x_t = scale <q_h, K_t>,  out_h = sum_t e^(x_t - m) V_t / sum_t e^(x_t - m),
 //   lse_h = m + ln sum_t e^(x_t - m).
 //
 // Decode is HBM-bound: one (query, KV head, split) per workgroup, four waves,
-// each wave streaming whole 64-token blocks of head g (K and V rows of 256 B
-// at a 2 KiB stride).  Per block and wave, with the G query heads of g as the
-// 16 MFMA columns:
+// each wave streaming 64-token tiles of head g (K and V rows of 256 B at a
+// 2 KiB stride; a block of 128, 256 or 512 tokens is 2, 4 or 8 consecutive
+// tiles).  Per tile and wave, with the G query heads of g as the 16 MFMA
+// columns:
 //   S^T[64 tok x 16 heads] = K[64 x 128] . Q^T        16 x mfma 16x16x32 bf16
 //   online softmax per head (lane's head = lane % 16 in every tile)
 //   O^T[128 x 16] += V^T[128 x 64] . P^T[64 x 16]       32 x mfma (P = hi + lo bf16)
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     uint32_t* lut = reinterpret_cast<uint32_t*>(&vs_a[0][0]);
     float* sc = reinterpret_cast<float*>(lut + 256);
     double* wsq = reinterpret_cast<double*>(sc + kMaxScoredBlocks);
-    const int local = pos / kBlockSize;  // <= maxb - 1 < kMaxScoredBlocks (host check)
+    const int local = pos >> kv.bs_shift;  // <= maxb - 1 < kMaxScoredBlocks (host check)
     for (int c = threadIdx.x; c < 256; c += 64 * kAttnWaves) lut[c] = digits_of_code((uint32_t)c);
     for (int j = threadIdx.x; j <= local; j += 64 * kAttnWaves) tab[j] = trow[j];
     __syncthreads();
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   }
   if (kMode == kAttnSelect) {
     if (wave == 0) {
-      const int local = pos / kBlockSize;  // <= maxb - 1 < kMaxSelectBlocks
+      const int local = pos >> kv.bs_shift;  // <= maxb - 1 < kMaxSelectBlocks
       const float* row = scores + (size_t)qi * kv.maxb;
       int c;
       if (local <= 64 * 2) {
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     }
   }
   if (kMode == kAttnCand) {
-    const int local = pos / kBlockSize;
+    const int local = pos >> kv.bs_shift;
     const int need = top_k - 1;
     if (local <= need || need == 0) {  // uniform over the workgroup
       if (wave == 0) {
@@ -337,8 +338,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     n_sel = cnt[qi];
     sel = idx + (size_t)qi * top_k;
   }
-  const int per = (top_k + splits - 1) / splits;
-  const int b0 = sp * per, b1 = min(n_sel, b0 + per);
+  // A block of 64 m tokens (m = 1, 2, 4, 8) is m tiles of 64 tokens; the
+  // splits and the waves share tiles.  The last selected block (the query's
+  // own block, in the Top-K kernels' ascending lists) contributes only its
+  // tiles up to the query's last visible token, and at least one.
+  const int lim = min(pos, len - 1);  // last attended token
+  const int sub_shift = kv.bs_shift - 6;
+  int n_items = n_sel << sub_shift;
+  if (sub_shift > 0 && n_sel > 0) {
+    const int vis = (lim >> 6) - (sel[n_sel - 1] << sub_shift) + 1;
+    n_items -= (1 << sub_shift) - min(max(vis, 1), 1 << sub_shift);
+  }
+  const int per = ((top_k << sub_shift) + splits - 1) / splits;
+  const int b0 = sp * per, b1 = min(n_items, b0 + per);
 
   // Q^T fragments (B operand): column = head r of group g, k = dims 32c + 8gq .. +8
   i16x8 qf[4];
@@ -359,27 +371,29 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
 
   uint16_t* vs = vs_a[wave];
   const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
-  const size_t blk_elems = (size_t)kBlockSize * tok_stride;
-  const int lim = min(pos, len - 1);  // last attended token
+  const size_t tile_elems = (size_t)kBlockSize * tok_stride;
   const uint32_t v_off = dma_v_lane_offset(tok_stride, lane);
   const uint32_t k_off = (uint32_t)(((size_t)r * tok_stride + 8 * gq) * 2);
 
-  // The wave's blocks are b0 + wave + 4 i.  Their logical ids and physical
-  // blocks are fetched up front, one per lane (64 at a time), so that the
-  // loop never waits on a dependent table read before issuing block loads.
+  // The wave's tiles are b0 + wave + W i.  Their logical tile ids (my_j) and
+  // their tiles in the pool (my_p: physical block * m + tile within it) are
+  // fetched up front, one per lane (64 at a time), so that the loop never
+  // waits on a dependent table read before issuing tile loads.
   const int nmine = b1 > b0 + wave ? (b1 - b0 - wave + kAttnWaves - 1) / kAttnWaves : 0;
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int cn = min(64, nmine - c0);
     int my_j = 0, my_p = 0;
     if (lane < cn) {
-      my_j = sel[b0 + wave + kAttnWaves * (c0 + lane)];
-      my_p = trow[my_j];
+      const int item = b0 + wave + kAttnWaves * (c0 + lane);
+      const int jb = sel[item >> sub_shift], h = item & ((1 << sub_shift) - 1);
+      my_j = (jb << sub_shift) | h;
+      my_p = (trow[jb] << sub_shift) | h;
     }
     if (kVBufs == 1) {
       for (int i = 0; i < cn; ++i) {
         const int j = __builtin_amdgcn_readlane(my_j, i);
         const int p = __builtin_amdgcn_readlane(my_p, i);
-        const size_t base = (size_t)p * blk_elems + (size_t)g * kHeadDim;
+        const size_t base = (size_t)p * tile_elems + (size_t)g * kHeadDim;
         // previous block's LDS reads are complete before the DMA overwrites vs
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
@@ -405,7 +419,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       i16x8 ka[4][4], kb[4][4];
       auto base_of = [&](int t) {
         const int p = __builtin_amdgcn_readlane(my_p, t);
-        return (size_t)p * blk_elems + (size_t)g * kHeadDim;
+        return (size_t)p * tile_elems + (size_t)g * kHeadDim;
       };
       auto pin_order = [] {
         asm volatile("" ::: "memory");
@@ -525,26 +539,26 @@ __global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict
 
 }  // namespace
 
-AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill) {
+AttnPlan attn_plan(int nq, int hkv, int tiles, bool prefill) {
   AttnPlan a;
   const long units = (long)nq * hkv;
   // Enough (query, KV head) pairs to give every CU a workgroup: no split.
-  // Otherwise the selected blocks are split across workgroups until every
+  // Otherwise the selected tiles are split across workgroups until every
   // CU has one.
   // Four waves, each double-buffering V (eight single-buffered waves measured
   // no faster for batched decode and 13% slower for a chunked prefill of 8192
   // queries, whose gather is latency-bound).
   a.waves = 4;
   a.splits = 1;
-  if (!prefill && top_k <= 8 && units < kNumCUs) {
-    // at most eight blocks: one per wave of one eight-wave workgroup, with
-    // no split partials and no merge launch
+  if (!prefill && tiles <= 8 && units < kNumCUs) {
+    // at most eight 64-token tiles: one per wave of one eight-wave
+    // workgroup, with no split partials and no merge launch
     a.waves = 8;
     return a;
   }
   if (!prefill && units > 0 && units < kNumCUs) {
     int splits = (int)((kNumCUs + units - 1) / units);
-    const int max_splits = (top_k + a.waves - 1) / a.waves;  // >= one block per wave
+    const int max_splits = (tiles + a.waves - 1) / a.waves;  // >= one tile per wave
     a.splits = splits < max_splits ? splits : max_splits;
     if (a.splits < 1) a.splits = 1;
   }

@@ -10,7 +10,7 @@
 // Trillion-Parameter Models...", "Index Selection Path" and "KV Cache
 // Layout": ids in gather order, one table row per sequence): a query at
 // position pos sees logical blocks j with j * 64 <= pos; a list holds cnt
-// ascending visible ids ending with the local block pos / 64, then -1.
+// ascending visible ids ending with the local block pos / block_size, then -1.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,9 +36,9 @@ __global__ __launch_bounds__(256) void check_inputs(KvView kv, QView Q,
     if (it < n_tab) {
       const int s = (int)(it / kv.maxb), j = (int)(it % kv.maxb);
       const int len = kv.seq_lens[s];
-      if (j == 0 && (len < 1 || (long)len > (long)kv.maxb * kBlockSize)) f |= DSA_CHECK_SEQ_LEN;
+      if (j == 0 && (len < 1 || (long)len > ((long)kv.maxb << kv.bs_shift))) f |= DSA_CHECK_SEQ_LEN;
       // entries of blocks that hold tokens must name pool blocks
-      if ((long)j * kBlockSize < (long)len) {
+      if (((long)j << kv.bs_shift) < (long)len) {
         const int p = kv.table[it];
         if (p < 0 || p >= kv.num_blocks) f |= DSA_CHECK_TABLE;
       }
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void check_inputs(KvView kv, QView Q,
       continue;
     }
     if (block_idx) {
-      const int local = pos / kBlockSize;
+      const int local = pos >> kv.bs_shift;
       const int c = block_cnt[qi];
       if (c < 1 || c > top_k) {
         f |= DSA_CHECK_BLOCK_LIST;

@@ -32,6 +32,22 @@ dsa_status hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+bool block_size_ok(int bs) { return bs == 64 || bs == 128 || bs == 256 || bs == 512; }
+
+int log2_block(int bs) { return bs == 512 ? 9 : bs == 256 ? 8 : bs == 128 ? 7 : 6; }
+
+// 64-token attention tiles in top_k blocks
+int tiles_of(const dsa_paged_kv* kv, int top_k) { return top_k << (log2_block(kv->block_size) - 6); }
+
+// Token positions and 64-token tile ids of the pool are 32-bit in the kernels.
+dsa_status check_extent(const dsa_paged_kv* kv) {
+  if ((long long)kv->max_blocks_per_seq * kv->block_size > INT32_MAX ||
+      (long long)kv->num_blocks * kv->block_size > INT32_MAX * 64LL)
+    return fail(DSA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size (or the pool's 64-token tiles) "
+                                     "exceed 2^31 - 1");
+  return DSA_OK;
+}
+
 enum Need : unsigned {
   kNeedIndex = 1u,  // idx_keys, idx_scale, q_idx, w_idx
   kNeedAttn = 2u,   // k_cache, v_cache, q
@@ -43,13 +59,14 @@ dsa_status check_common(const dsa_paged_kv* kv, const dsa_queries* qs, unsigned 
   if (qs->num_queries > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "num_queries %d: at most 65535 per call (one grid row per query)",
                 qs->num_queries);
-  if (kv->block_size != dsa::kBlockSize)
-    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
+  if (!block_size_ok(kv->block_size))
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: supported 64, 128, 256, 512", kv->block_size);
   if (kv->head_dim != dsa::kHeadDim)
     return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: this build supports 128", kv->head_dim);
   if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1 ||
       kv->num_kv_heads < 1)
     return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq, num_kv_heads must be >= 1");
+  if (check_extent(kv) != DSA_OK) return DSA_ERR_UNSUPPORTED;
   if (!kv->block_table || !kv->seq_lens) return fail(DSA_ERR_NULL, "block_table/seq_lens NULL");
   if (!qs->q_seq && qs->num_queries > kv->num_seqs)
     return fail(DSA_ERR_SHAPE, "decode batch (q_seq NULL) needs num_queries <= num_seqs");
@@ -95,6 +112,7 @@ dsa::KvView kv_view(const dsa_paged_kv* kv) {
   v.idx_dim = kv->idx_dim;
   v.num_seqs = kv->num_seqs;
   v.maxb = kv->max_blocks_per_seq;
+  v.bs_shift = log2_block(kv->block_size);
   return v;
 }
 
@@ -121,7 +139,7 @@ struct AttnLayout {
 
 AttnLayout attn_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k, size_t base) {
   AttnLayout a;
-  a.plan = dsa::attn_plan(qs->num_queries, kv->num_kv_heads, top_k, false);
+  a.plan = dsa::attn_plan(qs->num_queries, kv->num_kv_heads, tiles_of(kv, top_k), false);
   a.partials = base;
   a.total = align_up(a.partials + dsa::attn_partials_bytes(qs->num_queries, qs->num_q_heads,
                                                            a.plan.splits));
@@ -266,7 +284,7 @@ dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs
   return hip_status(dsa::launch_sparse_attn(kv_view(kv), q_view(qs), block_idx, block_cnt, top_k,
                                             softmax_scale, out, lse, nullptr,
                                             dsa::attn_plan(qs->num_queries, kv->num_kv_heads,
-                                                           top_k, true),
+                                                           tiles_of(kv, top_k), true),
                                             stream),
                     "sparse_attn_prefill launch");
 }
@@ -371,13 +389,14 @@ dsa_status dsa_kv_write(const dsa_paged_kv* kv, int32_t n_tokens, const int32_t*
                         hipStream_t stream) {
   if (!kv) return fail(DSA_ERR_NULL, "kv must not be NULL");
   if (n_tokens < 0) return fail(DSA_ERR_SHAPE, "n_tokens < 0");
-  if (kv->block_size != dsa::kBlockSize)
-    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
+  if (!block_size_ok(kv->block_size))
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: supported 64, 128, 256, 512", kv->block_size);
   if (kv->head_dim != dsa::kHeadDim)
     return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: this build supports 128", kv->head_dim);
   if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1 ||
       kv->num_kv_heads < 1)
     return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq, num_kv_heads must be >= 1");
+  if (check_extent(kv) != DSA_OK) return DSA_ERR_UNSUPPORTED;
   if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens)
     return fail(DSA_ERR_NULL, "k_cache/v_cache/block_table/seq_lens NULL");
   if (n_tokens > 0 && (!k_new || !v_new)) return fail(DSA_ERR_NULL, "k_new/v_new NULL");
@@ -419,10 +438,11 @@ dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
   if (!kv || !qs || !flags) return fail(DSA_ERR_NULL, "kv, qs and flags must not be NULL");
   if (!aligned(flags, 4)) return fail(DSA_ERR_ALIGN, "flags needs 4 B alignment");
   if (qs->num_queries < 0) return fail(DSA_ERR_SHAPE, "num_queries < 0");
-  if (kv->block_size != dsa::kBlockSize)
-    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: this build supports 64", kv->block_size);
+  if (!block_size_ok(kv->block_size))
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d: supported 64, 128, 256, 512", kv->block_size);
   if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1)
     return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq must be >= 1");
+  if (check_extent(kv) != DSA_OK) return DSA_ERR_UNSUPPORTED;
   if (!kv->block_table || !kv->seq_lens) return fail(DSA_ERR_NULL, "block_table/seq_lens NULL");
   if (!qs->q_seq && qs->num_queries > kv->num_seqs)
     return fail(DSA_ERR_SHAPE, "decode batch (q_seq NULL) needs num_queries <= num_seqs");

@@ -8,7 +8,7 @@
 
 namespace dsa {
 
-constexpr int kBlockSize = 64;   // tokens per KV block
+constexpr int kBlockSize = 64;   // tokens per attention tile (a KV block is 1, 2, 4 or 8 tiles)
 constexpr int kHeadDim = 128;    // attention head dim
 constexpr int kMaxGroup = 16;    // max query heads per KV head
 constexpr int kMaxIdxHeads = 16;
@@ -22,6 +22,7 @@ struct KvView {
   const int32_t* table;     // [B, maxb]
   const int32_t* seq_lens;  // [B]
   int num_blocks, num_kv_heads, idx_dim, num_seqs, maxb;
+  int bs_shift;             // log2(tokens per block): 6, 7, 8 or 9
 };
 
 struct QView {
@@ -64,7 +65,8 @@ struct AttnPlan {
   int waves;   // waves per workgroup (4 or 8)
   int splits;  // workgroups per (query, KV head)
 };
-AttnPlan attn_plan(int nq, int hkv, int top_k, bool prefill);
+// tiles: 64-token tiles per query (top_k * block_size / 64)
+AttnPlan attn_plan(int nq, int hkv, int tiles, bool prefill);
 size_t attn_partials_bytes(int nq, int hq, int splits);
 hipError_t launch_sparse_attn(const KvView& kv, const QView& q, const int32_t* idx,
                               const int32_t* cnt, int top_k, float scale, float* out, float* lse,

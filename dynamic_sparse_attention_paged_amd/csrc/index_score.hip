@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void topk_merge_candidates(
   const int s = query_seq(Q, qi);
   const int len = kv.seq_lens[s];
   const int pos_q = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos_q / kBlockSize;
+  const int local = pos_q >> kv.bs_shift;
   const int need = top_k - 1;
   int32_t* out = out_idx + (size_t)qi * top_k;
   if (local <= need) {  // uniform over the workgroup
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   }
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos / kBlockSize;
+  const int local = pos >> kv.bs_shift;
 
   // Workgroups whose blocks are all invisible only write -inf (or no candidates).
   if (blockIdx.x * kBlocksPerWg > local) {

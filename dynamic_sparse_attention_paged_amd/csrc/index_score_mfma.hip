@@ -117,7 +117,7 @@ void index_score_i8(KvView kv, QView Q, float* __restrict__ scores, int span) {
     if (q < Q.nq) {
       sq = query_seq(Q, q);
       const int pos = Q.q_pos ? Q.q_pos[q] : kv.seq_lens[sq] - 1;
-      lq = pos / kBlockSize;
+      lq = pos >> kv.bs_shift;
     }
     seq_s[tid] = sq;
     loc_s[tid] = lq;

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void index_topk_i8(KvView kv, QVi
   qr.fetch(Q, qi, lane);
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos / kBlockSize;  // visible blocks: 0 .. local
+  const int local = pos >> kv.bs_shift;  // visible blocks: 0 .. local
   for (int c = tid; c < 256; c += 64 * kFusedWaves) lut[c] = digits_of_code((uint32_t)c);
   for (int j = tid; j <= local; j += 64 * kFusedWaves) tab[j] = kv.table[(size_t)s * kv.maxb + j];
   __syncthreads();

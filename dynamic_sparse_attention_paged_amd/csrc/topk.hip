@@ -5,7 +5,7 @@
 // rather than a full sort, padding for ragged batches; [P5] "Day-0 Readiness
 // for Trillion-Parameter Models...", "Index Selection Path": the selected
 // indices are ordered the way the gather consumes them):
-//   - the local block l = pos / 64 is always kept;
+//   - the local block l = pos / block_size is always kept;
 //   - of the candidates j < l the K-1 with the largest score are kept,
 //     equal scores going to the lower j (and -0.0 == +0.0);
 //   - output in ascending j (so l is last), -1 padded, count = min(K, l+1).
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const float* __restrict__
   const int s = query_seq(Q, qi);
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos / kBlockSize;
+  const int local = pos >> kv.bs_shift;
   const int n = local;              // candidates 0..local-1 (the local block is forced)
   const int need = top_k - 1;       // how many candidates to keep
   const float* row = scores + (size_t)qi * kv.maxb;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(64) void topk_wave(const float* __restrict__ scores
   const float* row = scores + (size_t)qi * kv.maxb;
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int c = select_query_blocks<M>(row, kv.maxb, pos / kBlockSize, top_k, hist4,
+  const int c = select_query_blocks<M>(row, kv.maxb, pos >> kv.bs_shift, top_k, hist4,
                                        out_idx + (size_t)qi * top_k);
   if (lane == 0) out_cnt[qi] = c;
 }
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64 * kTreeWaves) void topk_tree(
   const int s = query_seq(Q, qi);
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos / kBlockSize;
+  const int local = pos >> kv.bs_shift;
   const int n = local;
   const int need = top_k - 1;
   const float* row = scores + (size_t)qi * kv.maxb;

@@ -39,10 +39,10 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_rows(
     const int s = tok_seq ? tok_seq[i] : i;
     if (s < 0 || s >= kv.num_seqs) continue;
     const int pos = tok_pos ? tok_pos[i] : kv.seq_lens[s] - 1;
-    if (pos < 0 || pos / kBlockSize >= kv.maxb) continue;
-    const int p = kv.table[(size_t)s * kv.maxb + pos / kBlockSize];
+    if (pos < 0 || (pos >> kv.bs_shift) >= kv.maxb) continue;
+    const int p = kv.table[(size_t)s * kv.maxb + (pos >> kv.bs_shift)];
     if (p < 0 || p >= kv.num_blocks) continue;
-    const size_t row = (size_t)p * kBlockSize + pos % kBlockSize;
+    const size_t row = ((size_t)p << kv.bs_shift) + (pos & ((1 << kv.bs_shift) - 1));
     const uint4 val = (is_v ? v_new : k_new)[(size_t)i * chunks + c];
     (is_v ? v_out : k_out)[row * chunks + c] = val;
   }

@@ -60,6 +60,13 @@ typedef enum {
  * maps each sequence's logical block j to a physical block), together with
  * the coarse per-block index keys used for block selection ([P1] section
  * 4(2): compressed index blocks kept apart from the fine-grained KV blocks).
+ *
+ * Block size: selection works at the granularity of the cache's pages ([P1]
+ * section 4(2): index granularity aligned with page granularity; [P3] section
+ * 4.2: blocks aligned to the hardware tile); the pages recommend tuning it,
+ * starting from 256 or 512 tokens ([P2] section 2.1, note).  Any of 64, 128,
+ * 256, 512 is accepted at run time; max_blocks_per_seq * block_size and
+ * num_blocks * block_size / 64 must stay below 2^31 (DSA_ERR_UNSUPPORTED).
  */
 typedef struct {
   const void* k_cache;         /* bf16 [num_blocks, block_size, num_kv_heads, head_dim], 16 B aligned */
@@ -69,7 +76,7 @@ typedef struct {
   const int32_t* block_table;  /* int32 [num_seqs, max_blocks_per_seq]: logical -> physical block    */
   const int32_t* seq_lens;     /* int32 [num_seqs]: tokens in the cache, current token included      */
   int32_t num_blocks;          /* physical blocks in the pool, >= 1                                  */
-  int32_t block_size;          /* tokens per block; this build: 64                                  */
+  int32_t block_size;          /* tokens per block: 64, 128, 256 or 512 (see below)                  */
   int32_t num_kv_heads;        /* >= 1                                                               */
   int32_t head_dim;            /* this build: 128                                                    */
   int32_t idx_dim;             /* coarse key length: 64 or 128                                       */

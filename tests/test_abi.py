@@ -65,7 +65,11 @@ def test_validation_errors(lib):
     E = {v: k for k, v in _lib.STATUS.items()}
     assert lib.dsa_index_score(None, None, FAKE, None) == E["DSA_ERR_NULL"]
     assert "NULL" in lib.dsa_last_error().decode()
-    assert _score(lib, _kv(block_size=128), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+    for bs in (32, 96, 1024):
+        assert _score(lib, _kv(block_size=bs), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+    # positions past 2^31 - 1
+    assert _score(lib, _kv(block_size=512, max_blocks_per_seq=1 << 22), _qs()) == \
+        E["DSA_ERR_UNSUPPORTED"]
     assert _score(lib, _kv(head_dim=64), _qs()) == E["DSA_ERR_UNSUPPORTED"]
     assert _score(lib, _kv(idx_dim=96), _qs()) == E["DSA_ERR_UNSUPPORTED"]
     assert _score(lib, _kv(), _qs(idx_heads=17)) == E["DSA_ERR_UNSUPPORTED"]

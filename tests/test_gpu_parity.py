@@ -374,3 +374,93 @@ def test_random_prefill_configs(dsa, seed):
                                di=di, top_k=top_k)
     _say(f"random prefill L={L} count={count} hq={hkv * G} hkv={hkv} hi={hi} di={di} K={top_k}")
     _run_all_stages(dsa, w, f"random_prefill[{seed}]")
+
+
+# ---------------------------------------------------------------------------
+# blocks of 128, 256 and 512 tokens: every kernel takes the block size at run
+# time; attention walks a selected block as 64-token tiles
+# ---------------------------------------------------------------------------
+BLOCK_SIZES = [128, 256, 512]
+
+
+@pytest.mark.parametrize("bs", BLOCK_SIZES)
+def test_block_size_decode_stages(dsa, bs):
+    """Stages and the fused entry (in-attention scoring: short contexts, one
+    round of workgroups) on ragged lengths that end mid-tile and mid-block."""
+    lens = (bs * 7 - 17, bs * 30, bs * 3 - 1, 1, bs, 65)
+    w = workload.small_decode(seed=2700 + bs, lens=lens, hq=16, hkv=2, hi=4, di=128, top_k=5,
+                              bs=bs)
+    _say(f"block size {bs}: decode stages")
+    kv, qs, refs = _run_all_stages(dsa, w, f"decode_bs{bs}")
+    K = w.top_k
+    bi = torch.empty(w.num_queries, K, dtype=torch.int32, device="cuda")
+    bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
+    out, _, _, _ = dsa.decode_fused(kv, qs, K, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    bi2, bc2 = dsa.index_topk(kv, qs, K)
+    torch.cuda.synchronize()
+    for qi, r in enumerate(refs):
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        assert np.array_equal(bi2[qi].cpu().numpy(), r["idx"]) and int(bc2[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"fused bs{bs} q{qi}: {a:.3e} {rel:.3e}"
+
+
+@pytest.mark.parametrize("bs", BLOCK_SIZES)
+@pytest.mark.parametrize("nq,hkv,top_k,nb", [
+    (40, 8, 6, 200),   # 320 workgroups: fused scoring + selection, then attention
+    (2, 2, 16, 200),   # 4 (query, KV head) pairs, each split over its 64-token tiles
+    (3, 2, 4, 600),    # past 256 blocks: scoring, then selection inside attention
+])
+def test_block_size_fused_paths(dsa, bs, nq, hkv, top_k, nb):
+    rng = np.random.default_rng(bs + nq)
+    lens = tuple(int(x) for x in rng.integers(1, bs * nb, size=nq))
+    w = workload.small_decode(seed=2710 + bs + nq, lens=lens, hq=8 * hkv, hkv=hkv, hi=8, di=64,
+                              top_k=top_k, bs=bs)
+    _say(f"block size {bs}: fused nq={nq} hkv={hkv} K={top_k} maxb={w.block_table.shape[1]}")
+    kv, qs = parity.to_device(w)
+    bi = torch.empty(nq, top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.decode_fused(kv, qs, top_k, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    torch.cuda.synchronize()
+    for qi in range(nq):
+        r = parity.oracle_query(w, qi)
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"bs{bs} q{qi}: attention {a:.3e} {rel:.3e}"
+        la, _ = parity.attn_errors(lse[qi].cpu().numpy(), r["lse"])
+        assert la <= 1e-3, f"bs{bs} q{qi}: lse {la:.3e}"
+
+
+@pytest.mark.parametrize("bs", BLOCK_SIZES)
+def test_block_size_prefill_stages(dsa, bs):
+    """A prefill chunk of 96 queries (vector scorer) and one of 256 (int8
+    matrix-core scorer), both ending inside a block."""
+    w = workload.small_prefill(seed=2720 + bs, L=bs * 12 - 5, count=96, top_k=4, bs=bs)
+    _say(f"block size {bs}: prefill 96")
+    _run_all_stages(dsa, w, f"prefill_bs{bs}")
+    w = workload.small_prefill(seed=2730 + bs, L=bs * 9 + 70, count=256, hi=8, di=64, top_k=3,
+                               bs=bs)
+    _say(f"block size {bs}: prefill 256")
+    _run_all_stages(dsa, w, f"prefill256_bs{bs}")
+
+
+def test_block_size_long_context_candidates(dsa):
+    """2100 blocks of 512 tokens (1.07M tokens): the candidate-list path of
+    the fused entry and of index_topk."""
+    bs, top_k = 512, 6
+    lens = (bs * 2100 - 100, bs * 1500 + 3)
+    w = workload.small_decode(seed=2740, lens=lens, hq=8, hkv=1, hi=4, di=64, top_k=top_k,
+                              bs=bs, extra=2)
+    _say(f"block size {bs}: long context maxb={w.block_table.shape[1]}")
+    kv, qs = parity.to_device(w)
+    bi = torch.empty(2, top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(2, dtype=torch.int32, device="cuda")
+    out, _, _, _ = dsa.decode_fused(kv, qs, top_k, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    bi2, bc2 = dsa.index_topk(kv, qs, top_k)
+    torch.cuda.synchronize()
+    for qi in range(2):
+        r = parity.oracle_query(w, qi)
+        assert np.array_equal(bi[qi].cpu().numpy(), r["idx"]) and int(bc[qi]) == r["cnt"]
+        assert np.array_equal(bi2[qi].cpu().numpy(), r["idx"]) and int(bc2[qi]) == r["cnt"]
+        good, a, rel = parity.attn_ok(out[qi].cpu().numpy(), r["out"])
+        assert good, f"long bs{bs} q{qi}: {a:.3e} {rel:.3e}"

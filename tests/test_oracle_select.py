@@ -85,3 +85,10 @@ def test_visible_blocks_are_the_causal_prefix():
                 want = sorted({a // bs for a in range(pos + 1)})
                 assert v == want
                 assert v[-1] == local_block(pos, bs)
+    # the larger block sizes, on lengths and positions around block edges
+    for bs in (128, 256, 512):
+        for L in (1, bs - 1, bs, bs + 1, 3 * bs - 5, 4 * bs):
+            for pos in sorted({0, bs - 1, bs, 2 * bs - 1, 2 * bs + 7, L - 1} & set(range(L))):
+                v = visible_blocks(pos, L, bs).tolist()
+                assert v == sorted({a // bs for a in range(pos + 1)})
+                assert v[-1] == local_block(pos, bs)

@@ -95,3 +95,19 @@ def test_kv_write_round_trip():
     k3, _ = kv_write(k_pool, v_pool, table, seq_lens, None, None, k_new[:2], v_new[:2], bs)
     assert np.array_equal(k3[table[0][199 // bs], 199 % bs], k_new[0])
     assert np.array_equal(k3[table[1][129 // bs], 129 % bs], k_new[1])
+
+
+def test_kv_write_round_trip_large_blocks():
+    rng = np.random.default_rng(8)
+    for bs in (128, 512):
+        P, H, d = 5, 1, 4
+        k_pool = rng.integers(0, 1 << 16, size=(P, bs, H, d), dtype=np.uint16)
+        table = np.array([[4, 0, 2], [1, 3, -1]], dtype=np.int32)
+        seq_lens = np.array([2 * bs + 3, bs + 1], dtype=np.int32)
+        tok_seq = np.array([0, 0, 1, 1], dtype=np.int32)
+        tok_pos = np.array([bs - 1, 2 * bs + 2, bs, 0], dtype=np.int32)
+        k_new = rng.integers(0, 1 << 16, size=(4, H, d), dtype=np.uint16)
+        k2, _ = kv_write(k_pool, k_pool, table, seq_lens, tok_seq, tok_pos, k_new, k_new, bs)
+        want = k_pool.copy()
+        want[4, bs - 1], want[2, 2], want[3, 0], want[1, 0] = k_new
+        assert np.array_equal(k2, want)
