@@ -327,6 +327,19 @@ def prefill_indexer_extra(steps):
                     "frac_of_fp8_mfma_peak counts the algorithmic FP8 flops, "
                     "frac_of_int8_mfma_peak the digit products issued for them",
                topk_ms=round(tk_ms, 4), attention_ms=round(at_ms, 3))
+    # the one-call prefill: scoring, selection and the block-inverted attention
+    from dynamic_sparse_attention_paged_amd import _lib
+    ws = D.dsa.make_workspace(_lib.OP_PREFILL_FUSED, D.kv, D.sets[0], w.top_k)
+
+    def fused(i):
+        D.dsa.prefill_fused(D.kv, D.sets[0], w.top_k, w.softmax_scale, out=D.out, lse=D.lse,
+                            workspace=ws)
+    f_ms = event_time_ms(fused, max(2, steps // 2), 1)
+    res.update(prefill_fused_ms=round(f_ms, 3),
+               prefill_fused_queries_per_s=round(w.num_queries / (f_ms * 1e-3), 1),
+               prefill_fused_workspace_gb=round(ws.numel() / 1e9, 2),
+               prefill_stagewise_ms=round(ms + tk_ms + at_ms, 3))
+    del ws
     del D
     torch.cuda.empty_cache()
     return res

@@ -225,6 +225,33 @@ def decode_fused(kv, qs, top_k, softmax_scale, out=None, lse=None, block_idx=Non
     return out, lse, block_idx, block_cnt
 
 
+def prefill_fused(kv, qs, top_k, softmax_scale, out=None, lse=None, block_idx=None,
+                  block_cnt=None, workspace=None):
+    """Chunked prefill in one call: scoring, selection and the block-inverted
+    attention (each K/V tile read once for all the queries that picked it).
+    q_seq and q_pos are required.  Returns (out, lse, block_idx, block_cnt);
+    block_idx / block_cnt are None unless tensors are passed in to receive them.
+    The workspace holds one partial state per (query, pick, head): see
+    workspace_size(OP_PREFILL_FUSED, ...)."""
+    lib = _lib.load()
+    _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.k_cache.device
+    nq, hq = qs.q.shape[0], qs.q.shape[1]
+    if out is None:
+        out = torch.empty(nq, hq, 128, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(nq, hq, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(workspace_size(_lib.OP_PREFILL_FUSED, kv, qs, top_k), dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_sparse_prefill_fused(
+        ctypes.byref(kvs), ctypes.byref(qss), top_k, float(softmax_scale), out.data_ptr(),
+        lse.data_ptr(), block_idx.data_ptr() if block_idx is not None else None,
+        block_cnt.data_ptr() if block_cnt is not None else None, workspace.data_ptr(),
+        workspace.numel(), _stream(dev)))
+    return out, lse, block_idx, block_cnt
+
+
 def index_topk(kv, qs, top_k, block_idx=None, block_cnt=None, workspace=None):
     lib = _lib.load()
     _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))

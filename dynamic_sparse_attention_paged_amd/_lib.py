@@ -12,9 +12,11 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_UNS
 OP_ATTN_DECODE = 1
 OP_DECODE_FUSED = 2
 OP_INDEX_TOPK = 3
+OP_PREFILL_FUSED = 4
 
 EXPORTS = ["dsa_index_score", "dsa_topk_blocks", "dsa_sparse_attn_decode",
-           "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_index_topk",
+           "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_sparse_prefill_fused",
+           "dsa_index_topk",
            "dsa_workspace_size", "dsa_check_inputs", "dsa_kv_write", "dsa_index_key_write",
            "dsa_status_str", "dsa_last_error", "dsa_abi_version"]
 CHECK_FLAGS = {1: "seq_len", 2: "table", 4: "q_seq", 8: "q_pos", 16: "block_list"}
@@ -72,6 +74,7 @@ def load():
         "dsa_sparse_attn_decode": [kvp, qp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
         "dsa_sparse_attn_prefill": [kvp, qp, vp, vp, i32, f32, vp, vp, vp],
         "dsa_sparse_decode_fused": [kvp, qp, i32, f32, vp, vp, vp, vp, vp, sz, vp],
+        "dsa_sparse_prefill_fused": [kvp, qp, i32, f32, vp, vp, vp, vp, vp, sz, vp],
         "dsa_index_topk": [kvp, qp, i32, vp, vp, vp, sz, vp],
         "dsa_workspace_size": [ctypes.c_int, kvp, qp, i32, P(sz)],
         "dsa_check_inputs": [kvp, qp, vp, vp, i32, vp, vp],

@@ -148,6 +148,46 @@ AttnLayout attn_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k,
 }
 
 // Fused-decode workspace: attention layout | scores | idx | cnt.
+// Scoring and Top-K selection into (idx, cnt), the cheapest route for the
+// shape; scores: nq * max_blocks_per_seq floats of scratch.
+dsa_status select_blocks(const dsa::KvView& kvv, const dsa::QView& qv, int top_k, int32_t* idx,
+                         int32_t* cnt, float* scores, hipStream_t stream, const char* who) {
+  char what[96];
+  if (dsa::index_topk_fused_supported(kvv, qv)) {
+    snprintf(what, sizeof what, "%s: index_topk fused launch", who);
+    return hip_status(dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream), what);
+  }
+  if (dsa::index_cand_topk_supported(kvv, qv, top_k)) {
+    snprintf(what, sizeof what, "%s: candidate launch", who);
+    return hip_status(dsa::launch_index_cand_topk(kvv, qv, top_k, scores, idx, cnt, stream), what);
+  }
+  hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
+  if (e != hipSuccess) {
+    snprintf(what, sizeof what, "%s: score launch", who);
+    return hip_status(e, what);
+  }
+  snprintf(what, sizeof what, "%s: topk launch", who);
+  return hip_status(dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream), what);
+}
+
+// Fused prefill workspace: scores, the selection, then the block-inverted
+// attention's CSR lists and partial states.
+struct PrefillLayout {
+  size_t scores, idx, cnt, total;
+  dsa::InvLayout inv;
+};
+PrefillLayout prefill_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k) {
+  PrefillLayout f;
+  const size_t nq = (size_t)qs->num_queries;
+  f.scores = 0;
+  f.idx = align_up(nq * kv->max_blocks_per_seq * sizeof(float));
+  f.cnt = align_up(f.idx + nq * top_k * sizeof(int32_t));
+  f.inv = dsa::inv_layout(kv_view(kv), qs->num_queries, qs->num_q_heads, top_k,
+                          align_up(f.cnt + nq * sizeof(int32_t)));
+  f.total = f.inv.total;
+  return f;
+}
+
 struct FusedLayout {
   AttnLayout attn;
   size_t scores, idx, cnt, total;
@@ -201,6 +241,12 @@ dsa_status dsa_workspace_size(int op, const dsa_paged_kv* kv, const dsa_queries*
       if ((st = check_common(kv, qs, kNeedAttn | kNeedIndex)) != DSA_OK) return st;
       if ((st = check_topk(top_k)) != DSA_OK) return st;
       *bytes = fused_layout(kv, qs, top_k).total;
+      return ok();
+    }
+    case DSA_OP_PREFILL_FUSED: {
+      if ((st = check_common(kv, qs, kNeedAttn | kNeedIndex)) != DSA_OK) return st;
+      if ((st = check_topk(top_k)) != DSA_OK) return st;
+      *bytes = prefill_layout(kv, qs, top_k).total;
       return ok();
     }
     case DSA_OP_INDEX_TOPK: {
@@ -368,20 +414,41 @@ dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t
     return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
   if (qs->num_queries == 0) return ok();
-  float* scores = static_cast<float*>(workspace);
+  return select_blocks(kv_view(kv), q_view(qs), top_k, block_idx, block_cnt,
+                       static_cast<float*>(workspace), stream, "index_topk");
+}
+
+dsa_status dsa_sparse_prefill_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                                    float softmax_scale, float* out, float* lse,
+                                    int32_t* block_idx_out, int32_t* block_cnt_out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = check_common(kv, qs, kNeedAttn | kNeedIndex);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!qs->q_seq || !qs->q_pos) return fail(DSA_ERR_NULL, "prefill needs q_seq and q_pos");
+  if (!out) return fail(DSA_ERR_NULL, "out NULL");
+  if (!aligned(out, 8) || (lse && !aligned(lse, 4)))
+    return fail(DSA_ERR_ALIGN, "out needs 8 B alignment, lse 4 B");
+  if ((block_idx_out && !aligned(block_idx_out, 4)) || (block_cnt_out && !aligned(block_cnt_out, 4)))
+    return fail(DSA_ERR_ALIGN, "block_idx_out/block_cnt_out need 4 B alignment");
+  if ((block_idx_out == nullptr) != (block_cnt_out == nullptr))
+    return fail(DSA_ERR_NULL, "block_idx_out and block_cnt_out go together");
+  const PrefillLayout f = prefill_layout(kv, qs, top_k);
+  if (!workspace || workspace_bytes < f.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, f.total);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
+  if (qs->num_queries == 0) return ok();
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + f.idx);
+  int32_t* cnt = block_cnt_out ? block_cnt_out : reinterpret_cast<int32_t*>(ws + f.cnt);
   const dsa::KvView kvv = kv_view(kv);
   const dsa::QView qv = q_view(qs);
-  if (dsa::index_topk_fused_supported(kvv, qv))
-    return hip_status(dsa::launch_index_topk_fused(kvv, qv, top_k, block_idx, block_cnt, stream),
-                      "index_topk: fused launch");
-  if (dsa::index_cand_topk_supported(kvv, qv, top_k))
-    return hip_status(dsa::launch_index_cand_topk(kvv, qv, top_k, scores, block_idx, block_cnt,
-                                                  stream),
-                      "index_topk: candidate launch");
-  hipError_t e = dsa::launch_index_score(kvv, qv, scores, stream);
-  if (e != hipSuccess) return hip_status(e, "index_topk: score launch");
-  return hip_status(dsa::launch_topk(scores, kvv, qv, top_k, block_idx, block_cnt, stream),
-                    "index_topk: topk launch");
+  st = select_blocks(kvv, qv, top_k, idx, cnt, reinterpret_cast<float*>(ws + f.scores), stream,
+                     "prefill_fused");
+  if (st != DSA_OK) return st;
+  return hip_status(dsa::launch_prefill_inv(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse, ws,
+                                            f.inv, stream),
+                    "prefill_fused: block-inverted attention launch");
 }
 
 dsa_status dsa_kv_write(const dsa_paged_kv* kv, int32_t n_tokens, const int32_t* tok_seq,

@@ -15,7 +15,7 @@ constexpr int kMaxIdxHeads = 16;
 constexpr int kMaxTopK = 4096;
 
 struct KvView {
-  const uint16_t* k;        // bf16 [P, 64, Hkv, 128]
+  const uint16_t* k;        // bf16 [P, block size, Hkv, 128]
   const uint16_t* v;
   const uint8_t* idx_keys;  // [P, dI]
   const float* idx_scale;   // [P]
@@ -111,5 +111,22 @@ hipError_t launch_index_key_write(const KvView& kv, int n, const int32_t* blk, c
 hipError_t launch_check_inputs(const KvView& kv, const QView& q, const int32_t* block_idx,
                                const int32_t* block_cnt, int top_k, uint32_t* flags,
                                hipStream_t s);
+
+// Block-inverted prefill attention (prefill_inv.hip): the selection becomes a
+// CSR list "pool tile -> (query, pick)", one workgroup per (tile, KV head)
+// attends all of a tile's queries, and a merge combines each query's partial
+// states {o[128], m, l, pad} (kInvPartRow floats per (query, pick, head)).
+constexpr int kInvPartRow = kHeadDim + 4;
+struct InvLayout {
+  int items_max;      // item slots per query: top_k * tiles per block
+  long pool_tiles;    // num_blocks * tiles per block
+  long tile_slots;    // grid rows of the attention kernel
+  size_t n_items, count, offset, cursor, tiles, n_tiles, entries, part, total;  // byte offsets
+};
+InvLayout inv_layout(const KvView& kv, int nq, int hq, int top_k, size_t base);
+bool prefill_inv_supported(const KvView& kv, const QView& q);
+hipError_t launch_prefill_inv(const KvView& kv, const QView& q, const int32_t* idx,
+                              const int32_t* cnt, int top_k, float scale, float* out, float* lse,
+                              char* ws, const InvLayout& layout, hipStream_t s);
 
 }  // namespace dsa

@@ -190,6 +190,29 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * One-call chunked prefill ([P1] section 4(3): prefill is compute-intensive,
+ * and scoring, block selection and attention can run as one pipeline; [P3]
+ * section 4.3: selection fused with the attention inside blocks; [P5]
+ * "Differentiated Adaptation of Prefill and Decode": batch the prefill's
+ * selection).  The selection is that of dsa_index_topk; the attention is that
+ * of dsa_sparse_attn_prefill (same formula and tolerance, a different
+ * summation order), computed block-inverted: the selection is transposed into
+ * per-pool-tile lists of (query, pick), each 64-token tile of K/V is read once
+ * per KV head for all the queries that picked it, and one partial softmax
+ * state per (query, pick, head) is merged per query in pick order (results do
+ * not depend on scheduling).  q_seq and q_pos are required; out: fp32
+ * [Nq, Hq, 128], 8 B aligned; lse (nullable) fp32 [Nq, Hq].  block_idx_out /
+ * block_cnt_out (nullable, together) receive the selection.  workspace: at
+ * least dsa_workspace_size(DSA_OP_PREFILL_FUSED) bytes, 256 B aligned; it
+ * grows as Nq * top_k * (block_size / 64) * Hq * 528 B (the partial states:
+ * 17.7 GB for 8192 queries, K 64, 64 query heads, 64-token blocks).
+ */
+dsa_status dsa_sparse_prefill_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                                    float softmax_scale, float* out, float* lse,
+                                    int32_t* block_idx_out, int32_t* block_cnt_out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Scoring and selection in one entry point ([P3] section 4.1: top-k fused
  * with the scoring before it to avoid materialising intermediate tensors).
  * Same block_idx / block_cnt as dsa_index_score followed by dsa_topk_blocks.
@@ -273,7 +296,8 @@ dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
                             uint32_t* flags, hipStream_t stream);
 
 /* Workspace sizes.  op: one of the DSA_OP_* values. */
-enum { DSA_OP_ATTN_DECODE = 1, DSA_OP_DECODE_FUSED = 2, DSA_OP_INDEX_TOPK = 3 };
+enum { DSA_OP_ATTN_DECODE = 1, DSA_OP_DECODE_FUSED = 2, DSA_OP_INDEX_TOPK = 3,
+       DSA_OP_PREFILL_FUSED = 4 };
 dsa_status dsa_workspace_size(int op, const dsa_paged_kv* kv, const dsa_queries* qs,
                               int32_t top_k, size_t* bytes);
 

@@ -155,6 +155,29 @@ def test_workspace_contract(lib):
                                   ctypes.byref(m)) == E["DSA_ERR_SHAPE"]
 
 
+def test_prefill_fused_contract(lib):
+    E = {v: k for k, v in _lib.STATUS.items()}
+    kv, qs = _kv(), _qs(q_seq=FAKE, q_pos=FAKE)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_workspace_size(_lib.OP_PREFILL_FUSED, ctypes.byref(kv), ctypes.byref(qs), 4,
+                                  ctypes.byref(n)) == 0
+    # at least one partial state {o[128], m, l, pad} per (query, pick, head)
+    assert n.value >= qs.num_queries * 4 * qs.num_q_heads * 132 * 4
+
+    def call(kv=kv, qs=qs, top_k=4, out=FAKE, ws=FAKE, nbytes=n.value, bi=None, bc=None):
+        return lib.dsa_sparse_prefill_fused(ctypes.byref(kv), ctypes.byref(qs), top_k, 0.1, out,
+                                            None, bi, bc, ws, nbytes, None)
+    assert call(nbytes=n.value - 1) == E["DSA_ERR_WORKSPACE"]
+    assert call(ws=FAKE + 64) == E["DSA_ERR_ALIGN"]
+    assert call(out=FAKE + 4) == E["DSA_ERR_ALIGN"]
+    assert call(out=None) == E["DSA_ERR_NULL"]
+    assert call(bi=FAKE) == E["DSA_ERR_NULL"]          # block_idx_out without block_cnt_out
+    assert call(qs=_qs(q_seq=None, q_pos=FAKE)) == E["DSA_ERR_NULL"]
+    assert call(top_k=0) == E["DSA_ERR_SHAPE"]
+    assert call(kv=_kv(block_size=96)) == E["DSA_ERR_UNSUPPORTED"]
+    assert call(qs=_qs(q_seq=FAKE, q_pos=FAKE, num_queries=0)) == 0
+
+
 def test_empty_batch_is_a_noop(lib):
     # Nq == 0 returns DSA_OK without launching anything (no GPU needed)
     assert _score(lib, _kv(), _qs(num_queries=0)) == 0

@@ -1,0 +1,121 @@
+"""GPU parity of the one-call chunked prefill (dsa_sparse_prefill_fused: scoring,
+selection, then the block-inverted attention) against the oracle: the
+selection bit for bit, attention and lse to the usual bar, for every query
+of chunks that span several tiles and end mid-block.  Also: every grouping
+of query heads (1, 2, 4, 8, 16 per KV head, and 3 and 12, which take one
+query per MFMA tile), block sizes 64-512, several sequences in one chunk,
+both scorers, and run-to-run bit determinism."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from dsa_synth import workload
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as m
+    m._lib.load()
+    return m
+
+
+def _run(dsa, w, label):
+    kv, qs = parity.to_device(w)
+    K = w.top_k
+    bi = torch.empty(w.num_queries, K, dtype=torch.int32, device="cuda")
+    bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
+    out, lse, _, _ = dsa.prefill_fused(kv, qs, K, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    bi_h, bc_h = bi.cpu().numpy(), bc.cpu().numpy()
+    worst = (0.0, 0.0)
+    for qi in range(w.num_queries):
+        r = parity.oracle_query(w, qi)
+        ok, swapped = parity.check_indices(bi_h[qi], bc_h[qi], r, K)
+        assert ok, f"{label} q{qi}: idx {bi_h[qi]} cnt {bc_h[qi]} vs {r['idx']} {r['cnt']}"
+        if swapped:  # a near-tie swap: attention is checked on the GPU's own selection
+            r = parity.oracle_query(w, qi, sel_override=bi_h[qi][:bc_h[qi]])
+        good, a, rel = parity.attn_ok(out_h[qi], r["out"])
+        assert good, f"{label} q{qi}: attention max-abs {a:.3e} max-rel {rel:.3e}"
+        la, _ = parity.attn_errors(lse_h[qi], r["lse"])
+        assert la <= 1e-3, f"{label} q{qi}: lse max-abs {la:.3e}"
+        worst = (max(worst[0], a), max(worst[1], rel))
+    _say(f"{label}: {w.num_queries} queries ok; worst attention max-abs {worst[0]:.2e} "
+         f"max-rel {worst[1]:.2e}")
+    return kv, qs, out, lse
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (8, 8), (4, 2), (16, 4), (16, 1), (6, 2), (24, 2)],
+                         ids=["G8", "G1", "G2", "G4", "G16", "G3", "G12"])
+def test_prefill_fused_head_groups(dsa, hq, hkv):
+    w = workload.small_prefill(seed=2800 + hq * 3 + hkv, L=64 * 20 - 5, count=70, hq=hq, hkv=hkv,
+                               hi=4, di=128, top_k=6)
+    _run(dsa, w, f"prefill_fused hq{hq} hkv{hkv}")
+
+
+@pytest.mark.parametrize("bs", [64, 128, 256, 512])
+def test_prefill_fused_block_sizes(dsa, bs):
+    w = workload.small_prefill(seed=2820 + bs, L=bs * 11 + 37, count=80, hq=16, hkv=2, hi=8,
+                               di=64, top_k=4, bs=bs)
+    _run(dsa, w, f"prefill_fused bs{bs}")
+
+
+def test_prefill_fused_many_queries_int8_scorer(dsa):
+    """300 queries of one sequence: scored on the int8 matrix cores."""
+    w = workload.small_prefill(seed=2840, L=64 * 300 + 13, count=300, hq=16, hkv=2, hi=8, di=64,
+                               top_k=16)
+    _run(dsa, w, "prefill_fused 300q")
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_prefill_fused_several_sequences(dsa, interleave):
+    w = workload.multi_prefill(seed=2850 + interleave, interleave=interleave)
+    _run(dsa, w, f"prefill_fused multi interleave={interleave}")
+
+
+def test_prefill_fused_matches_per_query_kernel_and_is_deterministic(dsa):
+    """The same selection through the per-query prefill kernel gives the same
+    attention to within rounding; two fused runs agree bit for bit."""
+    w = workload.small_prefill(seed=2860, L=64 * 40 + 9, count=150, hq=32, hkv=4, hi=4, di=128,
+                               top_k=12)
+    kv, qs, out, lse = _run(dsa, w, "prefill_fused vs per-query")
+    bi = torch.empty(w.num_queries, w.top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
+    out2, lse2, _, _ = dsa.prefill_fused(kv, qs, w.top_k, w.softmax_scale, block_idx=bi,
+                                         block_cnt=bc)
+    ref, ref_lse = dsa.sparse_attn_prefill(kv, qs, bi, bc, w.top_k, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert float((out - ref).abs().max()) < 1e-4
+    assert float((lse - ref_lse).abs().max()) < 1e-4
+
+
+def test_prefill_fused_workspace_reuse(dsa):
+    """One workspace sized for the larger chunk serves a smaller one after it
+    (the CSR counters are cleared on every call)."""
+    big = workload.small_prefill(seed=2870, L=64 * 30 + 1, count=120, hq=16, hkv=2, hi=4, di=128,
+                                 top_k=8)
+    small = workload.small_prefill(seed=2871, L=64 * 9 + 50, count=40, hq=16, hkv=2, hi=4,
+                                   di=128, top_k=8)
+    from dynamic_sparse_attention_paged_amd import _lib
+    kv_b, qs_b = parity.to_device(big)
+    ws = dsa.make_workspace(_lib.OP_PREFILL_FUSED, kv_b, qs_b, 8)
+    for w in (big, small):
+        kv, qs = parity.to_device(w)
+        out, _, _, _ = dsa.prefill_fused(kv, qs, 8, w.softmax_scale, workspace=ws)
+        fresh, _, _, _ = dsa.prefill_fused(kv, qs, 8, w.softmax_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh), w.name
