@@ -34,7 +34,9 @@ METRIC = "decode queries/sec + achieved HBM GB/s (% roofline); prefill indexer M
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 INT8_PEAK_TOPS = 5000.0
-ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", "attn.hip")
+# the decode attention kernel's sources (the traffic counters are keyed to them)
+ATTN_SRCS = [os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", f)
+             for f in ("attn.hip", "attn_tile.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_split_batched_decode.json")
 
 
@@ -174,7 +176,7 @@ def traffic_from_profile():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()
         if t.get("attn_src_sha256") != src:
             return None
         return t.get("bytes_per_launch")

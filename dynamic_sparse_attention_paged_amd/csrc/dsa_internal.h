@@ -115,13 +115,14 @@ hipError_t launch_check_inputs(const KvView& kv, const QView& q, const int32_t* 
 // Block-inverted prefill attention (prefill_inv.hip): the selection becomes a
 // CSR list "pool tile -> (query, pick)", one workgroup per (tile, KV head)
 // attends all of a tile's queries, and a merge combines each query's partial
-// states {o[128], m, l, pad} (kInvPartRow floats per (query, pick, head)).
-constexpr int kInvPartRow = kHeadDim + 4;
+// states: o[128] (512 B rows, whole cache lines) and {m, l}, per (query, head,
+// pick).
 struct InvLayout {
   int items_max;      // item slots per query: top_k * tiles per block
   long pool_tiles;    // num_blocks * tiles per block
   long tile_slots;    // grid rows of the attention kernel
-  size_t n_items, count, offset, cursor, tiles, n_tiles, entries, part, total;  // byte offsets
+  long entries_max;   // nq * items_max: (query, pick) slots
+  size_t n_items, count, offset, cursor, tiles, n_tiles, entries, part_o, part_ml, total;  // bytes
 };
 InvLayout inv_layout(const KvView& kv, int nq, int hq, int top_k, size_t base);
 bool prefill_inv_supported(const KvView& kv, const QView& q);

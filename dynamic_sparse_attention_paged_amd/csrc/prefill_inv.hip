@@ -109,12 +109,14 @@ __device__ __forceinline__ int2 wave_incl_scan(int2 v) {
 }
 
 // One workgroup: offset[t] = sum of count[< t] (offset[T] = total), cursor =
-// offset, and the non-empty tiles in ascending order in tiles[0 .. *n_tiles).
+// offset, the non-empty tiles in ascending order in tiles[0 .. *n_tiles), and
+// the sentinel entry.
 __global__ __launch_bounds__(kScanThreads) void inv_scan(const int32_t* __restrict__ count,
                                                           int T, int32_t* __restrict__ offset,
                                                           int32_t* __restrict__ cursor,
                                                           int32_t* __restrict__ tiles,
-                                                          int32_t* __restrict__ n_tiles) {
+                                                          int32_t* __restrict__ n_tiles,
+                                                          int4* __restrict__ sentinel, int nq) {
   __shared__ int2 wsum[kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (T + kScanThreads - 1) / kScanThreads;
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan(const int32_t* __restri
   if (tid == kScanThreads - 1) {
     offset[T] = run;
     *n_tiles = k;
+    *sentinel = make_int4(nq, 0, 0, -1);  // the entry of columns without one
   }
 }
 
@@ -153,8 +156,9 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan(const int32_t* __restri
 template <int kQPT>
 __global__ __launch_bounds__(kInvThreads) void inv_attend(
     KvView kv, QView Q, const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    const int32_t* __restrict__ offset, const int4* __restrict__ entries, int items_max,
-    float scale2, float* __restrict__ part) {
+    const int32_t* __restrict__ offset, int4* entries, int sentinel,
+    int items_max,
+    float scale2, float* __restrict__ part_o, float2* __restrict__ part_ml) {
   __shared__ uint16_t vs[64 * kHeadDim];
   if ((int)blockIdx.x >= *n_tiles) return;  // the whole workgroup
   const int tile_id = tiles[blockIdx.x];
@@ -183,23 +187,30 @@ __global__ __launch_bounds__(kInvThreads) void inv_attend(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  constexpr int kG = kQPT > 1 ? 16 / kQPT : 0;
+  constexpr int kG = kQPT > 1 ? 16 / kQPT : 1;
   const int ce = kQPT > 1 ? r / kG : 0;       // entry of the column within the MFMA tile
   const int hl = kQPT > 1 ? r - ce * kG : r;  // head of the column within group g
   const bool col_ok = hl < G;
-  for (int e = e0 + wave * kQPT; e < e1; e += 4 * kQPT) {
+  // Software pipeline over MFMA tiles, unrolled by two with two register sets
+  // (no copies between iterations): while a tile computes, the Q rows of the
+  // next one and the entries of the one after are in flight.  The body has no
+  // branches, so the compiler's waits stay partial: a column without an entry
+  // reads the sentinel entry {query Nq, pick 0, lim -1} (every token masked),
+  // whose partial rows lie in a trash region past the last query's, and its
+  // Q row is read from query Nq - 1.  entries is not declared read-only: that
+  // keeps the compiler from re-reading an entry (with a full wait) instead of
+  // holding it in a register.
+  auto entry_at = [&](int e) {
     const int my_e = e + ce;
-    const bool ok = col_ok && my_e < e1;
-    const int4 en = ok ? entries[my_e] : make_int4(0, 0, 0, -1);  // lim -1: all masked
-    i16x8 qf[4];
-    if (ok) {
-      const uint16_t* qp = Q.q + ((size_t)en.x * Q.hq + g * G + hl) * kHeadDim + 8 * gq;
+    return entries[(col_ok && my_e < e1) ? my_e : sentinel];
+  };
+  auto load_q = [&](const int4& en, i16x8 (&qf)[4]) {
+    const int qq = min(en.x, Q.nq - 1);
+    const uint16_t* qp = Q.q + ((size_t)qq * Q.hq + g * G + hl) * kHeadDim + 8 * gq;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[c] = *reinterpret_cast<const i16x8*>(qp + 32 * c);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf[c] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int c = 0; c < 4; ++c) qf[c] = *reinterpret_cast<const i16x8*>(qp + 32 * c);
+  };
+  auto compute = [&](const int4& en, const i16x8 (&qf)[4]) {
     f32x4 sc[4];
     block_logits(kf, qf, sc);
     WaveState st;
@@ -208,44 +219,109 @@ __global__ __launch_bounds__(kInvThreads) void inv_attend(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     block_softmax_pv(sc, scale2, en.z, en.w, vs, st);
-    if (ok) {
-      const size_t row = ((size_t)en.x * items_max + en.y) * Q.hq + g * G + hl;
-      float* pr = part + row * kInvPartRow;
+    // partial rows [query][head][pick]: a query's picks of one head are contiguous
+    const size_t row = ((size_t)en.x * Q.hq + g * G + hl) * items_max + en.y;
+    // streaming stores: the partial states are read once, by the merge, long
+    // after; they should not push the Q rows out of the caches
+    float* pr = part_o + row * kHeadDim;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(pr + 16 * dt + 4 * gq) = st.o[dt];
-      if (gq == 0) *reinterpret_cast<float2*>(pr + kHeadDim) = make_float2(st.m, st.l);
-    }
+    for (int dt = 0; dt < 8; ++dt)
+      __builtin_nontemporal_store(st.o[dt], reinterpret_cast<f32x4*>(pr + 16 * dt + 4 * gq));
+    // the column's four lanes hold the same values
+    __builtin_nontemporal_store(f32x2{st.m, st.l}, reinterpret_cast<f32x2*>(part_ml + row));
+  };
+  // keeps the scheduler from sinking the prefetches down to their uses
+  auto pin_order = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int kStep = 4 * kQPT;
+  int e = e0 + wave * kQPT;
+  if (e >= e1) return;
+  // The first tile is peeled, so that the loop is entered with the same
+  // loads and stores in flight as at its back edge.
+  int4 enA = entry_at(e), enB = entry_at(e + kStep);
+  i16x8 qfA[4], qfB[4];
+  load_q(enA, qfA);
+  load_q(enB, qfB);
+  int4 enA2 = entry_at(e + 2 * kStep);
+  pin_order();
+  compute(enA, qfA);
+  if (e + kStep >= e1) return;
+  for (;;) {
+    load_q(enA2, qfA);
+    const int4 enB2 = entry_at(e + 3 * kStep);
+    pin_order();
+    compute(enB, qfB);
+    e += 2 * kStep;
+    if (e >= e1) break;
+    load_q(enB2, qfB);
+    const int4 enA3 = entry_at(e + 2 * kStep);
+    pin_order();
+    compute(enA2, qfA);
+    if (e + kStep >= e1) break;
+    enB = enB2;
+    enA2 = enA3;
   }
 }
 
-// grid (Nq, Hq), one wave: combine query q's partials of head h in pick order
-// (lane l: dims 2l, 2l + 1).
-__global__ __launch_bounds__(64) void inv_merge(const float* __restrict__ part,
+// grid (Nq, Hq), one wave: combine query q's partials of head h in pick order.
+// The picks' (m, l) are read one per lane; lane l then sums dims 2l, 2l + 1 of
+// the o rows, o being unnormalized (sum of 2^(x - m) V):
+//   O = sum_k 2^(m_k - M) o_k,  L = sum_k 2^(m_k - M) l_k,  out = O / L.
+__global__ __launch_bounds__(64) void inv_merge(const float* __restrict__ part_o,
+                                                const float2* __restrict__ part_ml,
                                                 const int32_t* __restrict__ n_items,
                                                 int items_max, int hq, float* __restrict__ out,
                                                 float* __restrict__ lse) {
   const int q = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int n = n_items[q];
-  const size_t stride = (size_t)hq * kInvPartRow;
-  const float* pr = part + ((size_t)q * items_max * hq + h) * kInvPartRow;
-  float M = -INFINITY;
-  for (int k = 0; k < n; ++k) M = fmaxf(M, pr[k * stride + kHeadDim]);
-  // o is unnormalized (sum of 2^(x - m) V): O = sum 2^(m - M) o, L = sum 2^(m - M) l
-  float L = 0.f;
-  float2 O = make_float2(0.f, 0.f);
-#pragma unroll 4
-  for (int k = 0; k < n; ++k) {
-    const float* pk = pr + k * stride;
-    const float2 ml = *reinterpret_cast<const float2*>(pk + kHeadDim);
-    const float f = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
-    const float2 o = *reinterpret_cast<const float2*>(pk + 2 * lane);
-    L += f * ml.y;
-    O.x += f * o.x;
-    O.y += f * o.y;
-  }
   const size_t qh = (size_t)q * hq + h;
-  *reinterpret_cast<float2*>(out + qh * kHeadDim + 2 * lane) = make_float2(O.x / L, O.y / L);
-  if (lse && lane == 0) lse[qh] = (M + log2f(L)) * kLn2;
+  const float* po = part_o + qh * items_max * kHeadDim + 2 * lane;
+  const float2* pml = part_ml + qh * items_max;
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < n; c0 += 64)
+    if (c0 + lane < n) M = fmaxf(M, pml[c0 + lane].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float Lp = 0.f;
+  float2 O = make_float2(0.f, 0.f);
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    float f = 0.f;
+    if (c0 + lane < n) {
+      const float2 ml = pml[c0 + lane];
+      f = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      Lp += f * ml.y;
+    }
+    const int cn = min(64, n - c0);
+    const float* rows = po + (size_t)c0 * kHeadDim;
+    auto fj = [&](int j) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+    };
+    auto row = [&](int j) {
+      return __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(rows + (size_t)j * kHeadDim));
+    };
+    int j = 0;
+    for (; j + 8 <= cn; j += 8) {  // eight rows in flight, summed in pick order
+      f32x2 o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = row(j + u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        O.x += fj(j + u) * o[u][0];
+        O.y += fj(j + u) * o[u][1];
+      }
+    }
+    for (; j < cn; ++j) {
+      const f32x2 o = row(j);
+      O.x += fj(j) * o[0];
+      O.y += fj(j) * o[1];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off, 64);
+  *reinterpret_cast<float2*>(out + qh * kHeadDim + 2 * lane) = make_float2(O.x / Lp, O.y / Lp);
+  if (lse && lane == 0) lse[qh] = (M + log2f(Lp)) * kLn2;
 }
 
 template <int kQPT>
@@ -256,8 +332,9 @@ void launch_attend(const KvView& kv, const QView& Q, const InvLayout& L, char* w
                      reinterpret_cast<const int32_t*>(ws + L.tiles),
                      reinterpret_cast<const int32_t*>(ws + L.n_tiles),
                      reinterpret_cast<const int32_t*>(ws + L.offset),
-                     reinterpret_cast<const int4*>(ws + L.entries), L.items_max, scale2,
-                     reinterpret_cast<float*>(ws + L.part));
+                     reinterpret_cast<int4*>(ws + L.entries), (int)L.entries_max,
+                     L.items_max, scale2, reinterpret_cast<float*>(ws + L.part_o),
+                     reinterpret_cast<float2*>(ws + L.part_ml));
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -270,6 +347,7 @@ InvLayout inv_layout(const KvView& kv, int nq, int hq, int top_k, size_t base) {
   L.items_max = top_k << sub;
   L.pool_tiles = (long)kv.num_blocks << sub;
   const long entries = (long)nq * L.items_max;
+  L.entries_max = entries;
   L.tile_slots = L.pool_tiles < entries ? L.pool_tiles : entries;
   size_t at = align256(base);
   L.n_items = at;
@@ -284,10 +362,16 @@ InvLayout inv_layout(const KvView& kv, int nq, int hq, int top_k, size_t base) {
   at = align256(at + (size_t)L.pool_tiles * 4);
   L.n_tiles = at;
   at = align256(at + 4);
+  // entries, then the sentinel entry
   L.entries = at;
-  at = align256(at + (size_t)entries * sizeof(int4));
-  L.part = at;
-  at = align256(at + (size_t)entries * hq * kInvPartRow * sizeof(float));
+  at = align256(at + (size_t)(entries + 1) * sizeof(int4));
+  // partial rows [query][head][pick], then the sentinel query's (Nq): hq + 16
+  // heads' worth, enough for any column of any KV head
+  const size_t rows = ((size_t)nq * hq + hq + 16) * L.items_max;
+  L.part_o = at;
+  at = align256(at + rows * kHeadDim * sizeof(float));
+  L.part_ml = at;
+  at = align256(at + rows * sizeof(float2));
   L.total = at;
   return L;
 }
@@ -317,7 +401,7 @@ hipError_t launch_prefill_inv(const KvView& kv, const QView& Q, const int32_t* i
   hipLaunchKernelGGL(inv_scan, dim3(1), dim3(kScanThreads), 0, st, count, (int)L.pool_tiles,
                      reinterpret_cast<int32_t*>(ws + L.offset), cursor,
                      reinterpret_cast<int32_t*>(ws + L.tiles),
-                     reinterpret_cast<int32_t*>(ws + L.n_tiles));
+                     reinterpret_cast<int32_t*>(ws + L.n_tiles), entries + L.entries_max, Q.nq);
   hipLaunchKernelGGL(inv_entries<true>, dim3(egu), dim3(kInvThreads), 0, st, kv, Q, idx, cnt,
                      top_k, L.items_max, cursor, n_items, entries);
   const int G = Q.hq / kv.num_kv_heads;
@@ -329,7 +413,8 @@ hipError_t launch_prefill_inv(const KvView& kv, const QView& Q, const int32_t* i
     default: launch_attend<1>(kv, Q, L, ws, scale2, st); break;
   }
   hipLaunchKernelGGL(inv_merge, dim3(Q.nq, Q.hq), dim3(64), 0, st,
-                     reinterpret_cast<const float*>(ws + L.part), n_items, L.items_max, Q.hq, out,
+                     reinterpret_cast<const float*>(ws + L.part_o),
+                     reinterpret_cast<const float2*>(ws + L.part_ml), n_items, L.items_max, Q.hq, out,
                      lse);
   return hipGetLastError();
 }

@@ -204,7 +204,7 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
  * [Nq, Hq, 128], 8 B aligned; lse (nullable) fp32 [Nq, Hq].  block_idx_out /
  * block_cnt_out (nullable, together) receive the selection.  workspace: at
  * least dsa_workspace_size(DSA_OP_PREFILL_FUSED) bytes, 256 B aligned; it
- * grows as Nq * top_k * (block_size / 64) * Hq * 528 B (the partial states:
+ * grows as Nq * top_k * (block_size / 64) * Hq * 520 B (the partial states:
  * 17.7 GB for 8192 queries, K 64, 64 query heads, 64-token blocks).
  */
 dsa_status dsa_sparse_prefill_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
