@@ -219,8 +219,10 @@ __global__ __launch_bounds__(kInvThreads) void inv_attend(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     block_softmax_pv(sc, scale2, en.z, en.w, vs, st);
-    // partial rows [query][head][pick]: a query's picks of one head are contiguous
-    const size_t row = ((size_t)en.x * Q.hq + g * G + hl) * items_max + en.y;
+    // partial rows [head][query][pick]: a query's picks of one head are
+    // contiguous, and the workgroups running together (one KV head: the tile
+    // index varies fastest in the grid) write into one head group's region
+    const size_t row = ((size_t)(g * G + hl) * (Q.nq + 1) + en.x) * items_max + en.y;
     // (plain stores: the two 64 B halves of a row's 128 B line, written by
     // consecutive instructions, merge in L2; streaming stores measured 23%
     // more HBM write traffic)
@@ -276,8 +278,9 @@ __global__ __launch_bounds__(64) void inv_merge(const float* __restrict__ part_o
   const int q = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int n = n_items[q];
   const size_t qh = (size_t)q * hq + h;
-  const float* po = part_o + qh * items_max * kHeadDim + 2 * lane;
-  const float2* pml = part_ml + qh * items_max;
+  const size_t hq_row = ((size_t)h * (gridDim.x + 1) + q) * items_max;  // [head][query (+ sentinel)][pick]
+  const float* po = part_o + hq_row * kHeadDim + 2 * lane;
+  const float2* pml = part_ml + hq_row;
   float M = -INFINITY;
   for (int c0 = 0; c0 < n; c0 += 64)
     if (c0 + lane < n) M = fmaxf(M, pml[c0 + lane].x);
@@ -364,9 +367,9 @@ InvLayout inv_layout(const KvView& kv, int nq, int hq, int top_k, size_t base) {
   // entries, then the sentinel entry
   L.entries = at;
   at = align256(at + (size_t)(entries + 1) * sizeof(int4));
-  // partial rows [query][head][pick], then the sentinel query's (Nq): hq + 16
-  // heads' worth, enough for any column of any KV head
-  const size_t rows = ((size_t)nq * hq + hq + 16) * L.items_max;
+  // partial rows [head][query][pick], each head with the sentinel query Nq
+  // after its real ones, plus 16 heads' worth for columns past the last head
+  const size_t rows = ((size_t)(hq + 16) * (nq + 1)) * L.items_max;
   L.part_o = at;
   at = align256(at + rows * kHeadDim * sizeof(float));
   L.part_ml = at;
