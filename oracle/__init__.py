@@ -34,6 +34,9 @@ What the pages fix, and what the oracle follows:
   * the write path: tokens' K/V rows go to their blocks through the table,
     and each block's coarse key is stored as E4M3 codes with a per-block
     float32 scale ([P5] "KV Cache Layout"; [P1] section 4(2)); write.py.
+  * the MXFP4 expert path: MXFP4 weights unpacked to an FP8 workspace, and
+    the grouped expert matmul in FP8 with block scales ([P1] section 5; [P2]
+    sections 3.1-3.2; [P5] "MXFP4 Expert Weights"); moe.py.
 
 Where the pages are silent the oracle takes the plainest reading; each reading
 is named in the function that uses it.  Parity pins: every function in this

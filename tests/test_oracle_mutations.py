@@ -12,21 +12,25 @@ import pytest
 import oracle
 import oracle.dsa as D
 import oracle.fp8 as F
+import oracle.moe as M
 import oracle.pipeline as P
 import oracle.write as W
 from tests import test_oracle_attention as TA
 from tests import test_oracle_fp8 as TF
+from tests import test_oracle_moe as TM
 from tests import test_oracle_score as TS
 from tests import test_oracle_select as TSEL
 from tests import test_oracle_write as TW
 
-_MODULES = (oracle, D, F, P, W, TA, TF, TS, TSEL, TW)
+_MODULES = (oracle, D, F, M, P, W, TA, TF, TM, TS, TSEL, TW)
 _real = {name: getattr(D, name, None) or getattr(F, name, None) or getattr(P, name, None)
          or getattr(W, name)
          for name in ("e4m3_decode", "e4m3_encode", "quantize_q_idx", "index_scores",
                       "select_blocks", "visible_blocks", "_gather_tokens",
                       "attention_partial", "merge_partials", "sparse_attention",
                       "dense_attention", "score_query", "quantize_coarse_key", "kv_write")}
+_real.update({name: getattr(M, name) for name in ("e2m1_decode", "unpack_fp4", "mxfp4_dequant",
+                                                    "mx_quantize_e4m3", "mx_dequant_e4m3")})
 
 
 def _patch(monkeypatch, name, fn):
@@ -195,6 +199,44 @@ def kv_write_position_off_by_one(k_pool, v_pool, table, seq_lens, tok_seq, tok_p
                              v_new, block_size)
 
 
+def e2m1_exponent_bias_zero(codes):
+    c = np.asarray(codes).astype(np.int64)
+    v = _real["e2m1_decode"](c)
+    return np.where(((c >> 1) & 3) > 0, 2 * v, v)  # normals doubled
+
+
+def unpack_high_nibble_first(packed, k):
+    p = np.asarray(packed).astype(np.uint8)
+    return _real["unpack_fp4"](((p & 0x0F) << 4) | (p >> 4), k)
+
+
+def mxfp4_scale_bias_128(packed, scales):
+    return _real["mxfp4_dequant"](packed, scales) * 0.5
+
+
+def mx_quantize_emax_7(x):
+    # shared exponent floor(log2 amax) - 7: block maxima land in [128, 256)
+    x = np.asarray(x, dtype=np.float64)
+    _, s = _real["mx_quantize_e4m3"](x)
+    s2 = np.where(s > 0, s.astype(np.int64) + 1, 0)
+    y = x / np.repeat(np.exp2(s2 - 127.0), 32, -1)
+    return F.e4m3_encode(np.clip(y, -448.0, 448.0)), s2.astype(np.uint8)
+
+
+def mx_quantize_ceil_log2(x):
+    x = np.asarray(x, dtype=np.float64)
+    codes, s = _real["mx_quantize_e4m3"](x)
+    blocks = np.abs(x).reshape(x.shape[:-1] + (-1, 32)).max(-1)
+    pow2 = (blocks > 0) & (np.frexp(np.where(blocks > 0, blocks, 1.0))[0] == 0.5)
+    bump = (blocks > 0) & ~pow2
+    c2, _ = _real["mx_quantize_e4m3"](x / np.repeat(np.where(bump, 2.0, 1.0), 32, -1))
+    return c2, np.where(bump, s + 1, s).astype(np.uint8)
+
+
+def mx_dequant_ignores_scale(codes, scales):
+    return F.e4m3_decode(codes)
+
+
 CASES = [
     ("e4m3_decode", decode_wrong_bias, ["TF.test_spot_codes"]),
     ("e4m3_encode", encode_ties_away, ["TF.test_encode_ties_to_even",
@@ -223,13 +265,23 @@ CASES = [
     ("quantize_coarse_key", coarse_key_truncated, ["TW.test_codes_match_torch_float8_conversion",
                                                    "TW.test_largest_entry_and_error_bound"]),
     ("kv_write", kv_write_position_off_by_one, ["TW.test_kv_write_round_trip"]),
+    ("e2m1_decode", e2m1_exponent_bias_zero, ["TM.test_e2m1_matches_the_spec_table"]),
+    ("unpack_fp4", unpack_high_nibble_first, ["TM.test_fp4_packing_low_nibble_first",
+                                              "TM.test_grouped_gemm_brute_force"]),
+    ("mxfp4_dequant", mxfp4_scale_bias_128, ["TM.test_fp8_workspace_is_exact_and_matches_torch_encoder",
+                                             "TM.test_grouped_gemm_brute_force"]),
+    ("mx_quantize_e4m3", mx_quantize_emax_7, ["TM.test_mxfp8_hand_example",
+                                              "TM.test_mxfp8_matches_torch_encoder_and_range"]),
+    ("mx_quantize_e4m3", mx_quantize_ceil_log2, ["TM.test_mxfp8_hand_example",
+                                                 "TM.test_mxfp8_matches_torch_encoder_and_range"]),
+    ("mx_dequant_e4m3", mx_dequant_ignores_scale, ["TM.test_grouped_gemm_brute_force"]),
 ]
 
 
 @pytest.mark.parametrize("name,mutant,pins", CASES, ids=[c[1].__name__ for c in CASES])
 def test_pins_catch_mutant(monkeypatch, golden, name, mutant, pins):
     _patch(monkeypatch, name, mutant)
-    mods = {"TA": TA, "TF": TF, "TS": TS, "TSEL": TSEL, "TW": TW}
+    mods = {"TA": TA, "TF": TF, "TM": TM, "TS": TS, "TSEL": TSEL, "TW": TW}
     failures = 0
     for pin in pins:
         mod, fn = pin.split(".")
