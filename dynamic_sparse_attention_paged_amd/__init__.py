@@ -319,3 +319,77 @@ def index_key_write(kv, block_ids, coarse):
     _check(lib.dsa_index_key_write(ctypes.byref(kvs), int(block_ids.shape[0]),
                                    block_ids.data_ptr(), coarse.data_ptr(),
                                    _stream(kv.idx_keys.device)))
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 expert weights
+# ---------------------------------------------------------------------------
+@dataclass
+class MxExperts:
+    w_fp4: torch.Tensor    # uint8 [E, N, K/2]: E2M1 codes, element 2i in the low nibble
+    w_scale: torch.Tensor  # uint8 [E, N, K/32]: E8M0 scales
+
+    def struct(self):
+        e, n, kh = self.w_fp4.shape
+        return _lib.MxExpertsStruct(self.w_fp4.data_ptr(), self.w_scale.data_ptr(), e, n, 2 * kh)
+
+
+def mx_quantize(x, codes=None, scales=None):
+    """bf16 [rows, K] -> MXFP8 (E4M3 codes uint8 [rows, K], E8M0 scales uint8 [rows, K/32])."""
+    lib = _lib.load()
+    _check_tensors(x, codes, scales)
+    rows, k = x.shape
+    if codes is None:
+        codes = torch.empty(rows, k, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, k // 32, dtype=torch.uint8, device=x.device)
+    _check(lib.dsa_mx_quantize(x.data_ptr(), rows, k, codes.data_ptr(), scales.data_ptr(),
+                               _stream(x.device)))
+    return codes, scales
+
+
+def mxfp4_to_fp8(w, experts, ws_codes=None, ws_scales=None):
+    """The online conversion of experts (int32 [n]) into FP8 workspace slots:
+    (E4M3 codes uint8 [n, N, K], E8M0 scales uint8 [n, N, K/32])."""
+    lib = _lib.load()
+    _check_tensors(w.w_fp4, w.w_scale, experts, ws_codes, ws_scales)
+    e, n, kh = w.w_fp4.shape
+    m = experts.shape[0]
+    if ws_codes is None:
+        ws_codes = torch.empty(m, n, 2 * kh, dtype=torch.uint8, device=experts.device)
+    if ws_scales is None:
+        ws_scales = torch.empty(m, n, 2 * kh // 32, dtype=torch.uint8, device=experts.device)
+    ws = w.struct()
+    _check(lib.dsa_mxfp4_to_fp8(ctypes.byref(ws), experts.data_ptr(), m, ws_codes.data_ptr(),
+                                ws_scales.data_ptr(), _stream(experts.device)))
+    return ws_codes, ws_scales
+
+
+def moe_workspace_size(w, tokens, slots, mode):
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    ws = w.struct()
+    _check(lib.dsa_moe_workspace_size(ctypes.byref(ws), tokens, slots, mode, ctypes.byref(n)))
+    return n.value
+
+
+def moe_grouped_gemm(w, x_codes, x_scales, route, mode=None, out=None, workspace=None):
+    """out[t, j, :] = xq[t] . W[route[t, j]]^T (fp32 [T, slots, N]); rows of
+    slots routed to no expert (-1) are zero.  mode: MOE_FP4_DIRECT (default:
+    FP4 weights straight to the matrix cores) or MOE_FP8_WORKSPACE (the routed
+    experts unpacked to FP8 in the workspace first)."""
+    lib = _lib.load()
+    _check_tensors(w.w_fp4, w.w_scale, x_codes, x_scales, route, out)
+    mode = _lib.MOE_FP4_DIRECT if mode is None else mode
+    t, slots = route.shape
+    n = w.w_fp4.shape[1]
+    if out is None:
+        out = torch.empty(t, slots, n, dtype=torch.float32, device=route.device)
+    if workspace is None:
+        workspace = _workspace(moe_workspace_size(w, t, slots, mode), route.device)
+    ws = w.struct()
+    _check(lib.dsa_moe_grouped_gemm(ctypes.byref(ws), x_codes.data_ptr(), x_scales.data_ptr(), t,
+                                    route.data_ptr(), slots, mode, out.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(),
+                                    _stream(route.device)))
+    return out

@@ -18,8 +18,11 @@ EXPORTS = ["dsa_index_score", "dsa_topk_blocks", "dsa_sparse_attn_decode",
            "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_sparse_prefill_fused",
            "dsa_index_topk",
            "dsa_workspace_size", "dsa_check_inputs", "dsa_kv_write", "dsa_index_key_write",
+           "dsa_mx_quantize", "dsa_mxfp4_to_fp8", "dsa_moe_workspace_size", "dsa_moe_grouped_gemm",
            "dsa_status_str", "dsa_last_error", "dsa_abi_version"]
 CHECK_FLAGS = {1: "seq_len", 2: "table", 4: "q_seq", 8: "q_pos", 16: "block_list"}
+MOE_FP8_WORKSPACE = 0
+MOE_FP4_DIRECT = 1
 
 
 class PagedKVStruct(ctypes.Structure):
@@ -53,6 +56,16 @@ class QueriesStruct(ctypes.Structure):
     ]
 
 
+class MxExpertsStruct(ctypes.Structure):
+    _fields_ = [
+        ("w_fp4", ctypes.c_void_p),
+        ("w_scale", ctypes.c_void_p),
+        ("num_experts", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -66,7 +79,7 @@ def load():
                            "(there is no non-HIP fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
-    kvp, qp = P(PagedKVStruct), P(QueriesStruct)
+    kvp, qp, mxp = P(PagedKVStruct), P(QueriesStruct), P(MxExpertsStruct)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     sig = {
         "dsa_index_score": [kvp, qp, vp, vp],
@@ -80,6 +93,10 @@ def load():
         "dsa_check_inputs": [kvp, qp, vp, vp, i32, vp, vp],
         "dsa_kv_write": [kvp, i32, vp, vp, vp, vp, vp],
         "dsa_index_key_write": [kvp, i32, vp, vp, vp],
+        "dsa_mx_quantize": [vp, i32, i32, vp, vp, vp],
+        "dsa_mxfp4_to_fp8": [mxp, vp, i32, vp, vp, vp],
+        "dsa_moe_workspace_size": [mxp, i32, i32, i32, P(sz)],
+        "dsa_moe_grouped_gemm": [mxp, vp, vp, i32, vp, i32, i32, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

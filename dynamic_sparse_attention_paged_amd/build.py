@@ -20,7 +20,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["index_score.hip", "index_score_mfma.hip", "index_topk_fused.hip", "topk.hip", "attn.hip", "prefill_inv.hip", "check.hip", "write.hip", "dsa_api.cpp"]
+SOURCES = ["index_score.hip", "index_score_mfma.hip", "index_topk_fused.hip", "topk.hip", "attn.hip", "prefill_inv.hip", "moe.hip", "check.hip", "write.hip", "dsa_api.cpp"]
 
 
 def _compile(src, obj):

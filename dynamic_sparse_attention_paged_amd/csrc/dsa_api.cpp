@@ -499,6 +499,93 @@ dsa_status dsa_index_key_write(const dsa_paged_kv* kv, int32_t n_blocks, const i
                     "index_key_write launch");
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 expert weights
+// ---------------------------------------------------------------------------
+namespace {
+dsa_status check_experts(const dsa_mx_experts* w) {
+  if (!w) return fail(DSA_ERR_NULL, "experts must not be NULL");
+  if (!w->w_fp4 || !w->w_scale) return fail(DSA_ERR_NULL, "w_fp4/w_scale NULL");
+  if (w->num_experts < 1 || w->n < 1 || w->k < 128)
+    return fail(DSA_ERR_SHAPE, "num_experts, n >= 1 and k >= 128 required");
+  if (w->k % 128) return fail(DSA_ERR_UNSUPPORTED, "k %d: a multiple of 128 required", w->k);
+  if ((long long)w->num_experts * w->n * (w->k / 2) > (1LL << 46))
+    return fail(DSA_ERR_UNSUPPORTED, "weights too large");
+  if (!aligned(w->w_fp4, 16)) return fail(DSA_ERR_ALIGN, "w_fp4 needs 16 B alignment");
+  return DSA_OK;
+}
+dsa::MxExperts mx_view(const dsa_mx_experts* w) {
+  dsa::MxExperts m;
+  m.fp4 = w->w_fp4;
+  m.scale = w->w_scale;
+  m.num_experts = w->num_experts;
+  m.n = w->n;
+  m.k = w->k;
+  return m;
+}
+}  // namespace
+
+dsa_status dsa_mx_quantize(const void* x, int32_t rows, int32_t k, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream) {
+  if (rows < 0 || k < 0) return fail(DSA_ERR_SHAPE, "rows, k >= 0 required");
+  if (k % 32) return fail(DSA_ERR_UNSUPPORTED, "k %d: a multiple of 32 required", k);
+  if (rows == 0 || k == 0) return ok();
+  if (!x || !codes || !scales) return fail(DSA_ERR_NULL, "x/codes/scales NULL");
+  if (!aligned(x, 16) || !aligned(codes, 16)) return fail(DSA_ERR_ALIGN, "x/codes need 16 B alignment");
+  return hip_status(dsa::launch_mx_quant_act(static_cast<const uint16_t*>(x), rows, k, codes, scales,
+                                             stream),
+                    "mx_quantize launch");
+}
+
+dsa_status dsa_mxfp4_to_fp8(const dsa_mx_experts* w, const int32_t* experts, int32_t n_experts,
+                            uint8_t* ws_codes, uint8_t* ws_scales, hipStream_t stream) {
+  dsa_status st = check_experts(w);
+  if (st != DSA_OK) return st;
+  if (n_experts < 0) return fail(DSA_ERR_SHAPE, "n_experts < 0");
+  if (n_experts == 0) return ok();
+  if (!experts || !ws_codes || !ws_scales) return fail(DSA_ERR_NULL, "experts/ws_codes/ws_scales NULL");
+  if (!aligned(ws_codes, 16)) return fail(DSA_ERR_ALIGN, "ws_codes needs 16 B alignment");
+  return hip_status(dsa::launch_mxfp4_unpack(mx_view(w), experts, n_experts, ws_codes, ws_scales,
+                                             stream),
+                    "mxfp4_to_fp8 launch");
+}
+
+dsa_status dsa_moe_workspace_size(const dsa_mx_experts* w, int32_t tokens, int32_t slots,
+                                  int32_t mode, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_NULL, "bytes NULL");
+  *bytes = 0;
+  dsa_status st = check_experts(w);
+  if (st != DSA_OK) return st;
+  if (tokens < 0 || slots < 1) return fail(DSA_ERR_SHAPE, "tokens >= 0, slots >= 1 required");
+  if ((long long)tokens * slots > (1LL << 30)) return fail(DSA_ERR_UNSUPPORTED, "too many pairs");
+  if (mode != DSA_MOE_FP8_WORKSPACE && mode != DSA_MOE_FP4_DIRECT)
+    return fail(DSA_ERR_SHAPE, "unknown mode %d", mode);
+  *bytes = dsa::moe_layout(mx_view(w), tokens * slots, mode == DSA_MOE_FP8_WORKSPACE, 0).total;
+  return ok();
+}
+
+dsa_status dsa_moe_grouped_gemm(const dsa_mx_experts* w, const uint8_t* x_codes,
+                                const uint8_t* x_scales, int32_t tokens, const int32_t* route,
+                                int32_t slots, int32_t mode, float* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  dsa_status st = dsa_moe_workspace_size(w, tokens, slots, mode, &need);
+  if (st != DSA_OK) return st;
+  if (tokens == 0) return ok();
+  if (!x_codes || !x_scales || !route || !out) return fail(DSA_ERR_NULL, "x_codes/x_scales/route/out NULL");
+  if (!aligned(x_codes, 16) || !aligned(route, 4) || !aligned(out, 4))
+    return fail(DSA_ERR_ALIGN, "x_codes 16 B, route and out 4 B alignment required");
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
+  const dsa::MxExperts m = mx_view(w);
+  const bool fp8 = mode == DSA_MOE_FP8_WORKSPACE;
+  return hip_status(dsa::launch_moe_gemm(m, fp8, x_codes, x_scales, tokens, route, slots, out,
+                                         static_cast<char*>(workspace),
+                                         dsa::moe_layout(m, tokens * slots, fp8, 0), stream),
+                    "moe_grouped_gemm launch");
+}
+
 dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
                             const int32_t* block_idx, const int32_t* block_cnt, int32_t top_k,
                             uint32_t* flags, hipStream_t stream) {

@@ -130,4 +130,25 @@ hipError_t launch_prefill_inv(const KvView& kv, const QView& q, const int32_t* i
                               const int32_t* cnt, int top_k, float scale, float* out, float* lse,
                               char* ws, const InvLayout& layout, hipStream_t s);
 
+// MXFP4 expert weights (moe.hip): MXFP8 activations, the online MXFP4 -> FP8
+// conversion, and the grouped expert matmul on the scaled matrix cores.
+struct MxExperts {
+  const uint8_t* fp4;    // [E][N][K/2] E2M1 codes, element 2i in the low nibble
+  const uint8_t* scale;  // [E][N][K/32] E8M0
+  int num_experts, n, k;
+};
+struct MoeLayout {
+  int max_tiles, max_active;
+  size_t active, slot, n_active, ws_codes, ws_scales;                      // bytes
+  size_t count, cursor, list, tile_e, tile_p0, tile_p1, n_tiles, total;  // bytes
+};
+hipError_t launch_mx_quant_act(const uint16_t* x, int t, int k, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s);
+hipError_t launch_mxfp4_unpack(const MxExperts& w, const int32_t* experts, int n_active,
+                               uint8_t* ws_codes, uint8_t* ws_scales, hipStream_t s);
+MoeLayout moe_layout(const MxExperts& w, int pairs, bool fp8_workspace, size_t base);
+hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t* a_codes,
+                           const uint8_t* a_scales, int t, const int32_t* route, int slots,
+                           float* out, char* ws, const MoeLayout& layout, hipStream_t s);
+
 }  // namespace dsa

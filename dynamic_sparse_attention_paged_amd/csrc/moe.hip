@@ -1,0 +1,431 @@
+// MXFP4 expert weights: the online MXFP4 -> FP8 conversion into a reused
+// workspace, MXFP8 activations, and the grouped expert matmul.
+//
+// [P1] "Day-0 Adaptation for Massive LLMs...", section 5: expert weights are
+// MXFP4 (4-bit elements in fixed blocks with a block-level scale); the routed
+// experts' weights are unpacked to FP8 online into a shared workspace and the
+// expert matmuls run in FP8 with the block scales, the unpacked layout being
+// the matmul's input layout.  [P2] "Day-0 Adaptation for Trillion-Parameter
+// LLMs...", sections 3.1-3.2: conversion in registers / shared memory,
+// results fed straight to the matrix units, one global FP8 workspace reused
+// across layers.  Formats: the OCP MX specification v1.0 (E2M1 elements, E8M0
+// scales, blocks of 32).
+//
+// gfx950 runs the scaled matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4,
+// which applies one E8M0 scale per 32-element block of each operand in
+// hardware and takes FP8 or FP4 operands.  So the matmul here consumes the
+// block scales as they are, from either the FP8 workspace (the pages' path) or
+// the MXFP4 weights directly (no workspace: a quarter of the weight bytes of
+// unpacking and re-reading).  Operand layout of the 16x16x128 instruction, for
+// lane (r, kg), r = lane % 16, kg = lane / 16, over a 128-wide K step:
+//   FP8: K [16 kg, 16 kg + 16) and [64 + 16 kg, 64 + 16 kg + 16) (32 bytes);
+//   FP4: K [32 kg, 32 kg + 32) (16 bytes, element 2i in the low nibble);
+//   the lane's scale operand is the E8M0 scale of block kg, K [32 kg, 32 kg + 32);
+//   D[4 kg + i][r] = element i of the lane's result (row: A row, column: B row).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) int v8i;
+typedef __attribute__((ext_vector_type(4))) int v4i;
+typedef __attribute__((ext_vector_type(4))) float v4f;
+
+constexpr int kMoeThreads = 256;
+constexpr int kMoeBM = 32;    // pairs per workgroup tile (two 16-row MFMA tiles)
+constexpr int kMoeBN = 256;   // output columns per workgroup (four waves x 64)
+constexpr int kScanThreads = 1024;
+
+// E4M3 codes of the 16 E2M1 values (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+// negatives): E4M3 value (1 + M/8) 2^(E - 7), so 0.5 = E 6, 1 = E 7, 1.5 = E 7
+// M 4, 2 = E 8, 3 = E 8 M 4, 4 = E 9, 6 = E 9 M 4; code 8 (-0) is 0x80.
+__constant__ uint8_t kE2m1ToE4m3[16] = {0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C,
+                                        0x80, 0xB0, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8, 0xCC};
+
+// One thread per 32-element block of one activation row: MXFP8 with E4M3
+// elements.  shared = floor(log2 max|x|) - 8 (clamped to [-127, 127]), scale
+// code shared + 127 (0 for a zero block), elements E4M3(x * 2^-shared)
+// clamped to +-448, round to nearest even (v_cvt_pk_fp8_f32).  x * 2^-shared
+// is exact (a power of two, ldexp), so the only rounding is the conversion.
+__global__ __launch_bounds__(kMoeThreads) void mx_quant_act(const uint16_t* __restrict__ x,
+                                                            long blocks, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  for (long b = (long)blockIdx.x * kMoeThreads + threadIdx.x; b < blocks;
+       b += (long)gridDim.x * kMoeThreads) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = src[q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
+        v[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int s = 0, shared = 0;
+    if (amax > 0.f) {
+      shared = min(max(__builtin_amdgcn_frexp_expf(amax) - 1 - 8, -127), 127);
+      s = shared + 127;
+    }
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float y0 = fminf(fmaxf(ldexpf(v[4 * i + 2 * h], -shared), -448.f), 448.f);
+        const float y1 = fminf(fmaxf(ldexpf(v[4 * i + 2 * h + 1], -shared), -448.f), 448.f);
+        const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
+        word |= pk << (16 * h);
+      }
+      out[i] = word;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    scales[b] = (uint8_t)s;
+  }
+}
+
+// The online conversion: active expert list[a] -> workspace slot a.  One
+// thread per 32-element block: 16 packed bytes in, 32 E4M3 codes out, and the
+// block's E8M0 scale copied.
+__global__ __launch_bounds__(kMoeThreads) void mxfp4_unpack(
+    const uint8_t* __restrict__ w_fp4, const uint8_t* __restrict__ w_scale, int n, int k,
+    const int32_t* __restrict__ experts, int n_active, const int32_t* __restrict__ n_active_dev,
+    uint8_t* __restrict__ ws_codes, uint8_t* __restrict__ ws_scales) {
+  const long per_expert = (long)n * (k / 32);
+  const long total = per_expert * (n_active_dev ? min(*n_active_dev, n_active) : n_active);
+  for (long b = (long)blockIdx.x * kMoeThreads + threadIdx.x; b < total;
+       b += (long)gridDim.x * kMoeThreads) {
+    const int a = (int)(b / per_expert);
+    const long off = b - (long)a * per_expert;  // block within the expert: row-major [n][k/32]
+    const long src_blk = (long)experts[a] * per_expert + off;
+    const uint4 p = *reinterpret_cast<const uint4*>(w_fp4 + src_blk * 16);
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t c = kE2m1ToE4m3[(w[i] >> (4 * j)) & 15u];
+        lo |= c << (8 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t c = kE2m1ToE4m3[(w[i] >> (16 + 4 * j)) & 15u];
+        hi |= c << (8 * j);
+      }
+      out[2 * i] = lo;
+      out[2 * i + 1] = hi;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(ws_codes + ((long)a * per_expert + off) * 32);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    ws_scales[(long)a * per_expert + off] = w_scale[src_blk];
+  }
+}
+
+__global__ __launch_bounds__(kMoeThreads) void moe_zero(int32_t* __restrict__ a, int n) {
+  for (int i = blockIdx.x * kMoeThreads + threadIdx.x; i < n; i += gridDim.x * kMoeThreads) a[i] = 0;
+}
+
+// One thread per (token, slot) pair: count the pairs of every expert
+// (kScatter = false), or place each pair into its expert's list (true).
+template <bool kScatter>
+__global__ __launch_bounds__(kMoeThreads) void moe_pairs(const int32_t* __restrict__ route,
+                                                         int pairs, int num_experts,
+                                                         int32_t* __restrict__ count_or_cursor,
+                                                         int32_t* __restrict__ list) {
+  for (int p = blockIdx.x * kMoeThreads + threadIdx.x; p < pairs; p += gridDim.x * kMoeThreads) {
+    const int e = route[p];
+    if (e < 0 || e >= num_experts) continue;
+    const int at = atomicAdd(&count_or_cursor[e], 1);
+    if (kScatter) list[at] = p;
+  }
+}
+
+// One workgroup: offsets of every expert's pair list (cursor = offset), and the
+// row tiles of kMoeBM pairs: tile i covers list[tile_p0[i] .. tile_p1[i]) of
+// expert tile_e[i].
+// ... and the routed experts in ascending order: active[a] = e, slot[e] = a
+// (-1 for an expert no pair is routed to), *n_active.
+__global__ __launch_bounds__(kScanThreads) void moe_scan(const int32_t* __restrict__ count,
+                                                         int num_experts,
+                                                         int32_t* __restrict__ cursor,
+                                                         int32_t* __restrict__ tile_e,
+                                                         int32_t* __restrict__ tile_p0,
+                                                         int32_t* __restrict__ tile_p1,
+                                                         int32_t* __restrict__ n_tiles,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ slot,
+                                                         int32_t* __restrict__ n_active) {
+  __shared__ int s_off[kScanThreads], s_til[kScanThreads], s_act[kScanThreads];
+  const int tid = threadIdx.x;
+  const int per = (num_experts + kScanThreads - 1) / kScanThreads;
+  const int beg = min(num_experts, tid * per), end = min(num_experts, beg + per);
+  int off = 0, til = 0, act = 0;
+  for (int e = beg; e < end; ++e) {
+    off += count[e];
+    til += (count[e] + kMoeBM - 1) / kMoeBM;
+    act += count[e] > 0;
+  }
+  s_off[tid] = off;
+  s_til[tid] = til;
+  s_act[tid] = act;
+  __syncthreads();
+  // inclusive prefix over threads (Hillis-Steele in LDS)
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    const int a = tid >= d ? s_off[tid - d] : 0, b = tid >= d ? s_til[tid - d] : 0,
+              c = tid >= d ? s_act[tid - d] : 0;
+    __syncthreads();
+    s_off[tid] += a;
+    s_til[tid] += b;
+    s_act[tid] += c;
+    __syncthreads();
+  }
+  int o = s_off[tid] - off, t = s_til[tid] - til, q = s_act[tid] - act;
+  for (int e = beg; e < end; ++e) {
+    const int c = count[e];
+    cursor[e] = o;
+    for (int m = 0; m < c; m += kMoeBM) {
+      tile_e[t] = e;
+      tile_p0[t] = o + m;
+      tile_p1[t] = o + min(c, m + kMoeBM);
+      ++t;
+    }
+    if (c > 0) {
+      active[q] = e;
+      slot[e] = q++;
+    } else {
+      slot[e] = -1;
+    }
+    o += c;
+  }
+  if (tid == kScanThreads - 1) {
+    *n_tiles = s_til[tid];
+    *n_active = s_act[tid];
+  }
+}
+
+// One wave per (token, slot) pair not routed to any expert: its output row is zero.
+__global__ __launch_bounds__(kMoeThreads) void moe_clear_unrouted(const int32_t* __restrict__ route,
+                                                                  int pairs, int num_experts,
+                                                                  int n, float* __restrict__ out) {
+  const int p = blockIdx.x * (kMoeThreads / 64) + (threadIdx.x >> 6);
+  if (p >= pairs) return;
+  const int e = route[p];
+  if (e >= 0 && e < num_experts) return;
+  for (int c = threadIdx.x & 63; c < n; c += 64) out[(size_t)p * n + c] = 0.f;
+}
+
+__device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int kg) {
+  const v4i lo = *reinterpret_cast<const v4i*>(row + k0 + 16 * kg);
+  const v4i hi = *reinterpret_cast<const v4i*>(row + k0 + 64 + 16 * kg);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// grid (row-tile slots, ceil(N / 256)), block 256.  Workgroup (x, y): row tile
+// x (kMoeBM pairs of one expert; consecutive workgroups share an expert's B
+// columns), columns [256 y, 256 y + 256); wave w owns 64
+// of them as four 16-column MFMA tiles, over the two 16-row tiles.  B rows are
+// read straight from memory (each weight once per row tile), A rows gathered
+// per pair.  kFp4: B is the MXFP4 weights; otherwise the FP8 workspace (expert
+// e in slot b_slot[e]).
+template <bool kFp4>
+__global__ __launch_bounds__(kMoeThreads) void moe_gemm(
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+    const int32_t* __restrict__ b_slot, int n, int k, const uint8_t* __restrict__ a_codes,
+    const uint8_t* __restrict__ a_scales, int slots, const int32_t* __restrict__ list,
+    const int32_t* __restrict__ tile_e, const int32_t* __restrict__ tile_p0,
+    const int32_t* __restrict__ tile_p1, const int32_t* __restrict__ n_tiles,
+    float* __restrict__ out) {
+  const int tile = blockIdx.x;
+  if (tile >= *n_tiles) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kg = lane >> 4;
+  const int n0 = blockIdx.y * kMoeBN + wave * 64;
+  if (n0 >= n) return;  // no barriers in this kernel
+  const int e = tile_e[tile], p0 = tile_p0[tile], p1 = tile_p1[tile];
+  const int slot = kFp4 ? e : b_slot[e];
+  const int kb = k / 32;
+  // A rows of this lane: pair p0 + 16 rt + r (rows past the tile read the tile's first pair)
+  const uint8_t* arow[2];
+  const uint8_t* asc[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int p = p0 + 16 * rt + r;
+    const int t = list[p < p1 ? p : p0] / slots;
+    arow[rt] = a_codes + (size_t)t * k;
+    asc[rt] = a_scales + (size_t)t * kb;
+  }
+  const uint8_t* brow[4];
+  const uint8_t* bsc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int col = min(n0 + 16 * ct + r, n - 1);
+    const size_t row = (size_t)slot * n + col;
+    brow[ct] = b_codes + row * (kFp4 ? k / 2 : k);
+    bsc[ct] = b_scales + row * kb;
+  }
+  v4f acc[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int k0 = 0; k0 < k; k0 += 128) {
+    const int blk = k0 / 32 + kg;
+    v8i a[2];
+    int sa[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      a[rt] = load_fp8_operand(arow[rt], k0, kg);
+      sa[rt] = asc[rt][blk];
+    }
+    v8i b[4];
+    int sb[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (kFp4) {
+        const v4i q = *reinterpret_cast<const v4i*>(brow[ct] + k0 / 2 + 16 * kg);
+        b[ct] = v8i{q[0], q[1], q[2], q[3], 0, 0, 0, 0};
+      } else {
+        b[ct] = load_fp8_operand(brow[ct], k0, kg);
+      }
+      sb[ct] = bsc[ct][blk];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a[rt], b[ct], acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa[rt], 0, sb[ct]);
+  }
+  // D[4 kg + i][r]: pair row 16 rt + 4 kg + i, column n0 + 16 ct + r
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + 16 * rt + 4 * kg + i;
+      if (p >= p1) continue;
+      float* orow = out + (size_t)list[p] * n;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col = n0 + 16 * ct + r;
+        if (col < n) orow[col] = acc[rt][ct][i];
+      }
+    }
+}
+
+unsigned grid_for(long work, long cap) {
+  long g = (work + kMoeThreads - 1) / kMoeThreads;
+  return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant_act(const uint16_t* x, int t, int k, uint8_t* codes, uint8_t* scales,
+                               hipStream_t st) {
+  const long blocks = (long)t * (k / 32);
+  hipLaunchKernelGGL(mx_quant_act, dim3(grid_for(blocks, 65536)), dim3(kMoeThreads), 0, st, x,
+                     blocks, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_unpack(const MxExperts& w, const int32_t* experts, int n_active,
+                               uint8_t* ws_codes, uint8_t* ws_scales, hipStream_t st) {
+  const long work = (long)n_active * w.n * (w.k / 32);
+  hipLaunchKernelGGL(mxfp4_unpack, dim3(grid_for(work, 65536)), dim3(kMoeThreads), 0, st, w.fp4,
+                     w.scale, w.n, w.k, experts, n_active, nullptr, ws_codes, ws_scales);
+  return hipGetLastError();
+}
+
+MoeLayout moe_layout(const MxExperts& w, int pairs, bool fp8_workspace, size_t base) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int num_experts = w.num_experts;
+  MoeLayout L;
+  L.max_tiles = (pairs + kMoeBM - 1) / kMoeBM + num_experts;
+  L.max_active = num_experts < pairs ? num_experts : pairs;
+  size_t at = al(base);
+  L.active = at;
+  at = al(at + (size_t)num_experts * 4);
+  L.slot = at;
+  at = al(at + (size_t)num_experts * 4);
+  L.n_active = at;
+  at = al(at + 4);
+  // the FP8 workspace: the routed experts' weights, one slot each
+  L.ws_codes = at;
+  if (fp8_workspace) at = al(at + (size_t)L.max_active * w.n * w.k);
+  L.ws_scales = at;
+  if (fp8_workspace) at = al(at + (size_t)L.max_active * w.n * (w.k / 32));
+  L.count = at;
+  at = al(at + (size_t)num_experts * 4);
+  L.cursor = at;
+  at = al(at + (size_t)num_experts * 4);
+  L.list = at;
+  at = al(at + (size_t)pairs * 4);
+  L.tile_e = at;
+  at = al(at + (size_t)L.max_tiles * 4);
+  L.tile_p0 = at;
+  at = al(at + (size_t)L.max_tiles * 4);
+  L.tile_p1 = at;
+  at = al(at + (size_t)L.max_tiles * 4);
+  L.n_tiles = at;
+  at = al(at + 4);
+  L.total = at;
+  return L;
+}
+
+hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t* a_codes,
+                           const uint8_t* a_scales, int t, const int32_t* route, int slots,
+                           float* out, char* ws, const MoeLayout& L, hipStream_t st) {
+  const int pairs = t * slots;
+  int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+  int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
+  int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
+  int32_t* te = reinterpret_cast<int32_t*>(ws + L.tile_e);
+  int32_t* tp0 = reinterpret_cast<int32_t*>(ws + L.tile_p0);
+  int32_t* tp1 = reinterpret_cast<int32_t*>(ws + L.tile_p1);
+  int32_t* nt = reinterpret_cast<int32_t*>(ws + L.n_tiles);
+  hipLaunchKernelGGL(moe_zero, dim3(grid_for(w.num_experts, 64)), dim3(kMoeThreads), 0, st, count,
+                     w.num_experts);
+  hipLaunchKernelGGL(moe_pairs<false>, dim3(grid_for(pairs, 4096)), dim3(kMoeThreads), 0, st,
+                     route, pairs, w.num_experts, count, list);
+  int32_t* active = reinterpret_cast<int32_t*>(ws + L.active);
+  int32_t* slot = reinterpret_cast<int32_t*>(ws + L.slot);
+  int32_t* n_active = reinterpret_cast<int32_t*>(ws + L.n_active);
+  hipLaunchKernelGGL(moe_scan, dim3(1), dim3(kScanThreads), 0, st, count, w.num_experts, cursor,
+                     te, tp0, tp1, nt, active, slot, n_active);
+  hipLaunchKernelGGL(moe_pairs<true>, dim3(grid_for(pairs, 4096)), dim3(kMoeThreads), 0, st,
+                     route, pairs, w.num_experts, cursor, list);
+  hipLaunchKernelGGL(moe_clear_unrouted, dim3((pairs + 3) / 4), dim3(kMoeThreads), 0, st, route,
+                     pairs, w.num_experts, w.n, out);
+  const dim3 grid((unsigned)L.max_tiles, (unsigned)((w.n + kMoeBN - 1) / kMoeBN));
+  if (fp8_workspace) {
+    // the pages' path: the routed experts unpacked to FP8 into the workspace,
+    // then the matmul on the workspace
+    uint8_t* wc = reinterpret_cast<uint8_t*>(ws + L.ws_codes);
+    uint8_t* wsc = reinterpret_cast<uint8_t*>(ws + L.ws_scales);
+    const long work = (long)L.max_active * w.n * (w.k / 32);
+    hipLaunchKernelGGL(mxfp4_unpack, dim3(grid_for(work, 65536)), dim3(kMoeThreads), 0, st, w.fp4,
+                       w.scale, w.n, w.k, active, L.max_active, n_active, wc, wsc);
+    hipLaunchKernelGGL(moe_gemm<false>, grid, dim3(kMoeThreads), 0, st, wc, wsc, slot, w.n, w.k,
+                       a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+  } else {
+    hipLaunchKernelGGL(moe_gemm<true>, grid, dim3(kMoeThreads), 0, st, w.fp4, w.scale, slot, w.n,
+                       w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -295,6 +295,71 @@ dsa_status dsa_check_inputs(const dsa_paged_kv* kv, const dsa_queries* qs,
                             const int32_t* block_idx, const int32_t* block_cnt, int32_t top_k,
                             uint32_t* flags, hipStream_t stream);
 
+/*
+ * MXFP4 expert weights of one MoE layer ([P1] "Day-0 Adaptation for Massive
+ * LLMs...", section 5; [P5] "Day-0 Readiness...", "MXFP4 Expert Weights"):
+ * expert e's weight W_e [n, k] (outputs x inputs) in MXFP4 along k (OCP MX
+ * specification v1.0): E2M1 codes, two per byte, element 2i in bits 3-0;
+ * one E8M0 scale (value 2^(s - 127)) per 32 consecutive elements.
+ */
+typedef struct {
+  const uint8_t* w_fp4;    /* [num_experts, n, k / 2], 16 B aligned                               */
+  const uint8_t* w_scale;  /* [num_experts, n, k / 32]                                             */
+  int32_t num_experts;     /* >= 1                                                                 */
+  int32_t n;               /* >= 1                                                                 */
+  int32_t k;               /* a multiple of 128                                                    */
+} dsa_mx_experts;
+
+/*
+ * Activations to MXFP8 ([P1] section 5(2): the expert matmuls run in FP8):
+ * per 32-element block of each row of x (bf16 [rows, k], k a multiple of 32,
+ * 16 B aligned), shared = floor(log2 max|x|) - 8 clamped to [-127, 127],
+ * scales[block] = shared + 127 (0 for a block of zeros), codes = E4M3(x /
+ * 2^shared) (OCP E4M3, round to nearest even, clamped to +-448).  codes: uint8
+ * [rows, k], 16 B aligned; scales: uint8 [rows, k / 32].
+ */
+dsa_status dsa_mx_quantize(const void* x, int32_t rows, int32_t k, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream);
+
+/*
+ * The online conversion ([P1] section 5(2) and its schematic; [P2] "Day-0
+ * Adaptation for Trillion-Parameter LLMs...", section 3.1): the weights of
+ * experts[0 .. n_experts) (device int32, each in [0, num_experts)) unpacked
+ * into workspace slots 0 .. n_experts-1: ws_codes uint8 [n_experts, n, k]
+ * holds the E4M3 code of every E2M1 element (exact), ws_scales uint8
+ * [n_experts, n, k / 32] the E8M0 scales unchanged, so the block scales stay
+ * apart from the FP8 elements and nothing leaves the FP8 range ([P1] section
+ * 5(3)).  The layout is the grouped matmul's FP8 input layout.
+ */
+dsa_status dsa_mxfp4_to_fp8(const dsa_mx_experts* w, const int32_t* experts, int32_t n_experts,
+                            uint8_t* ws_codes, uint8_t* ws_scales, hipStream_t stream);
+
+/*
+ * The grouped expert matmul ([P1] section 5(2): grouped FP8 matmul with block
+ * scales; [P5] "MXFP4 Expert Weights": only the routed experts are
+ * converted).  For each (token t, slot j) with e = route[t, j] in [0,
+ * num_experts): out[t, j, :] = xq[t, :] . W_e^T, where xq is the MXFP8 row
+ * (x_codes uint8 [tokens, k], 16 B aligned; x_scales uint8 [tokens, k / 32],
+ * from dsa_mx_quantize) and W_e the MXFP4 weights; rows of other slots are
+ * zero.  out: fp32 [tokens, slots, n].  Computed on the scaled matrix cores
+ * (E8M0 block scales applied in hardware; the products are exact, the sums
+ * are the matrix unit's, within 2^-9 of sum |xq w| per output).  mode:
+ *   DSA_MOE_FP8_WORKSPACE  the pages' path: the routed experts are unpacked
+ *                          to FP8 into the workspace, then multiplied;
+ *   DSA_MOE_FP4_DIRECT     the FP4 weights feed the matrix cores directly
+ *                          (same values; no FP8 copy).
+ * workspace: at least dsa_moe_workspace_size bytes, 256 B aligned (with
+ * DSA_MOE_FP8_WORKSPACE it holds min(num_experts, tokens * slots) expert
+ * slots of n * k + n * k / 32 bytes).  route: int32 [tokens, slots].
+ */
+enum { DSA_MOE_FP8_WORKSPACE = 0, DSA_MOE_FP4_DIRECT = 1 };
+dsa_status dsa_moe_workspace_size(const dsa_mx_experts* w, int32_t tokens, int32_t slots,
+                                  int32_t mode, size_t* bytes);
+dsa_status dsa_moe_grouped_gemm(const dsa_mx_experts* w, const uint8_t* x_codes,
+                                const uint8_t* x_scales, int32_t tokens, const int32_t* route,
+                                int32_t slots, int32_t mode, float* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace sizes.  op: one of the DSA_OP_* values. */
 enum { DSA_OP_ATTN_DECODE = 1, DSA_OP_DECODE_FUSED = 2, DSA_OP_INDEX_TOPK = 3,
        DSA_OP_PREFILL_FUSED = 4 };

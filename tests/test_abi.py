@@ -22,7 +22,7 @@ def lib():
 
 def _declared():
     text = open(os.path.join(ROOT, "include", "dsa.h")).read()
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -188,3 +188,45 @@ def test_empty_batch_is_a_noop(lib):
 def test_status_strings(lib):
     for s in _lib.STATUS:
         assert lib.dsa_status_str(s)
+
+
+def _mx(**over):
+    f = dict(w_fp4=FAKE, w_scale=FAKE, num_experts=4, n=64, k=256)
+    f.update(over)
+    return _lib.MxExpertsStruct(**f)
+
+
+def test_moe_validation(lib):
+    E = {v: k for k, v in _lib.STATUS.items()}
+    n = ctypes.c_size_t(0)
+    w = _mx()
+    for mode in (_lib.MOE_FP8_WORKSPACE, _lib.MOE_FP4_DIRECT):
+        assert lib.dsa_moe_workspace_size(ctypes.byref(w), 8, 2, mode, ctypes.byref(n)) == 0
+    # the FP8 workspace holds min(experts, pairs) unpacked experts
+    fp8 = ctypes.c_size_t(0)
+    lib.dsa_moe_workspace_size(ctypes.byref(w), 8, 2, _lib.MOE_FP8_WORKSPACE, ctypes.byref(fp8))
+    assert fp8.value >= 4 * 64 * 256 + 4 * 64 * 8
+    assert lib.dsa_moe_workspace_size(ctypes.byref(_mx(k=200)), 8, 2, 1, ctypes.byref(n)) == \
+        E["DSA_ERR_UNSUPPORTED"]
+    assert lib.dsa_moe_workspace_size(ctypes.byref(_mx(n=0)), 8, 2, 1, ctypes.byref(n)) == \
+        E["DSA_ERR_SHAPE"]
+    assert lib.dsa_moe_workspace_size(ctypes.byref(_mx(w_fp4=None)), 8, 2, 1, ctypes.byref(n)) == \
+        E["DSA_ERR_NULL"]
+    assert lib.dsa_moe_workspace_size(ctypes.byref(_mx(w_fp4=FAKE + 8)), 8, 2, 1,
+                                      ctypes.byref(n)) == E["DSA_ERR_ALIGN"]
+    assert lib.dsa_moe_workspace_size(ctypes.byref(w), 8, 2, 7, ctypes.byref(n)) == E["DSA_ERR_SHAPE"]
+    lib.dsa_moe_workspace_size(ctypes.byref(w), 8, 2, 1, ctypes.byref(n))
+
+    def gemm(ws=FAKE, nbytes=n.value, out=FAKE, route=FAKE, tokens=8, mode=1):
+        return lib.dsa_moe_grouped_gemm(ctypes.byref(w), FAKE, FAKE, tokens, route, 2, mode, out,
+                                        ws, nbytes, None)
+    assert gemm(nbytes=n.value - 1) == E["DSA_ERR_WORKSPACE"]
+    assert gemm(ws=FAKE + 64) == E["DSA_ERR_ALIGN"]
+    assert gemm(out=None) == E["DSA_ERR_NULL"]
+    assert gemm(tokens=0) == 0
+    assert lib.dsa_mx_quantize(FAKE, 4, 48, FAKE, FAKE, None) == E["DSA_ERR_UNSUPPORTED"]
+    assert lib.dsa_mx_quantize(FAKE + 8, 4, 64, FAKE, FAKE, None) == E["DSA_ERR_ALIGN"]
+    assert lib.dsa_mx_quantize(None, 0, 64, None, None, None) == 0
+    assert lib.dsa_mxfp4_to_fp8(ctypes.byref(w), None, 2, FAKE, FAKE, None) == E["DSA_ERR_NULL"]
+    assert lib.dsa_mxfp4_to_fp8(ctypes.byref(w), FAKE, 0, None, None, None) == 0
+
