@@ -266,6 +266,61 @@ def block_size_extra(steps):
     return res
 
 
+def moe_extra(steps):
+    """MXFP4 expert layer (synthetic weights and routing): 64 experts with
+    W_e [4096 x 7168] in MXFP4, each token routed to 8 distinct experts.  A
+    decode batch (256 tokens: 2048 pairs, ~32 per expert) is bound by reading
+    the weights; a prefill batch (4096 tokens) by the matrix cores.  Both modes
+    of the grouped matmul: FP4 weights straight to the scaled matrix cores, and
+    the pages' online unpack to an FP8 workspace followed by the FP8 matmul."""
+    import torch
+    import dynamic_sparse_attention_paged_amd as dsa
+    from dynamic_sparse_attention_paged_amd import _lib
+    e_n, n, k, top = 64, 4096, 7168, 8
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7001)
+    w_fp4 = torch.randint(0, 256, (e_n, n, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+    w_scale = torch.randint(118, 131, (e_n, n, k // 32), dtype=torch.uint8, device="cuda",
+                            generator=g)
+    w = dsa.MxExperts(w_fp4, w_scale)
+    res = {}
+    for label, t in (("decode_256_tokens", 256), ("prefill_4096_tokens", 4096)):
+        x = torch.randn(t, k, device="cuda", generator=g).to(torch.bfloat16)
+        route = torch.rand(t, e_n, device="cuda", generator=g).argsort(dim=1)[:, :top]
+        route = route.to(torch.int32).contiguous()
+        xc, xs = dsa.mx_quantize(x)
+        out = torch.empty(t, top, n, dtype=torch.float32, device="cuda")
+        active = int(torch.unique(route).numel())
+        pairs = t * top
+        flops = 2.0 * pairs * n * k
+        w_bytes = active * (n * k // 2 + n * k // 32)
+        io_bytes = pairs * n * 4 + t * (k + k // 32)
+        row = dict(tokens=t, pairs=pairs, active_experts=active)
+        for mode, name in ((_lib.MOE_FP4_DIRECT, "fp4_direct"), (_lib.MOE_FP8_WORKSPACE,
+                                                                 "fp8_workspace")):
+            ws = dsa._workspace(dsa.moe_workspace_size(w, t, top, mode), x.device)
+
+            def step(i):
+                dsa.moe_grouped_gemm(w, xc, xs, route, mode=mode, out=out, workspace=ws)
+            ms = event_time_ms(step, steps, 2)
+            row[name] = dict(ms=round(ms, 4), tflops=round(flops / (ms * 1e-3) / 1e12, 1),
+                             weight_gbps=round(w_bytes / (ms * 1e-3) / 1e9, 1),
+                             frac_of_hbm_mxfp4_bytes=round((w_bytes + io_bytes) / (ms * 1e-3)
+                                                           / 1e9 / HBM_PEAK_GBPS, 4),
+                             workspace_gb=round(ws.numel() / 1e9, 3))
+            del ws
+        q_ms = event_time_ms(lambda i: dsa.mx_quantize(x, codes=xc, scales=xs), steps, 2)
+        row["mx_quantize_ms"] = round(q_ms, 4)
+        res[label] = row
+        del x, out, xc, xs
+    res["note"] = ("weight bytes = MXFP4 codes + scales of the routed experts; tflops counts "
+                   "2 * pairs * N * K; fp8 frac_of_fp8_mfma_peak for the prefill batch: "
+                   "tflops / 5000")
+    del w, w_fp4, w_scale
+    torch.cuda.empty_cache()
+    return res
+
+
 def write_path_extra(steps):
     """The paged write path at the chunked-prefill shape: one chunk of 8192
     tokens written into a 2048-block pool (HBM-bound copy through the block
@@ -361,7 +416,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--extra", choices=["tiny_decode", "million_decode", "ragged_decode",
-                                        "chunked_prefill", "write_path", "block_sizes"],
+                                        "chunked_prefill", "write_path", "block_sizes", "moe"],
                     help="run only this secondary workload (for profiling) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -382,6 +437,8 @@ def main():
             res = write_path_extra(args.steps)
         elif args.extra == "block_sizes":
             res = block_size_extra(args.steps)
+        elif args.extra == "moe":
+            res = moe_extra(args.steps)
         else:
             fn = getattr(workload, args.extra)
             res = decode_extra(fn(), args.steps, 4 if args.extra != "tiny_decode" else 8)
@@ -470,6 +527,8 @@ def main():
         log("extra: write path")
         extras["write_path"] = write_path_extra(20)
         extras["block_sizes"] = block_size_extra(20)
+        log("extra: MXFP4 expert layer")
+        extras["moe_mxfp4"] = moe_extra(10)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:

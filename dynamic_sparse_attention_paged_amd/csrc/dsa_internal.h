@@ -138,6 +138,7 @@ struct MxExperts {
   int num_experts, n, k;
 };
 struct MoeLayout {
+  int bm;  // pairs per row tile: 32, or 128 when the experts average many pairs
   int max_tiles, max_active;
   size_t active, slot, n_active, ws_codes, ws_scales;                      // bytes
   size_t count, cursor, list, tile_e, tile_p0, tile_p1, n_tiles, total;  // bytes

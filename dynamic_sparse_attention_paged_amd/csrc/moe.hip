@@ -35,7 +35,8 @@ typedef __attribute__((ext_vector_type(4))) int v4i;
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
 constexpr int kMoeThreads = 256;
-constexpr int kMoeBM = 32;    // pairs per workgroup tile (two 16-row MFMA tiles)
+constexpr int kMoeBMSmall = 32;   // pairs per row tile when experts get few pairs (decode)
+constexpr int kMoeBMLarge = 128;  // ... and when they get many (prefill): fewer weight re-reads
 constexpr int kMoeBN = 256;   // output columns per workgroup (four waves x 64)
 constexpr int kScanThreads = 1024;
 
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_pairs(const int32_t* __restri
 }
 
 // One workgroup: offsets of every expert's pair list (cursor = offset), and the
-// row tiles of kMoeBM pairs: tile i covers list[tile_p0[i] .. tile_p1[i]) of
+// row tiles of bm pairs: tile i covers list[tile_p0[i] .. tile_p1[i]) of
 // expert tile_e[i].
 // ... and the routed experts in ascending order: active[a] = e, slot[e] = a
 // (-1 for an expert no pair is routed to), *n_active.
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan(const int32_t* __restri
                                                          int32_t* __restrict__ n_tiles,
                                                          int32_t* __restrict__ active,
                                                          int32_t* __restrict__ slot,
-                                                         int32_t* __restrict__ n_active) {
+                                                         int32_t* __restrict__ n_active, int bm) {
   __shared__ int s_off[kScanThreads], s_til[kScanThreads], s_act[kScanThreads];
   const int tid = threadIdx.x;
   const int per = (num_experts + kScanThreads - 1) / kScanThreads;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan(const int32_t* __restri
   int off = 0, til = 0, act = 0;
   for (int e = beg; e < end; ++e) {
     off += count[e];
-    til += (count[e] + kMoeBM - 1) / kMoeBM;
+    til += (count[e] + bm - 1) / bm;
     act += count[e] > 0;
   }
   s_off[tid] = off;
@@ -197,10 +198,10 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan(const int32_t* __restri
   for (int e = beg; e < end; ++e) {
     const int c = count[e];
     cursor[e] = o;
-    for (int m = 0; m < c; m += kMoeBM) {
+    for (int m = 0; m < c; m += bm) {
       tile_e[t] = e;
       tile_p0[t] = o + m;
-      tile_p1[t] = o + min(c, m + kMoeBM);
+      tile_p1[t] = o + min(c, m + bm);
       ++t;
     }
     if (c > 0) {
@@ -234,14 +235,17 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+constexpr int kAPitch = 144;  // LDS bytes per A row: 128 + 16, so 16 rows hit distinct banks
+
 // grid (row-tile slots, ceil(N / 256)), block 256.  Workgroup (x, y): row tile
-// x (kMoeBM pairs of one expert; consecutive workgroups share an expert's B
-// columns), columns [256 y, 256 y + 256); wave w owns 64
-// of them as four 16-column MFMA tiles, over the two 16-row tiles.  B rows are
-// read straight from memory (each weight once per row tile), A rows gathered
-// per pair.  kFp4: B is the MXFP4 weights; otherwise the FP8 workspace (expert
-// e in slot b_slot[e]).
-template <bool kFp4>
+// x (16 RT pairs of one expert; consecutive workgroups share an expert's B
+// columns), columns [256 y, 256 y + 256); wave w owns 64 of them as four
+// 16-column MFMA tiles, over the RT 16-row tiles.  Per 128-wide K step the
+// workgroup stages the tile's A rows (gathered per pair) once in LDS (double
+// buffered), each wave reads its B rows straight from memory one step ahead,
+// and runs RT x 4 scaled MFMAs.  kFp4: B is the MXFP4 weights; otherwise the
+// FP8 workspace (expert e in slot b_slot[e]).
+template <bool kFp4, int RT>
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
     const int32_t* __restrict__ b_slot, int n, int k, const uint8_t* __restrict__ a_codes,
@@ -249,24 +253,31 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
     const int32_t* __restrict__ tile_e, const int32_t* __restrict__ tile_p0,
     const int32_t* __restrict__ tile_p1, const int32_t* __restrict__ n_tiles,
     float* __restrict__ out) {
+  constexpr int kRows = 16 * RT;
+  constexpr int kPasses = kRows * 8 / kMoeThreads;  // 16 B chunks: 8 per row and K step
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kRows * kAPitch];
+  __shared__ uint8_t s_lds[2][kRows * 4];
   const int tile = blockIdx.x;
-  if (tile >= *n_tiles) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (tile >= *n_tiles) return;  // the whole workgroup
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, kg = lane >> 4;
   const int n0 = blockIdx.y * kMoeBN + wave * 64;
-  if (n0 >= n) return;  // no barriers in this kernel
+  const bool wave_on = n0 < n;  // waves past N still stage A (barriers below)
   const int e = tile_e[tile], p0 = tile_p0[tile], p1 = tile_p1[tile];
   const int slot = kFp4 ? e : b_slot[e];
   const int kb = k / 32;
-  // A rows of this lane: pair p0 + 16 rt + r (rows past the tile read the tile's first pair)
-  const uint8_t* arow[2];
-  const uint8_t* asc[2];
+  // staging: thread tid copies chunk tid % 8 of rows tid / 8 + 32 q (q < kPasses);
+  // rows past the tile repeat the tile's first pair
+  const uint8_t* srow[kPasses];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int p = p0 + 16 * rt + r;
-    const int t = list[p < p1 ? p : p0] / slots;
-    arow[rt] = a_codes + (size_t)t * k;
-    asc[rt] = a_scales + (size_t)t * kb;
+  for (int q = 0; q < kPasses; ++q) {
+    const int p = p0 + tid / 8 + 32 * q;
+    srow[q] = a_codes + (size_t)(list[p < p1 ? p : p0] / slots) * k;
+  }
+  const uint8_t* sscale = nullptr;  // scale staging: thread tid < kRows * 4 / 4 copies one row's 4
+  if (tid < kRows) {
+    const int p = p0 + tid;
+    sscale = a_scales + (size_t)(list[p < p1 ? p : p0] / slots) * kb;
   }
   const uint8_t* brow[4];
   const uint8_t* bsc[4];
@@ -277,23 +288,19 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
     brow[ct] = b_codes + row * (kFp4 ? k / 2 : k);
     bsc[ct] = b_scales + row * kb;
   }
-  v4f acc[2][4];
+  auto load_a = [&](int k0, v4i (&st)[kPasses], uint32_t& sc) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int q = 0; q < kPasses; ++q)
+      st[q] = *reinterpret_cast<const v4i*>(srow[q] + k0 + 16 * (tid & 7));
+    if (tid < kRows) sc = *reinterpret_cast<const uint32_t*>(sscale + k0 / 32);
+  };
+  auto store_a = [&](int buf, const v4i (&st)[kPasses], uint32_t sc) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k0 = 0; k0 < k; k0 += 128) {
-    const int blk = k0 / 32 + kg;
-    v8i a[2];
-    int sa[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      a[rt] = load_fp8_operand(arow[rt], k0, kg);
-      sa[rt] = asc[rt][blk];
-    }
-    v8i b[4];
-    int sb[4];
+    for (int q = 0; q < kPasses; ++q)
+      *reinterpret_cast<v4i*>(&a_lds[buf][(tid / 8 + 32 * q) * kAPitch + 16 * (tid & 7)]) = st[q];
+    if (tid < kRows) *reinterpret_cast<uint32_t*>(&s_lds[buf][tid * 4]) = sc;
+  };
+  auto load_b = [&](int k0, v8i (&b)[4], int (&sb)[4]) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (kFp4) {
@@ -302,18 +309,61 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
       } else {
         b[ct] = load_fp8_operand(brow[ct], k0, kg);
       }
-      sb[ct] = bsc[ct][blk];
+      sb[ct] = bsc[ct][k0 / 32 + kg];
     }
+  };
+  v4f acc[RT][4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a[rt], b[ct], acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa[rt], 0, sb[ct]);
+    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4i st[kPasses];
+  uint32_t sc = 0;
+  load_a(0, st, sc);
+  store_a(0, st, sc);
+  v8i b[4];
+  int sb[4];
+  if (wave_on) load_b(0, b, sb);
+  __syncthreads();
+  const int steps = k / 128;
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < steps;
+    v8i bn[4];
+    int sbn[4];
+    if (more) {
+      load_a(128 * (s + 1), st, sc);
+      if (wave_on) load_b(128 * (s + 1), bn, sbn);
+    }
+    if (wave_on) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const uint8_t* ar = &a_lds[buf][(16 * rt + r) * kAPitch];
+        const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * kg);
+        const v4i hi = *reinterpret_cast<const v4i*>(ar + 64 + 16 * kg);
+        const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int sa = s_lds[buf][(16 * rt + r) * 4 + kg];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a, b[ct], acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sb[ct]);
+      }
+    }
+    if (more) {
+      store_a(buf ^ 1, st, sc);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        b[ct] = bn[ct];
+        sb[ct] = sbn[ct];
+      }
+    }
+    __syncthreads();
   }
+  if (!wave_on) return;
   // D[4 kg + i][r]: pair row 16 rt + 4 kg + i, column n0 + 16 ct + r
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = p0 + 16 * rt + 4 * kg + i;
@@ -354,7 +404,9 @@ MoeLayout moe_layout(const MxExperts& w, int pairs, bool fp8_workspace, size_t b
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int num_experts = w.num_experts;
   MoeLayout L;
-  L.max_tiles = (pairs + kMoeBM - 1) / kMoeBM + num_experts;
+  // tall row tiles once the experts average three 32-pair tiles or more
+  L.bm = (long)pairs >= 3L * kMoeBMSmall * num_experts ? kMoeBMLarge : kMoeBMSmall;
+  L.max_tiles = (pairs + L.bm - 1) / L.bm + num_experts;
   L.max_active = num_experts < pairs ? num_experts : pairs;
   size_t at = al(base);
   L.active = at;
@@ -405,7 +457,7 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
   int32_t* slot = reinterpret_cast<int32_t*>(ws + L.slot);
   int32_t* n_active = reinterpret_cast<int32_t*>(ws + L.n_active);
   hipLaunchKernelGGL(moe_scan, dim3(1), dim3(kScanThreads), 0, st, count, w.num_experts, cursor,
-                     te, tp0, tp1, nt, active, slot, n_active);
+                     te, tp0, tp1, nt, active, slot, n_active, L.bm);
   hipLaunchKernelGGL(moe_pairs<true>, dim3(grid_for(pairs, 4096)), dim3(kMoeThreads), 0, st,
                      route, pairs, w.num_experts, cursor, list);
   hipLaunchKernelGGL(moe_clear_unrouted, dim3((pairs + 3) / 4), dim3(kMoeThreads), 0, st, route,
@@ -419,11 +471,19 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
     const long work = (long)L.max_active * w.n * (w.k / 32);
     hipLaunchKernelGGL(mxfp4_unpack, dim3(grid_for(work, 65536)), dim3(kMoeThreads), 0, st, w.fp4,
                        w.scale, w.n, w.k, active, L.max_active, n_active, wc, wsc);
-    hipLaunchKernelGGL(moe_gemm<false>, grid, dim3(kMoeThreads), 0, st, wc, wsc, slot, w.n, w.k,
-                       a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+    if (L.bm == kMoeBMLarge)
+      hipLaunchKernelGGL((moe_gemm<false, 8>), grid, dim3(kMoeThreads), 0, st, wc, wsc, slot, w.n,
+                         w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+    else
+      hipLaunchKernelGGL((moe_gemm<false, 2>), grid, dim3(kMoeThreads), 0, st, wc, wsc, slot, w.n,
+                         w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
   } else {
-    hipLaunchKernelGGL(moe_gemm<true>, grid, dim3(kMoeThreads), 0, st, w.fp4, w.scale, slot, w.n,
-                       w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+    if (L.bm == kMoeBMLarge)
+      hipLaunchKernelGGL((moe_gemm<true, 8>), grid, dim3(kMoeThreads), 0, st, w.fp4, w.scale, slot,
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+    else
+      hipLaunchKernelGGL((moe_gemm<true, 2>), grid, dim3(kMoeThreads), 0, st, w.fp4, w.scale, slot,
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
   }
   return hipGetLastError();
 }

@@ -123,7 +123,8 @@ def _check_gemm(dsa, wp, ws, x, route, label):
 
 @pytest.mark.parametrize("e,n,k,t,slots", [(6, 320, 384, 37, 3),    # ragged: n, pairs
                                            (4, 256, 256, 64, 2),
-                                           (9, 64, 128, 5, 8)])
+                                           (9, 64, 128, 5, 8),
+                                           (4, 320, 512, 300, 2)])  # 150 pairs per expert: 128-row tiles
 def test_grouped_gemm_matches_oracle(dsa, e, n, k, t, slots):
     wp, ws, x, route = _gemm_case(40 + e, e, n, k, t, slots)
     _check_gemm(dsa, wp, ws, x, route, f"E{e} N{n} K{k} T{t} S{slots}")
