@@ -509,8 +509,9 @@ dsa_status check_experts(const dsa_mx_experts* w) {
   if (w->num_experts < 1 || w->n < 1 || w->k < 128)
     return fail(DSA_ERR_SHAPE, "num_experts, n >= 1 and k >= 128 required");
   if (w->k % 128) return fail(DSA_ERR_UNSUPPORTED, "k %d: a multiple of 128 required", w->k);
-  if ((long long)w->num_experts * w->n * (w->k / 2) > (1LL << 46))
-    return fail(DSA_ERR_UNSUPPORTED, "weights too large");
+  if ((long long)w->num_experts * w->n * (w->k / 2) > (1LL << 46) ||
+      (long long)w->n * w->k >= (1LL << 31))
+    return fail(DSA_ERR_UNSUPPORTED, "weights too large (n * k must stay below 2^31)");
   if (!aligned(w->w_fp4, 16)) return fail(DSA_ERR_ALIGN, "w_fp4 needs 16 B alignment");
   return DSA_OK;
 }

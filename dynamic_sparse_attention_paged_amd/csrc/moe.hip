@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -35,9 +37,9 @@ typedef __attribute__((ext_vector_type(4))) int v4i;
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
 constexpr int kMoeThreads = 256;
-constexpr int kMoeBMSmall = 32;   // pairs per row tile when experts get few pairs (decode)
+constexpr int kMoeBMSmall = 64;   // pairs per row tile when experts get few pairs (decode)
 constexpr int kMoeBMLarge = 128;  // ... and when they get many (prefill): fewer weight re-reads
-constexpr int kMoeBN = 256;   // output columns per workgroup (four waves x 64)
+// output columns per workgroup: four waves x 16 CT (CT column tiles per wave)
 constexpr int kScanThreads = 1024;
 
 // E4M3 codes of the 16 E2M1 values (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
@@ -237,15 +239,15 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
 
 constexpr int kAPitch = 144;  // LDS bytes per A row: 128 + 16, so 16 rows hit distinct banks
 
-// grid (row-tile slots, ceil(N / 256)), block 256.  Workgroup (x, y): row tile
-// x (16 RT pairs of one expert; consecutive workgroups share an expert's B
-// columns), columns [256 y, 256 y + 256); wave w owns 64 of them as four
+// grid (row-tile slots, ceil(N / (64 CT))), block 256.  Workgroup (x, y): row
+// tile x (16 RT pairs of one expert; consecutive workgroups share an expert's
+// B columns), columns [64 CT y, 64 CT (y + 1)); wave w owns 16 CT of them as CT
 // 16-column MFMA tiles, over the RT 16-row tiles.  Per 128-wide K step the
 // workgroup stages the tile's A rows (gathered per pair) once in LDS (double
 // buffered), each wave reads its B rows straight from memory one step ahead,
-// and runs RT x 4 scaled MFMAs.  kFp4: B is the MXFP4 weights; otherwise the
+// and runs RT x CT scaled MFMAs.  kFp4: B is the MXFP4 weights; otherwise the
 // FP8 workspace (expert e in slot b_slot[e]).
-template <bool kFp4, int RT>
+template <bool kFp4, int RT, int CT>
 __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
     const int32_t* __restrict__ b_slot, int n, int k, const uint8_t* __restrict__ a_codes,
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
   if (tile >= *n_tiles) return;  // the whole workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, kg = lane >> 4;
-  const int n0 = blockIdx.y * kMoeBN + wave * 64;
+  const int n0 = (blockIdx.y * 4 + wave) * 16 * CT;
   const bool wave_on = n0 < n;  // waves past N still stage A (barriers below)
   const int e = tile_e[tile], p0 = tile_p0[tile], p1 = tile_p1[tile];
   const int slot = kFp4 ? e : b_slot[e];
@@ -279,14 +281,16 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
     const int p = p0 + tid;
     sscale = a_scales + (size_t)(list[p < p1 ? p : p0] / slots) * kb;
   }
-  const uint8_t* brow[4];
-  const uint8_t* bsc[4];
+  // B rows of this lane: one base per expert, 32-bit offsets within it (n k / 2 < 2^31)
+  const int rb = kFp4 ? k / 2 : k;
+  const uint8_t* bbase = b_codes + (size_t)slot * n * rb;
+  const uint8_t* sbase = b_scales + (size_t)slot * n * kb;
+  uint32_t boff[CT], soff[CT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
     const int col = min(n0 + 16 * ct + r, n - 1);
-    const size_t row = (size_t)slot * n + col;
-    brow[ct] = b_codes + row * (kFp4 ? k / 2 : k);
-    bsc[ct] = b_scales + row * kb;
+    boff[ct] = (uint32_t)col * rb;
+    soff[ct] = (uint32_t)col * kb;
   }
   auto load_a = [&](int k0, v4i (&st)[kPasses], uint32_t& sc) {
 #pragma unroll
@@ -300,38 +304,44 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
       *reinterpret_cast<v4i*>(&a_lds[buf][(tid / 8 + 32 * q) * kAPitch + 16 * (tid & 7)]) = st[q];
     if (tid < kRows) *reinterpret_cast<uint32_t*>(&s_lds[buf][tid * 4]) = sc;
   };
-  auto load_b = [&](int k0, v8i (&b)[4], int (&sb)[4]) {
+  // FP4 fragments are 16 bytes (the instruction's upper four registers are
+  // unused for FP4 and passed as zeros at the call)
+  using BFrag = typename std::conditional<kFp4, v4i, v8i>::type;
+  auto load_b = [&](int k0, BFrag (&b)[CT], int (&sb)[CT]) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (kFp4) {
-        const v4i q = *reinterpret_cast<const v4i*>(brow[ct] + k0 / 2 + 16 * kg);
-        b[ct] = v8i{q[0], q[1], q[2], q[3], 0, 0, 0, 0};
+    for (int ct = 0; ct < CT; ++ct) {
+      if constexpr (kFp4) {
+        b[ct] = *reinterpret_cast<const v4i*>(bbase + boff[ct] + k0 / 2 + 16 * kg);
       } else {
-        b[ct] = load_fp8_operand(brow[ct], k0, kg);
+        b[ct] = load_fp8_operand(bbase + boff[ct], k0, kg);
       }
-      sb[ct] = bsc[ct][k0 / 32 + kg];
+      sb[ct] = sbase[soff[ct] + k0 / 32 + kg];
     }
   };
-  v4f acc[RT][4];
+  auto operand = [](const BFrag& b) {
+    if constexpr (kFp4) return v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    else return b;
+  };
+  v4f acc[RT][CT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
   v4i st[kPasses];
   uint32_t sc = 0;
   load_a(0, st, sc);
   store_a(0, st, sc);
-  v8i b[4];
-  int sb[4];
+  BFrag b[CT];
+  int sb[CT];
   if (wave_on) load_b(0, b, sb);
   __syncthreads();
   const int steps = k / 128;
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < steps;
-    v8i bn[4];
-    int sbn[4];
+    BFrag bn[CT];
+    int sbn[CT];
     if (more) {
       load_a(128 * (s + 1), st, sc);
       if (wave_on) load_b(128 * (s + 1), bn, sbn);
@@ -345,15 +355,15 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
         const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const int sa = s_lds[buf][(16 * rt + r) * 4 + kg];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
           acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              a, b[ct], acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sb[ct]);
+              a, operand(b[ct]), acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sb[ct]);
       }
     }
     if (more) {
       store_a(buf ^ 1, st, sc);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         b[ct] = bn[ct];
         sb[ct] = sbn[ct];
       }
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm(
       if (p >= p1) continue;
       float* orow = out + (size_t)list[p] * n;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         const int col = n0 + 16 * ct + r;
         if (col < n) orow[col] = acc[rt][ct][i];
       }
@@ -404,8 +414,8 @@ MoeLayout moe_layout(const MxExperts& w, int pairs, bool fp8_workspace, size_t b
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int num_experts = w.num_experts;
   MoeLayout L;
-  // tall row tiles once the experts average three 32-pair tiles or more
-  L.bm = (long)pairs >= 3L * kMoeBMSmall * num_experts ? kMoeBMLarge : kMoeBMSmall;
+  // tall row tiles once the experts average 96 pairs or more
+  L.bm = (long)pairs >= 96L * num_experts ? kMoeBMLarge : kMoeBMSmall;
   L.max_tiles = (pairs + L.bm - 1) / L.bm + num_experts;
   L.max_active = num_experts < pairs ? num_experts : pairs;
   size_t at = al(base);
@@ -462,7 +472,13 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
                      route, pairs, w.num_experts, cursor, list);
   hipLaunchKernelGGL(moe_clear_unrouted, dim3((pairs + 3) / 4), dim3(kMoeThreads), 0, st, route,
                      pairs, w.num_experts, w.n, out);
-  const dim3 grid((unsigned)L.max_tiles, (unsigned)((w.n + kMoeBN - 1) / kMoeBN));
+  // tall tiles: 128 pairs x 256 columns (each weight read once per 128 pairs);
+  // short tiles: 64 pairs x 256 columns (a typical decode expert in one tile)
+  const bool tall = L.bm == kMoeBMLarge;
+  const int wg_cols = 256;
+  const dim3 grid((unsigned)L.max_tiles, (unsigned)((w.n + wg_cols - 1) / wg_cols));
+  const uint8_t* bc = w.fp4;
+  const uint8_t* bs = w.scale;
   if (fp8_workspace) {
     // the pages' path: the routed experts unpacked to FP8 into the workspace,
     // then the matmul on the workspace
@@ -471,18 +487,20 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
     const long work = (long)L.max_active * w.n * (w.k / 32);
     hipLaunchKernelGGL(mxfp4_unpack, dim3(grid_for(work, 65536)), dim3(kMoeThreads), 0, st, w.fp4,
                        w.scale, w.n, w.k, active, L.max_active, n_active, wc, wsc);
-    if (L.bm == kMoeBMLarge)
-      hipLaunchKernelGGL((moe_gemm<false, 8>), grid, dim3(kMoeThreads), 0, st, wc, wsc, slot, w.n,
-                         w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
-    else
-      hipLaunchKernelGGL((moe_gemm<false, 2>), grid, dim3(kMoeThreads), 0, st, wc, wsc, slot, w.n,
-                         w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
-  } else {
-    if (L.bm == kMoeBMLarge)
-      hipLaunchKernelGGL((moe_gemm<true, 8>), grid, dim3(kMoeThreads), 0, st, w.fp4, w.scale, slot,
+    bc = wc;
+    bs = wsc;
+    if (tall)
+      hipLaunchKernelGGL((moe_gemm<false, 8, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
     else
-      hipLaunchKernelGGL((moe_gemm<true, 2>), grid, dim3(kMoeThreads), 0, st, w.fp4, w.scale, slot,
+      hipLaunchKernelGGL((moe_gemm<false, 4, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+  } else {
+    if (tall)
+      hipLaunchKernelGGL((moe_gemm<true, 8, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+    else
+      hipLaunchKernelGGL((moe_gemm<true, 4, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
   }
   return hipGetLastError();

@@ -307,7 +307,7 @@ typedef struct {
   const uint8_t* w_scale;  /* [num_experts, n, k / 32]                                             */
   int32_t num_experts;     /* >= 1                                                                 */
   int32_t n;               /* >= 1                                                                 */
-  int32_t k;               /* a multiple of 128                                                    */
+  int32_t k;               /* a multiple of 128; n * k < 2^31                                      */
 } dsa_mx_experts;
 
 /*
