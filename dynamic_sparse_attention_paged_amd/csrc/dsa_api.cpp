@@ -574,8 +574,8 @@ dsa_status dsa_moe_grouped_gemm(const dsa_mx_experts* w, const uint8_t* x_codes,
   if (st != DSA_OK) return st;
   if (tokens == 0) return ok();
   if (!x_codes || !x_scales || !route || !out) return fail(DSA_ERR_NULL, "x_codes/x_scales/route/out NULL");
-  if (!aligned(x_codes, 16) || !aligned(route, 4) || !aligned(out, 4))
-    return fail(DSA_ERR_ALIGN, "x_codes 16 B, route and out 4 B alignment required");
+  if (!aligned(x_codes, 16) || !aligned(x_scales, 4) || !aligned(route, 4) || !aligned(out, 4))
+    return fail(DSA_ERR_ALIGN, "x_codes 16 B; x_scales, route and out 4 B alignment required");
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");

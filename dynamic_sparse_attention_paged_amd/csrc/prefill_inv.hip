@@ -343,6 +343,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// (query, pick) slots: nq * top_k * tiles per block <= 65535 * 4096 * 8 < 2^31,
+// so entry indices (and the sentinel's, entries_max) fit in int.
 InvLayout inv_layout(const KvView& kv, int nq, int hq, int top_k, size_t base) {
   InvLayout L;
   const int sub = kv.bs_shift - 6;

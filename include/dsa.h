@@ -205,7 +205,7 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
  * block_cnt_out (nullable, together) receive the selection.  workspace: at
  * least dsa_workspace_size(DSA_OP_PREFILL_FUSED) bytes, 256 B aligned; it
  * grows as Nq * top_k * (block_size / 64) * Hq * 520 B (the partial states:
- * 17.7 GB for 8192 queries, K 64, 64 query heads, 64-token blocks).
+ * 17.4 GB for 8192 queries, K 64, 64 query heads, 64-token blocks).
  */
 dsa_status dsa_sparse_prefill_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
                                     float softmax_scale, float* out, float* lse,
@@ -340,7 +340,7 @@ dsa_status dsa_mxfp4_to_fp8(const dsa_mx_experts* w, const int32_t* experts, int
  * converted).  For each (token t, slot j) with e = route[t, j] in [0,
  * num_experts): out[t, j, :] = xq[t, :] . W_e^T, where xq is the MXFP8 row
  * (x_codes uint8 [tokens, k], 16 B aligned; x_scales uint8 [tokens, k / 32],
- * from dsa_mx_quantize) and W_e the MXFP4 weights; rows of other slots are
+ * 4 B aligned, from dsa_mx_quantize) and W_e the MXFP4 weights; rows of other slots are
  * zero.  out: fp32 [tokens, slots, n].  Computed on the scaled matrix cores
  * (E8M0 block scales applied in hardware; the products are exact, the sums
  * are the matrix unit's, within 2^-9 of sum |xq w| per output).  mode:

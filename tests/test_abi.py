@@ -178,6 +178,7 @@ def test_prefill_fused_contract(lib):
     assert call(qs=_qs(q_seq=FAKE, q_pos=FAKE, num_queries=0)) == 0
 
 
+
 def test_empty_batch_is_a_noop(lib):
     # Nq == 0 returns DSA_OK without launching anything (no GPU needed)
     assert _score(lib, _kv(), _qs(num_queries=0)) == 0
@@ -221,6 +222,8 @@ def test_moe_validation(lib):
         return lib.dsa_moe_grouped_gemm(ctypes.byref(w), FAKE, FAKE, tokens, route, 2, mode, out,
                                         ws, nbytes, None)
     assert gemm(nbytes=n.value - 1) == E["DSA_ERR_WORKSPACE"]
+    assert lib.dsa_moe_grouped_gemm(ctypes.byref(w), FAKE, FAKE + 1, 8, FAKE, 2, 1, FAKE, FAKE,
+                                    n.value, None) == E["DSA_ERR_ALIGN"]   # x_scales 4 B
     assert gemm(ws=FAKE + 64) == E["DSA_ERR_ALIGN"]
     assert gemm(out=None) == E["DSA_ERR_NULL"]
     assert gemm(tokens=0) == 0
