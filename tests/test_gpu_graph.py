@@ -105,3 +105,70 @@ def test_fused_workspace_reused_across_shapes():
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int32), fresh[k][0].view(torch.int32)), (rnd, k)
             assert torch.equal(lse.view(torch.int32), fresh[k][1].view(torch.int32)), (rnd, k)
+
+
+def test_fused_prefill_graph_replays_match_eager():
+    """The block-inverted prefill (its CSR counters are cleared by a kernel,
+    not a memset) replays bit for bit, with eager calls on other queries
+    between the replays."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as dsa
+    w = workload.small_prefill(seed=2880, L=64 * 30 + 7, count=120, hq=16, hkv=2, hi=4, top_k=8)
+    kv, qs = parity.to_device(w)
+    _, qs2 = parity.to_device(workload.with_query_seed(w, 2881))
+    K, nq = w.top_k, w.num_queries
+    ws = dsa.make_workspace(dsa._lib.OP_PREFILL_FUSED, kv, qs, K)
+    out = torch.empty(nq, w.num_q_heads, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(nq, w.num_q_heads, dtype=torch.float32, device="cuda")
+    bi = torch.empty(nq, K, dtype=torch.int32, device="cuda")
+    bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+
+    def call(q):
+        dsa.prefill_fused(kv, q, K, w.softmax_scale, out=out, lse=lse, block_idx=bi,
+                          block_cnt=bc, workspace=ws)
+    call(qs)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, bi, bc)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(qs)
+    for rep in range(4):
+        call(qs2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((out, lse, bi, bc), ref):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+
+
+def test_moe_grouped_gemm_graph_replays_match_eager():
+    """The MXFP4 grouped matmul in both modes (pair grouping, expert slots and,
+    for the FP8 mode, the unpack, all inside the graph) replays bit for bit."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import numpy as np
+    import dynamic_sparse_attention_paged_amd as dsa
+    rng = np.random.default_rng(2890)
+    e, n, k, t, slots = 8, 256, 256, 40, 3
+    w = dsa.MxExperts(torch.from_numpy(rng.integers(0, 256, (e, n, k // 2), dtype=np.uint8)).cuda(),
+                      torch.from_numpy(rng.integers(118, 131, (e, n, k // 32), dtype=np.uint8)).cuda())
+    x = torch.randn(t, k, device="cuda").to(torch.bfloat16)
+    xc, xs = dsa.mx_quantize(x)
+    route = torch.from_numpy(rng.integers(-1, e, (t, slots)).astype(np.int32)).cuda()
+    route2 = torch.from_numpy(rng.integers(0, e, (t, slots)).astype(np.int32)).cuda()
+    for mode in (dsa._lib.MOE_FP4_DIRECT, dsa._lib.MOE_FP8_WORKSPACE):
+        ws = dsa._workspace(dsa.moe_workspace_size(w, t, slots, mode), route.device)
+        out = torch.empty(t, slots, n, dtype=torch.float32, device="cuda")
+        dsa.moe_grouped_gemm(w, xc, xs, route, mode=mode, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dsa.moe_grouped_gemm(w, xc, xs, route, mode=mode, out=out, workspace=ws)
+        for rep in range(4):
+            dsa.moe_grouped_gemm(w, xc, xs, route2, mode=mode, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), (mode, rep)
