@@ -45,8 +45,18 @@ constexpr int kScanThreads = 1024;
 // E4M3 codes of the 16 E2M1 values (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
 // negatives): E4M3 value (1 + M/8) 2^(E - 7), so 0.5 = E 6, 1 = E 7, 1.5 = E 7
 // M 4, 2 = E 8, 3 = E 8 M 4, 4 = E 9, 6 = E 9 M 4; code 8 (-0) is 0x80.
-__constant__ uint8_t kE2m1ToE4m3[16] = {0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C,
-                                        0x80, 0xB0, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8, 0xCC};
+// The magnitudes (codes 0-7) are a byte table held in two registers and
+// indexed with v_perm_b32 (four elements per instruction); the sign (code bit
+// 3) becomes E4M3 bit 7.
+constexpr uint32_t kMagLo = 0x3C383000u;  // E4M3 of E2M1 magnitudes 0, 0.5, 1, 1.5
+constexpr uint32_t kMagHi = 0x4C484440u;  // ... 2, 3, 4, 6
+
+// E4M3 codes (one per byte) of the four E2M1 codes in bits 15-0 of x
+__device__ __forceinline__ uint32_t e2m1x4_to_e4m3(uint32_t x) {
+  const uint32_t spread = (x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) | ((x & 0xF000u) << 12);
+  const uint32_t mag = __builtin_amdgcn_perm(kMagHi, kMagLo, spread & 0x07070707u);
+  return mag | ((spread & 0x08080808u) << 4);
+}
 
 // One thread per 32-element block of one activation row: MXFP8 with E4M3
 // elements.  shared = floor(log2 max|x|) - 8 (clamped to [-127, 127]), scale
@@ -117,19 +127,8 @@ __global__ __launch_bounds__(kMoeThreads) void mxfp4_unpack(
     uint32_t out[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t c = kE2m1ToE4m3[(w[i] >> (4 * j)) & 15u];
-        lo |= c << (8 * j);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t c = kE2m1ToE4m3[(w[i] >> (16 + 4 * j)) & 15u];
-        hi |= c << (8 * j);
-      }
-      out[2 * i] = lo;
-      out[2 * i + 1] = hi;
+      out[2 * i] = e2m1x4_to_e4m3(w[i] & 0xFFFFu);  // elements 8i .. 8i+3
+      out[2 * i + 1] = e2m1x4_to_e4m3(w[i] >> 16);  // elements 8i+4 .. 8i+7
     }
     uint4* dst = reinterpret_cast<uint4*>(ws_codes + ((long)a * per_expert + off) * 32);
     dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
