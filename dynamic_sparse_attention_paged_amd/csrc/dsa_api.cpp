@@ -561,7 +561,12 @@ dsa_status dsa_moe_workspace_size(const dsa_mx_experts* w, int32_t tokens, int32
   if ((long long)tokens * slots > (1LL << 30)) return fail(DSA_ERR_UNSUPPORTED, "too many pairs");
   if (mode != DSA_MOE_FP8_WORKSPACE && mode != DSA_MOE_FP4_DIRECT)
     return fail(DSA_ERR_SHAPE, "unknown mode %d", mode);
-  *bytes = dsa::moe_layout(mx_view(w), tokens * slots, mode == DSA_MOE_FP8_WORKSPACE, 0).total;
+  const dsa::MoeLayout L = dsa::moe_layout(mx_view(w), tokens * slots, mode == DSA_MOE_FP8_WORKSPACE, 0);
+  // one workgroup per (row tile, column block of 128 or more): the grid must stay
+  // below 2^24 workgroups
+  if ((long long)L.max_tiles * ((w->n + 127) / 128) >= (1LL << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "too many pairs x columns for one launch");
+  *bytes = L.total;
   return ok();
 }
 

@@ -41,6 +41,7 @@ constexpr int kMoeBMSmall = 64;   // pairs per row tile when experts get few pai
 constexpr int kMoeBMLarge = 128;  // ... and when they get many (prefill): fewer weight re-reads
 // output columns per workgroup: four waves x 16 CT (CT column tiles per wave)
 constexpr int kScanThreads = 1024;
+constexpr int kMoeGroupTiles = 4;  // row tiles whose column blocks run together in the matmul
 
 // E4M3 codes of the 16 E2M1 values (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
 // negatives): E4M3 value (1 + M/8) 2^(E - 7), so 0.5 = E 6, 1 = E 7, 1.5 = E 7
@@ -238,31 +239,47 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
 
 constexpr int kAPitch = 144;  // LDS bytes per A row: 128 + 16, so 16 rows hit distinct banks
 
-// grid (row-tile slots, ceil(N / (64 CT))), block 256.  Workgroup (x, y): row
-// tile x (16 RT pairs of one expert; consecutive workgroups share an expert's
-// B columns), columns [64 CT y, 64 CT (y + 1)); wave w owns 16 CT of them as CT
-// 16-column MFMA tiles, over the RT 16-row tiles.  Per 128-wide K step the
+// grid (row-tile slots x ncb column blocks), block 256.  A work item (row
+// tile, column block c) covers the tile's 16 RT pairs of one expert and columns
+// [64 CT c, 64 CT (c + 1)); wave w owns 16 CT of them as CT 16-column MFMA
+// tiles, over the RT 16-row tiles.  Items are ordered so that each XCD (the
+// hardware deals workgroups to its 8 XCDs in turn) takes one contiguous run of
+// them, and within a run the column blocks of kMoeGroupTiles consecutive row
+// tiles come together: tiles of one expert then read its weight columns, and
+// column blocks of one tile its A rows, through the same L2 at about the same
+// time (workgroups past the live items exit).  Per 128-wide K step the
 // workgroup stages the tile's A rows (gathered per pair) once in LDS (double
 // buffered), each wave reads its B rows straight from memory one step ahead,
 // and runs RT x CT scaled MFMAs.  kFp4: B is the MXFP4 weights; otherwise the
-// FP8 workspace (expert e in slot b_slot[e]).
+// FP8 workspace (expert e in slot b_slot[e]).  Two waves per SIMD (at most 256
+// registers a lane; every variant launched fits without spills): one wave per
+// SIMD leaves the matrix unit idle through every load and barrier.
 template <bool kFp4, int RT, int CT>
-__global__ __launch_bounds__(kMoeThreads) void moe_gemm(
+__global__ __launch_bounds__(kMoeThreads)
+__attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
     const int32_t* __restrict__ b_slot, int n, int k, const uint8_t* __restrict__ a_codes,
     const uint8_t* __restrict__ a_scales, int slots, const int32_t* __restrict__ list,
     const int32_t* __restrict__ tile_e, const int32_t* __restrict__ tile_p0,
-    const int32_t* __restrict__ tile_p1, const int32_t* __restrict__ n_tiles,
+    const int32_t* __restrict__ tile_p1, const int32_t* __restrict__ n_tiles, int ncb,
     float* __restrict__ out) {
   constexpr int kRows = 16 * RT;
   constexpr int kPasses = kRows * 8 / kMoeThreads;  // 16 B chunks: 8 per row and K step
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kRows * kAPitch];
   __shared__ uint8_t s_lds[2][kRows * 4];
-  const int tile = blockIdx.x;
-  if (tile >= *n_tiles) return;  // the whole workgroup
+  const int live_tiles = *n_tiles, live = live_tiles * ncb;
+  const int hw = blockIdx.x;
+  if (hw >= live) return;  // the whole workgroup
+  // XCD x = hw % 8 takes items [x q + min(x, rem), ...) in dispatch order
+  const int q = live >> 3, rem = live & 7, x = hw & 7;
+  const int item = x * q + min(x, rem) + (hw >> 3);
+  const int g0 = item / (kMoeGroupTiles * ncb) * kMoeGroupTiles;
+  const int gt = min(kMoeGroupTiles, live_tiles - g0);
+  const int within = item - g0 * ncb;
+  const int tile = g0 + within % gt, cblk = within / gt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, kg = lane >> 4;
-  const int n0 = (blockIdx.y * 4 + wave) * 16 * CT;
+  const int n0 = (cblk * 4 + wave) * 16 * CT;
   const bool wave_on = n0 < n;  // waves past N still stage A (barriers below)
   const int e = tile_e[tile], p0 = tile_p0[tile], p1 = tile_p1[tile];
   const int slot = kFp4 ? e : b_slot[e];
@@ -471,11 +488,13 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
                      route, pairs, w.num_experts, cursor, list);
   hipLaunchKernelGGL(moe_clear_unrouted, dim3((pairs + 3) / 4), dim3(kMoeThreads), 0, st, route,
                      pairs, w.num_experts, w.n, out);
-  // tall tiles: 128 pairs x 256 columns (each weight read once per 128 pairs);
+  // tall tiles: 128 pairs x 256 columns (each weight read once per 128 pairs),
+  // x 128 columns over the FP8 workspace (twice the B fragment registers);
   // short tiles: 64 pairs x 256 columns (a typical decode expert in one tile)
   const bool tall = L.bm == kMoeBMLarge;
-  const int wg_cols = 256;
-  const dim3 grid((unsigned)L.max_tiles, (unsigned)((w.n + wg_cols - 1) / wg_cols));
+  const int wg_cols = tall && fp8_workspace ? 128 : 256;
+  const int ncb = (w.n + wg_cols - 1) / wg_cols;
+  const dim3 grid((unsigned)((long)L.max_tiles * ncb));
   const uint8_t* bc = w.fp4;
   const uint8_t* bs = w.scale;
   if (fp8_workspace) {
@@ -489,18 +508,18 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
     bc = wc;
     bs = wsc;
     if (tall)
-      hipLaunchKernelGGL((moe_gemm<false, 8, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+      hipLaunchKernelGGL((moe_gemm<false, 8, 2>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else
       hipLaunchKernelGGL((moe_gemm<false, 4, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
   } else {
     if (tall)
       hipLaunchKernelGGL((moe_gemm<true, 8, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else
       hipLaunchKernelGGL((moe_gemm<true, 4, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, out);
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
   }
   return hipGetLastError();
 }
