@@ -23,6 +23,8 @@
 //   the lane's scale operand is the E8M0 scale of block kg, K [32 kg, 32 kg + 32);
 //   D[4 kg + i][r] = element i of the lane's result (row: A row, column: B row).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include <type_traits>
@@ -142,18 +144,55 @@ __global__ __launch_bounds__(kMoeThreads) void moe_zero(int32_t* __restrict__ a,
   for (int i = blockIdx.x * kMoeThreads + threadIdx.x; i < n; i += gridDim.x * kMoeThreads) a[i] = 0;
 }
 
-// One thread per (token, slot) pair: count the pairs of every expert
-// (kScatter = false), or place each pair into its expert's list (true).
+// Count the pairs of every expert (kScatter = false), or place each pair into
+// its expert's list (true).  Each workgroup takes chunks of kPairChunk pairs:
+// it counts them per expert in LDS (the LDS atomic also gives each pair its
+// rank within the chunk), then makes one global atomic per expert and chunk,
+// which reserves the chunk's run in the expert's list.  With more experts than
+// the LDS table holds, one global atomic per pair.
+constexpr int kPairsPerThread = 8;
+constexpr int kPairChunk = kPairsPerThread * kMoeThreads;
+constexpr int kLdsExperts = 2048;
 template <bool kScatter>
 __global__ __launch_bounds__(kMoeThreads) void moe_pairs(const int32_t* __restrict__ route,
                                                          int pairs, int num_experts,
                                                          int32_t* __restrict__ count_or_cursor,
                                                          int32_t* __restrict__ list) {
-  for (int p = blockIdx.x * kMoeThreads + threadIdx.x; p < pairs; p += gridDim.x * kMoeThreads) {
-    const int e = route[p];
-    if (e < 0 || e >= num_experts) continue;
-    const int at = atomicAdd(&count_or_cursor[e], 1);
-    if (kScatter) list[at] = p;
+  const int tid = threadIdx.x;
+  if (num_experts > kLdsExperts) {
+    for (int p = blockIdx.x * kMoeThreads + tid; p < pairs; p += gridDim.x * kMoeThreads) {
+      const int e = route[p];
+      if (e < 0 || e >= num_experts) continue;
+      const int at = atomicAdd(&count_or_cursor[e], 1);
+      if (kScatter) list[at] = p;
+    }
+    return;
+  }
+  __shared__ int hist[kLdsExperts];
+  for (int c0 = blockIdx.x * kPairChunk; c0 < pairs; c0 += gridDim.x * kPairChunk) {
+    for (int e = tid; e < num_experts; e += kMoeThreads) hist[e] = 0;
+    __syncthreads();
+    int ex[kPairsPerThread], rank[kPairsPerThread];
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      const int p = c0 + j * kMoeThreads + tid;
+      const int e = p < pairs ? route[p] : -1;
+      ex[j] = e >= 0 && e < num_experts ? e : -1;
+      rank[j] = ex[j] >= 0 ? atomicAdd(&hist[ex[j]], 1) : 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < num_experts; e += kMoeThreads) {
+      const int h = hist[e];
+      const int at = h ? atomicAdd(&count_or_cursor[e], h) : 0;
+      if (kScatter) hist[e] = at;  // the chunk's first slot in expert e's list
+    }
+    if (kScatter) {
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kPairsPerThread; ++j)
+        if (ex[j] >= 0) list[hist[ex[j]] + rank[j]] = c0 + j * kMoeThreads + tid;
+    }
+    __syncthreads();  // the table is cleared for the next chunk
   }
 }
 
@@ -351,6 +390,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   BFrag b[CT];
   int sb[CT];
   if (wave_on) load_b(0, b, sb);
+  // Drain the prologue's loads here: the loop body reads b only after copying
+  // it from the loads of the step before (which it waits for), and without this
+  // the compiler's wait at the loop head also covers the loads issued for the
+  // next step, which would stall every step on a full memory round trip.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int steps = k / 128;
   for (int s = 0; s < steps; ++s) {
@@ -477,15 +521,16 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
   int32_t* nt = reinterpret_cast<int32_t*>(ws + L.n_tiles);
   hipLaunchKernelGGL(moe_zero, dim3(grid_for(w.num_experts, 64)), dim3(kMoeThreads), 0, st, count,
                      w.num_experts);
-  hipLaunchKernelGGL(moe_pairs<false>, dim3(grid_for(pairs, 4096)), dim3(kMoeThreads), 0, st,
-                     route, pairs, w.num_experts, count, list);
+  const unsigned pair_grid = (unsigned)std::max(1, std::min(1024, (pairs + kPairChunk - 1) / kPairChunk));
+  hipLaunchKernelGGL(moe_pairs<false>, dim3(pair_grid), dim3(kMoeThreads), 0, st, route, pairs,
+                     w.num_experts, count, list);
   int32_t* active = reinterpret_cast<int32_t*>(ws + L.active);
   int32_t* slot = reinterpret_cast<int32_t*>(ws + L.slot);
   int32_t* n_active = reinterpret_cast<int32_t*>(ws + L.n_active);
   hipLaunchKernelGGL(moe_scan, dim3(1), dim3(kScanThreads), 0, st, count, w.num_experts, cursor,
                      te, tp0, tp1, nt, active, slot, n_active, L.bm);
-  hipLaunchKernelGGL(moe_pairs<true>, dim3(grid_for(pairs, 4096)), dim3(kMoeThreads), 0, st,
-                     route, pairs, w.num_experts, cursor, list);
+  hipLaunchKernelGGL(moe_pairs<true>, dim3(pair_grid), dim3(kMoeThreads), 0, st, route, pairs,
+                     w.num_experts, cursor, list);
   hipLaunchKernelGGL(moe_clear_unrouted, dim3((pairs + 3) / 4), dim3(kMoeThreads), 0, st, route,
                      pairs, w.num_experts, w.n, out);
   // tall tiles: 128 pairs x 256 columns (each weight read once per 128 pairs),

@@ -124,7 +124,9 @@ def _check_gemm(dsa, wp, ws, x, route, label):
 @pytest.mark.parametrize("e,n,k,t,slots", [(6, 320, 384, 37, 3),    # ragged: n, pairs
                                            (4, 256, 256, 64, 2),
                                            (9, 64, 128, 5, 8),
-                                           (4, 320, 512, 300, 2)])  # 150 pairs per expert: 128-row tiles
+                                           (4, 320, 512, 300, 2),   # 150 pairs per expert: 128-row tiles
+                                           (8, 64, 128, 1500, 3),   # pairs over several grouping chunks
+                                           (2100, 64, 128, 300, 2)])  # more experts than the LDS table
 def test_grouped_gemm_matches_oracle(dsa, e, n, k, t, slots):
     wp, ws, x, route = _gemm_case(40 + e, e, n, k, t, slots)
     _check_gemm(dsa, wp, ws, x, route, f"E{e} N{n} K{k} T{t} S{slots}")
