@@ -351,6 +351,10 @@ dsa_status dsa_mxfp4_to_fp8(const dsa_mx_experts* w, const int32_t* experts, int
  * workspace: at least dsa_moe_workspace_size bytes, 256 B aligned (with
  * DSA_MOE_FP8_WORKSPACE it holds min(num_experts, tokens * slots) expert
  * slots of n * k + n * k / 32 bytes).  route: int32 [tokens, slots].
+ * Limits (DSA_ERR_UNSUPPORTED beyond them): tokens * slots <= 2^30, n * k <
+ * 2^31, and fewer than 2^24 (row tile, column block) work items.  Output rows are
+ * independent of the order pairs are grouped in, so results are bit-exact
+ * from run to run.
  */
 enum { DSA_MOE_FP8_WORKSPACE = 0, DSA_MOE_FP4_DIRECT = 1 };
 dsa_status dsa_moe_workspace_size(const dsa_mx_experts* w, int32_t tokens, int32_t slots,
