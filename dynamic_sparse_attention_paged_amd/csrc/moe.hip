@@ -276,7 +276,6 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-constexpr int kAPitch = 144;  // LDS bytes per A row: 128 + 16, so 16 rows hit distinct banks
 
 // grid (row-tile slots x ncb column blocks), block 256.  A work item (row
 // tile, column block c) covers the tile's 16 RT pairs of one expert and columns
@@ -286,14 +285,15 @@ constexpr int kAPitch = 144;  // LDS bytes per A row: 128 + 16, so 16 rows hit d
 // them, and within a run the column blocks of kMoeGroupTiles consecutive row
 // tiles come together: tiles of one expert then read its weight columns, and
 // column blocks of one tile its A rows, through the same L2 at about the same
-// time (workgroups past the live items exit).  Per 128-wide K step the
+// time (workgroups past the live items exit).  Per K step of 128 KS the
 // workgroup stages the tile's A rows (gathered per pair) once in LDS (double
 // buffered), each wave reads its B rows straight from memory one step ahead,
-// and runs RT x CT scaled MFMAs.  kFp4: B is the MXFP4 weights; otherwise the
+// and runs KS x RT x CT scaled MFMAs.  KS = 2 doubles the bytes each wave has
+// in flight (for the short tiles, whose B stream is bound by memory latency).  kFp4: B is the MXFP4 weights; otherwise the
 // FP8 workspace (expert e in slot b_slot[e]).  Two waves per SIMD (at most 256
 // registers a lane; every variant launched fits without spills): one wave per
 // SIMD leaves the matrix unit idle through every load and barrier.
-template <bool kFp4, int RT, int CT>
+template <bool kFp4, int RT, int CT, int KS>
 __global__ __launch_bounds__(kMoeThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
@@ -303,9 +303,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     const int32_t* __restrict__ tile_p1, const int32_t* __restrict__ n_tiles, int ncb,
     float* __restrict__ out) {
   constexpr int kRows = 16 * RT;
-  constexpr int kPasses = kRows * 8 / kMoeThreads;  // 16 B chunks: 8 per row and K step
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kRows * kAPitch];
-  __shared__ uint8_t s_lds[2][kRows * 4];
+  constexpr int kChunks = 8 * KS;                         // 16 B chunks of a row per K step
+  constexpr int kPasses = kRows * kChunks / kMoeThreads;  // chunks each thread stages
+  constexpr int kRowsPerPass = kMoeThreads / kChunks;
+  // LDS bytes per A row: 128 KS + 16, so the 16 rows of an MFMA read hit distinct banks
+  constexpr int kPitch = 128 * KS + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kRows * kPitch];
+  __shared__ uint8_t s_lds[2][kRows * 4 * KS];
   const int live_tiles = *n_tiles, live = live_tiles * ncb;
   const int hw = blockIdx.x;
   if (hw >= live) return;  // the whole workgroup
@@ -323,15 +327,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   const int e = tile_e[tile], p0 = tile_p0[tile], p1 = tile_p1[tile];
   const int slot = kFp4 ? e : b_slot[e];
   const int kb = k / 32;
-  // staging: thread tid copies chunk tid % 8 of rows tid / 8 + 32 q (q < kPasses);
-  // rows past the tile repeat the tile's first pair
+  // staging: thread tid copies chunk tid % kChunks of rows tid / kChunks +
+  // kRowsPerPass q (q < kPasses); rows past the tile repeat the tile's first pair
   const uint8_t* srow[kPasses];
 #pragma unroll
   for (int q = 0; q < kPasses; ++q) {
-    const int p = p0 + tid / 8 + 32 * q;
+    const int p = p0 + tid / kChunks + kRowsPerPass * q;
     srow[q] = a_codes + (size_t)(list[p < p1 ? p : p0] / slots) * k;
   }
-  const uint8_t* sscale = nullptr;  // scale staging: thread tid < kRows * 4 / 4 copies one row's 4
+  const uint8_t* sscale = nullptr;  // scale staging: thread tid < kRows copies one row's 4 KS
   if (tid < kRows) {
     const int p = p0 + tid;
     sscale = a_scales + (size_t)(list[p < p1 ? p : p0] / slots) * kb;
@@ -347,31 +351,43 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     boff[ct] = (uint32_t)col * rb;
     soff[ct] = (uint32_t)col * kb;
   }
-  auto load_a = [&](int k0, v4i (&st)[kPasses], uint32_t& sc) {
+  auto load_a = [&](int k0, v4i (&st)[kPasses], uint32_t (&sc)[KS]) {
 #pragma unroll
     for (int q = 0; q < kPasses; ++q)
-      st[q] = *reinterpret_cast<const v4i*>(srow[q] + k0 + 16 * (tid & 7));
-    if (tid < kRows) sc = *reinterpret_cast<const uint32_t*>(sscale + k0 / 32);
+      st[q] = *reinterpret_cast<const v4i*>(srow[q] + k0 + 16 * (tid % kChunks));
+    if (tid < kRows) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc[ks] = *reinterpret_cast<const uint32_t*>(sscale + k0 / 32 + 4 * ks);
+    }
   };
-  auto store_a = [&](int buf, const v4i (&st)[kPasses], uint32_t sc) {
+  auto store_a = [&](int buf, const v4i (&st)[kPasses], const uint32_t (&sc)[KS]) {
 #pragma unroll
     for (int q = 0; q < kPasses; ++q)
-      *reinterpret_cast<v4i*>(&a_lds[buf][(tid / 8 + 32 * q) * kAPitch + 16 * (tid & 7)]) = st[q];
-    if (tid < kRows) *reinterpret_cast<uint32_t*>(&s_lds[buf][tid * 4]) = sc;
+      *reinterpret_cast<v4i*>(
+          &a_lds[buf][(tid / kChunks + kRowsPerPass * q) * kPitch + 16 * (tid % kChunks)]) = st[q];
+    if (tid < kRows) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        *reinterpret_cast<uint32_t*>(&s_lds[buf][tid * 4 * KS + 4 * ks]) = sc[ks];
+    }
   };
   // FP4 fragments are 16 bytes (the instruction's upper four registers are
   // unused for FP4 and passed as zeros at the call)
   using BFrag = typename std::conditional<kFp4, v4i, v8i>::type;
-  auto load_b = [&](int k0, BFrag (&b)[CT], int (&sb)[CT]) {
+  auto load_b = [&](int k0, BFrag (&b)[KS][CT], int (&sb)[KS][CT]) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      if constexpr (kFp4) {
-        b[ct] = *reinterpret_cast<const v4i*>(bbase + boff[ct] + k0 / 2 + 16 * kg);
-      } else {
-        b[ct] = load_fp8_operand(bbase + boff[ct], k0, kg);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int kk = k0 + 128 * ks;
+        if constexpr (kFp4) {
+          b[ks][ct] = *reinterpret_cast<const v4i*>(bbase + boff[ct] + kk / 2 + 16 * kg);
+        } else {
+          b[ks][ct] = load_fp8_operand(bbase + boff[ct], kk, kg);
+        }
+        sb[ks][ct] = sbase[soff[ct] + kk / 32 + kg];
       }
-      sb[ct] = sbase[soff[ct] + k0 / 32 + kg];
-    }
   };
   auto operand = [](const BFrag& b) {
     if constexpr (kFp4) return v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0};
@@ -384,11 +400,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
   v4i st[kPasses];
-  uint32_t sc = 0;
+  uint32_t sc[KS] = {};
   load_a(0, st, sc);
   store_a(0, st, sc);
-  BFrag b[CT];
-  int sb[CT];
+  BFrag b[KS][CT];
+  int sb[KS][CT];
   if (wave_on) load_b(0, b, sb);
   // Drain the prologue's loads here: the loop body reads b only after copying
   // it from the loads of the step before (which it waits for), and without this
@@ -396,37 +412,41 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   // next step, which would stall every step on a full memory round trip.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int steps = k / 128;
+  const int steps = k / (128 * KS);
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < steps;
-    BFrag bn[CT];
-    int sbn[CT];
+    BFrag bn[KS][CT];
+    int sbn[KS][CT];
     if (more) {
-      load_a(128 * (s + 1), st, sc);
-      if (wave_on) load_b(128 * (s + 1), bn, sbn);
+      load_a(128 * KS * (s + 1), st, sc);
+      if (wave_on) load_b(128 * KS * (s + 1), bn, sbn);
     }
     if (wave_on) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const uint8_t* ar = &a_lds[buf][(16 * rt + r) * kAPitch];
-        const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * kg);
-        const v4i hi = *reinterpret_cast<const v4i*>(ar + 64 + 16 * kg);
-        const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int sa = s_lds[buf][(16 * rt + r) * 4 + kg];
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              a, operand(b[ct]), acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sb[ct]);
-      }
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint8_t* ar = &a_lds[buf][(16 * rt + r) * kPitch + 128 * ks];
+          const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * kg);
+          const v4i hi = *reinterpret_cast<const v4i*>(ar + 64 + 16 * kg);
+          const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int sa = s_lds[buf][(16 * rt + r) * 4 * KS + 4 * ks + kg];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a, operand(b[ks][ct]), acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sb[ks][ct]);
+        }
     }
     if (more) {
       store_a(buf ^ 1, st, sc);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        b[ct] = bn[ct];
-        sb[ct] = sbn[ct];
-      }
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          b[ks][ct] = bn[ks][ct];
+          sb[ks][ct] = sbn[ks][ct];
+        }
     }
     __syncthreads();
   }
@@ -537,6 +557,9 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
   // x 128 columns over the FP8 workspace (twice the B fragment registers);
   // short tiles: 64 pairs x 256 columns (a typical decode expert in one tile)
   const bool tall = L.bm == kMoeBMLarge;
+  // short tiles over the FP4 weights take K 256 at a time where K allows (twice
+  // the loads in flight; over the FP8 workspace that would spill registers)
+  const bool ks2 = w.k % 256 == 0;
   const int wg_cols = tall && fp8_workspace ? 128 : 256;
   const int ncb = (w.n + wg_cols - 1) / wg_cols;
   const dim3 grid((unsigned)((long)L.max_tiles * ncb));
@@ -553,17 +576,20 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
     bc = wc;
     bs = wsc;
     if (tall)
-      hipLaunchKernelGGL((moe_gemm<false, 8, 2>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<false, 8, 2, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else
-      hipLaunchKernelGGL((moe_gemm<false, 4, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<false, 4, 4, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
   } else {
     if (tall)
-      hipLaunchKernelGGL((moe_gemm<true, 8, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<true, 8, 4, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+    else if (ks2)
+      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 2>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else
-      hipLaunchKernelGGL((moe_gemm<true, 4, 4>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
   }
   return hipGetLastError();
