@@ -216,6 +216,14 @@ def test_moe_validation(lib):
     assert lib.dsa_moe_workspace_size(ctypes.byref(_mx(w_fp4=FAKE + 8)), 8, 2, 1,
                                       ctypes.byref(n)) == E["DSA_ERR_ALIGN"]
     assert lib.dsa_moe_workspace_size(ctypes.byref(w), 8, 2, 7, ctypes.byref(n)) == E["DSA_ERR_SHAPE"]
+    # size limits: more than 2^30 pairs; a launch of 2^24 or more (row tile,
+    # column block) work items (2^24 pairs in 128-pair tiles x 512 column blocks)
+    assert lib.dsa_moe_workspace_size(ctypes.byref(w), (1 << 29) + 1, 2, 1, ctypes.byref(n)) == \
+        E["DSA_ERR_UNSUPPORTED"]
+    wide = _mx(n=65536, k=128)
+    assert lib.dsa_moe_workspace_size(ctypes.byref(wide), 1 << 20, 16, 1, ctypes.byref(n)) == \
+        E["DSA_ERR_UNSUPPORTED"]
+    assert lib.dsa_moe_workspace_size(ctypes.byref(wide), 1 << 10, 16, 1, ctypes.byref(n)) == 0
     lib.dsa_moe_workspace_size(ctypes.byref(w), 8, 2, 1, ctypes.byref(n))
 
     def gemm(ws=FAKE, nbytes=n.value, out=FAKE, route=FAKE, tokens=8, mode=1):
