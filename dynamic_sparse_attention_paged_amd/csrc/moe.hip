@@ -306,8 +306,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   constexpr int kChunks = 8 * KS;                         // 16 B chunks of a row per K step
   constexpr int kPasses = kRows * kChunks / kMoeThreads;  // chunks each thread stages
   constexpr int kRowsPerPass = kMoeThreads / kChunks;
-  // LDS bytes per A row: 128 KS + 16, so the 16 rows of an MFMA read hit distinct banks
-  constexpr int kPitch = 128 * KS + 16;
+  // LDS bytes per A row: 128 KS, with the 16 B chunk c of row R stored in slot
+  // c ^ swizzle(R): (R / 2) % 8 for rows of 128 B, R % 16 for rows of 256 B.
+  // Either way the 16 rows of an MFMA read, and the chunks of a staging write,
+  // land on distinct banks.
+  constexpr int kPitch = 128 * KS;
+  auto swizzle = [](int row) { return KS == 1 ? (row >> 1) & 7 : row & 15; };
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kRows * kPitch];
   __shared__ uint8_t s_lds[2][kRows * 4 * KS];
   const int live_tiles = *n_tiles, live = live_tiles * ncb;
@@ -363,9 +367,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   };
   auto store_a = [&](int buf, const v4i (&st)[kPasses], const uint32_t (&sc)[KS]) {
 #pragma unroll
-    for (int q = 0; q < kPasses; ++q)
-      *reinterpret_cast<v4i*>(
-          &a_lds[buf][(tid / kChunks + kRowsPerPass * q) * kPitch + 16 * (tid % kChunks)]) = st[q];
+    for (int q = 0; q < kPasses; ++q) {
+      const int row = tid / kChunks + kRowsPerPass * q, c = tid % kChunks;
+      *reinterpret_cast<v4i*>(&a_lds[buf][row * kPitch + 16 * (c ^ swizzle(row))]) = st[q];
+    }
     if (tid < kRows) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -413,6 +418,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int steps = k / (128 * KS);
+  const int swz = swizzle(r);  // of the rows 16 rt + r this lane reads
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < steps;
@@ -427,9 +433,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const uint8_t* ar = &a_lds[buf][(16 * rt + r) * kPitch + 128 * ks];
-          const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * kg);
-          const v4i hi = *reinterpret_cast<const v4i*>(ar + 64 + 16 * kg);
+          const uint8_t* ar = &a_lds[buf][(16 * rt + r) * kPitch];
+          const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * ((8 * ks + kg) ^ swz));
+          const v4i hi = *reinterpret_cast<const v4i*>(ar + 16 * ((8 * ks + 4 + kg) ^ swz));
           const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const int sa = s_lds[buf][(16 * rt + r) * 4 * KS + 4 * ks + kg];
 #pragma unroll
