@@ -276,7 +276,6 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-
 // grid (row-tile slots x ncb column blocks), block 256.  A work item (row
 // tile, column block c) covers the tile's 16 RT pairs of one expert and columns
 // [64 CT c, 64 CT (c + 1)); wave w owns 16 CT of them as CT 16-column MFMA
@@ -289,10 +288,11 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
 // workgroup stages the tile's A rows (gathered per pair) once in LDS (double
 // buffered), each wave reads its B rows straight from memory one step ahead,
 // and runs KS x RT x CT scaled MFMAs.  KS = 2 doubles the bytes each wave has
-// in flight (for the short tiles, whose B stream is bound by memory latency).  kFp4: B is the MXFP4 weights; otherwise the
-// FP8 workspace (expert e in slot b_slot[e]).  Two waves per SIMD (at most 256
-// registers a lane; every variant launched fits without spills): one wave per
-// SIMD leaves the matrix unit idle through every load and barrier.
+// in flight (for the short tiles, whose B stream is bound by memory latency).
+// kFp4: B is the MXFP4 weights; otherwise the FP8 workspace (expert e in slot
+// b_slot[e]).  Two waves per SIMD (at most 256 registers a lane; every variant
+// launched fits without spills): one wave per SIMD leaves the matrix unit idle
+// through every load and barrier.
 template <bool kFp4, int RT, int CT, int KS>
 __global__ __launch_bounds__(kMoeThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
