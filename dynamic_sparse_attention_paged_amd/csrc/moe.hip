@@ -292,8 +292,11 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
 // kFp4: B is the MXFP4 weights; otherwise the FP8 workspace (expert e in slot
 // b_slot[e]).  Two waves per SIMD (at most 256 registers a lane; every variant
 // launched fits without spills): one wave per SIMD leaves the matrix unit idle
-// through every load and barrier.
-template <bool kFp4, int RT, int CT, int KS>
+// through every load and barrier.  SV (KS = 1, K % 512 == 0, weight scales 16 B
+// aligned): lane (r, kg) loads 16 B of weight scales of column 16 kg + r once
+// per 4 steps, and the lanes trade them by cross-lane reads, instead of four
+// 1-byte loads per step that each touch 16 cache lines for 64 bytes.
+template <bool kFp4, int RT, int CT, int KS, bool SV>
 __global__ __launch_bounds__(kMoeThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
@@ -391,7 +394,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
         } else {
           b[ks][ct] = load_fp8_operand(bbase + boff[ct], kk, kg);
         }
-        sb[ks][ct] = sbase[soff[ct] + kk / 32 + kg];
+        if constexpr (!SV) sb[ks][ct] = sbase[soff[ct] + kk / 32 + kg];
       }
   };
   auto operand = [](const BFrag& b) {
@@ -409,8 +412,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   load_a(0, st, sc);
   store_a(0, st, sc);
   BFrag b[KS][CT];
-  int sb[KS][CT];
+  int sb[KS][CT] = {};
   if (wave_on) load_b(0, b, sb);
+  static_assert(!SV || (KS == 1 && CT == 4), "16 B scale groups: one K slice, four column tiles");
+  v4i sg = {}, sgn = {};  // SV: scales of steps 4t .. 4t + 3 of column n0 + 16 kg + r
+  const uint32_t sgoff = (uint32_t)min(n0 + 16 * kg + r, n - 1) * kb;
+  if (SV && wave_on) sg = *reinterpret_cast<const v4i*>(sbase + sgoff);
   // Drain the prologue's loads here: the loop body reads b only after copying
   // it from the loads of the step before (which it waits for), and without this
   // the compiler's wait at the loop head also covers the loads issued for the
@@ -427,8 +434,24 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     if (more) {
       load_a(128 * KS * (s + 1), st, sc);
       if (wave_on) load_b(128 * KS * (s + 1), bn, sbn);
+      if (SV && wave_on && ((s + 1) & 3) == 0)
+        sgn = *reinterpret_cast<const v4i*>(sbase + sgoff + 16 * ((s + 1) >> 2));
     }
     if (wave_on) {
+      int sbv[KS][CT];
+      if constexpr (SV) {
+        // step s's byte kg of column 16 ct + r sits in word s % 4 of lane 16 ct + r
+        const int u = s & 3;
+        const int word = u == 0 ? sg[0] : u == 1 ? sg[1] : u == 2 ? sg[2] : sg[3];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          sbv[0][ct] = (__shfl(word, 16 * ct + r) >> (8 * kg)) & 0xff;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) sbv[ks][ct] = sb[ks][ct];
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -441,7 +464,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
             acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                a, operand(b[ks][ct]), acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sb[ks][ct]);
+                a, operand(b[ks][ct]), acc[rt][ct], 0, kFp4 ? 4 : 0, 0, sa, 0, sbv[ks][ct]);
         }
     }
     if (more) {
@@ -452,6 +475,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
         for (int ct = 0; ct < CT; ++ct) {
           b[ks][ct] = bn[ks][ct];
           sb[ks][ct] = sbn[ks][ct];
+      if (SV && ((s + 1) & 3) == 0) sg = sgn;
         }
     }
     __syncthreads();
@@ -566,6 +590,8 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
   // short tiles over the FP4 weights take K 256 at a time where K allows (twice
   // the loads in flight; over the FP8 workspace that would spill registers)
   const bool ks2 = w.k % 256 == 0;
+  // 16 B weight-scale groups (FP4 tall tiles): scale rows a multiple of 16 B, 16 B aligned
+  const bool sv = w.k % 512 == 0 && (reinterpret_cast<uintptr_t>(w.scale) & 15) == 0;
   const int wg_cols = tall && fp8_workspace ? 128 : 256;
   const int ncb = (w.n + wg_cols - 1) / wg_cols;
   const dim3 grid((unsigned)((long)L.max_tiles * ncb));
@@ -582,20 +608,23 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
     bc = wc;
     bs = wsc;
     if (tall)
-      hipLaunchKernelGGL((moe_gemm<false, 8, 2, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<false, 8, 2, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else
-      hipLaunchKernelGGL((moe_gemm<false, 4, 4, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<false, 4, 4, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
   } else {
-    if (tall)
-      hipLaunchKernelGGL((moe_gemm<true, 8, 4, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+    if (tall && sv)
+      hipLaunchKernelGGL((moe_gemm<true, 8, 4, 1, true>), grid, dim3(kMoeThreads), 0, st, bc, bs,
+                         slot, w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+    else if (tall)
+      hipLaunchKernelGGL((moe_gemm<true, 8, 4, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs,
+                         slot, w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else if (ks2)
-      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 2>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 2, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
     else
-      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 1>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
+      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
                          w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
   }
   return hipGetLastError();
