@@ -295,7 +295,8 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
 // through every load and barrier.  SV (KS = 1, K % 512 == 0, weight scales 16 B
 // aligned): lane (r, kg) loads 16 B of weight scales of column 16 kg + r once
 // per 4 steps, and the lanes trade them by cross-lane reads, instead of four
-// 1-byte loads per step that each touch 16 cache lines for 64 bytes.
+// 1-byte loads per step that each touch 16 cache lines for 64 bytes; the A
+// scales likewise come in 16 B a row per 4 steps.
 template <bool kFp4, int RT, int CT, int KS, bool SV>
 __global__ __launch_bounds__(kMoeThreads)
 __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
@@ -316,7 +317,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   constexpr int kPitch = 128 * KS;
   auto swizzle = [](int row) { return KS == 1 ? (row >> 1) & 7 : row & 15; };
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kRows * kPitch];
-  __shared__ uint8_t s_lds[2][kRows * 4 * KS];
+  // A scales: per step (4 KS bytes a row), or with SV per group of 4 steps (16 B a row)
+  constexpr int kScaleRow = SV ? 16 : 4 * KS;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[2][kRows * kScaleRow];
   const int live_tiles = *n_tiles, live = live_tiles * ncb;
   const int hw = blockIdx.x;
   if (hw >= live) return;  // the whole workgroup
@@ -362,7 +365,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
 #pragma unroll
     for (int q = 0; q < kPasses; ++q)
       st[q] = *reinterpret_cast<const v4i*>(srow[q] + k0 + 16 * (tid % kChunks));
-    if (tid < kRows) {
+    if (!SV && tid < kRows) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         sc[ks] = *reinterpret_cast<const uint32_t*>(sscale + k0 / 32 + 4 * ks);
@@ -374,11 +377,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
       const int row = tid / kChunks + kRowsPerPass * q, c = tid % kChunks;
       *reinterpret_cast<v4i*>(&a_lds[buf][row * kPitch + 16 * (c ^ swizzle(row))]) = st[q];
     }
-    if (tid < kRows) {
+    if (!SV && tid < kRows) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         *reinterpret_cast<uint32_t*>(&s_lds[buf][tid * 4 * KS + 4 * ks]) = sc[ks];
     }
+  };
+  // SV: the A scales of steps 4 t .. 4 t + 3 (16 B a row) into scale buffer t % 2
+  v4i scg = {};
+  auto load_a_scales = [&](int t) {
+    if (tid < kRows) scg = *reinterpret_cast<const v4i*>(sscale + 16 * t);
+  };
+  auto store_a_scales = [&](int t) {
+    if (tid < kRows) *reinterpret_cast<v4i*>(&s_lds[t & 1][tid * 16]) = scg;
   };
   // FP4 fragments are 16 bytes (the instruction's upper four registers are
   // unused for FP4 and passed as zeros at the call)
@@ -411,6 +422,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   uint32_t sc[KS] = {};
   load_a(0, st, sc);
   store_a(0, st, sc);
+  if constexpr (SV) {
+    load_a_scales(0);
+    store_a_scales(0);
+  }
   BFrag b[KS][CT];
   int sb[KS][CT] = {};
   if (wave_on) load_b(0, b, sb);
@@ -433,6 +448,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     int sbn[KS][CT];
     if (more) {
       load_a(128 * KS * (s + 1), st, sc);
+      if (SV && ((s + 1) & 3) == 0) load_a_scales((s + 1) >> 2);
       if (wave_on) load_b(128 * KS * (s + 1), bn, sbn);
       if (SV && wave_on && ((s + 1) & 3) == 0)
         sgn = *reinterpret_cast<const v4i*>(sbase + sgoff + 16 * ((s + 1) >> 2));
@@ -460,7 +476,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
           const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * ((8 * ks + kg) ^ swz));
           const v4i hi = *reinterpret_cast<const v4i*>(ar + 16 * ((8 * ks + 4 + kg) ^ swz));
           const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const int sa = s_lds[buf][(16 * rt + r) * 4 * KS + 4 * ks + kg];
+          const int sa = SV ? s_lds[(s >> 2) & 1][(16 * rt + r) * 16 + 4 * (s & 3) + kg]
+                            : s_lds[buf][(16 * rt + r) * 4 * KS + 4 * ks + kg];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
             acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -469,6 +486,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     }
     if (more) {
       store_a(buf ^ 1, st, sc);
+      if (SV && ((s + 1) & 3) == 0) store_a_scales((s + 1) >> 2);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -590,8 +608,9 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
   // short tiles over the FP4 weights take K 256 at a time where K allows (twice
   // the loads in flight; over the FP8 workspace that would spill registers)
   const bool ks2 = w.k % 256 == 0;
-  // 16 B weight-scale groups (FP4 tall tiles): scale rows a multiple of 16 B, 16 B aligned
-  const bool sv = w.k % 512 == 0 && (reinterpret_cast<uintptr_t>(w.scale) & 15) == 0;
+  // 16 B scale groups (FP4 tall tiles): scale rows a multiple of 16 B, 16 B aligned
+  const bool sv = w.k % 512 == 0 && (reinterpret_cast<uintptr_t>(w.scale) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0;
   const int wg_cols = tall && fp8_workspace ? 128 : 256;
   const int ncb = (w.n + wg_cols - 1) / wg_cols;
   const dim3 grid((unsigned)((long)L.max_tiles * ncb));
