@@ -292,9 +292,9 @@ __device__ __forceinline__ v8i load_fp8_operand(const uint8_t* row, int k0, int 
 // kFp4: B is the MXFP4 weights; otherwise the FP8 workspace (expert e in slot
 // b_slot[e]).  Two waves per SIMD (at most 256 registers a lane; every variant
 // launched fits without spills): one wave per SIMD leaves the matrix unit idle
-// through every load and barrier.  SV (KS = 1, K % 512 == 0, weight scales 16 B
-// aligned): lane (r, kg) loads 16 B of weight scales of column 16 kg + r once
-// per 4 steps, and the lanes trade them by cross-lane reads, instead of four
+// through every load and barrier.  SV (K % 512 == 0, scale arrays 16 B
+// aligned): lane (r, kg) loads 16 B of weight scales of column 16 (kg % CT) + r
+// once per 4 K slices of 128, and the lanes trade them by cross-lane reads, instead of four
 // 1-byte loads per step that each touch 16 cache lines for 64 bytes; the A
 // scales likewise come in 16 B a row per 4 steps.
 template <bool kFp4, int RT, int CT, int KS, bool SV>
@@ -429,9 +429,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
   BFrag b[KS][CT];
   int sb[KS][CT] = {};
   if (wave_on) load_b(0, b, sb);
-  static_assert(!SV || (KS == 1 && CT == 4), "16 B scale groups: one K slice, four column tiles");
-  v4i sg = {}, sgn = {};  // SV: scales of steps 4t .. 4t + 3 of column n0 + 16 kg + r
-  const uint32_t sgoff = (uint32_t)min(n0 + 16 * kg + r, n - 1) * kb;
+  static_assert(CT == 1 || CT == 2 || CT == 4, "column tiles per wave");
+  constexpr int G = 4 / KS;  // SV: steps per 16 B scale group (4 slices of K 128)
+  // SV: the weight scales of one group for column n0 + 16 (kg % CT) + r
+  v4i sg = {}, sgn = {};
+  const uint32_t sgoff = (uint32_t)min(n0 + 16 * (kg % CT) + r, n - 1) * kb;
   if (SV && wave_on) sg = *reinterpret_cast<const v4i*>(sbase + sgoff);
   // Drain the prologue's loads here: the loop body reads b only after copying
   // it from the loads of the step before (which it waits for), and without this
@@ -448,20 +450,23 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     int sbn[KS][CT];
     if (more) {
       load_a(128 * KS * (s + 1), st, sc);
-      if (SV && ((s + 1) & 3) == 0) load_a_scales((s + 1) >> 2);
+      if (SV && (s + 1) % G == 0) load_a_scales((s + 1) / G);
       if (wave_on) load_b(128 * KS * (s + 1), bn, sbn);
-      if (SV && wave_on && ((s + 1) & 3) == 0)
-        sgn = *reinterpret_cast<const v4i*>(sbase + sgoff + 16 * ((s + 1) >> 2));
+      if (SV && wave_on && (s + 1) % G == 0)
+        sgn = *reinterpret_cast<const v4i*>(sbase + sgoff + 16 * ((s + 1) / G));
     }
     if (wave_on) {
       int sbv[KS][CT];
       if constexpr (SV) {
-        // step s's byte kg of column 16 ct + r sits in word s % 4 of lane 16 ct + r
-        const int u = s & 3;
-        const int word = u == 0 ? sg[0] : u == 1 ? sg[1] : u == 2 ? sg[2] : sg[3];
+        // slice ks of step s: byte kg of word (s % G) KS + ks of lane 16 ct + r
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          sbv[0][ct] = (__shfl(word, 16 * ct + r) >> (8 * kg)) & 0xff;
+        for (int ks = 0; ks < KS; ++ks) {
+          const int u = (s % G) * KS + ks;
+          const int word = u == 0 ? sg[0] : u == 1 ? sg[1] : u == 2 ? sg[2] : sg[3];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            sbv[ks][ct] = (__shfl(word, 16 * ct + r) >> (8 * kg)) & 0xff;
+        }
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -476,7 +481,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
           const v4i lo = *reinterpret_cast<const v4i*>(ar + 16 * ((8 * ks + kg) ^ swz));
           const v4i hi = *reinterpret_cast<const v4i*>(ar + 16 * ((8 * ks + 4 + kg) ^ swz));
           const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const int sa = SV ? s_lds[(s >> 2) & 1][(16 * rt + r) * 16 + 4 * (s & 3) + kg]
+          const int sa = SV ? s_lds[(s / G) & 1][(16 * rt + r) * 16 + 4 * ((s % G) * KS + ks) + kg]
                             : s_lds[buf][(16 * rt + r) * 4 * KS + 4 * ks + kg];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
@@ -486,14 +491,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void moe_gemm(
     }
     if (more) {
       store_a(buf ^ 1, st, sc);
-      if (SV && ((s + 1) & 3) == 0) store_a_scales((s + 1) >> 2);
+      if (SV && (s + 1) % G == 0) store_a_scales((s + 1) / G);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           b[ks][ct] = bn[ks][ct];
           sb[ks][ct] = sbn[ks][ct];
-      if (SV && ((s + 1) & 3) == 0) sg = sgn;
+      if (SV && (s + 1) % G == 0) sg = sgn;
         }
     }
     __syncthreads();
@@ -608,14 +613,19 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
   // short tiles over the FP4 weights take K 256 at a time where K allows (twice
   // the loads in flight; over the FP8 workspace that would spill registers)
   const bool ks2 = w.k % 256 == 0;
-  // 16 B scale groups (FP4 tall tiles): scale rows a multiple of 16 B, 16 B aligned
-  const bool sv = w.k % 512 == 0 && (reinterpret_cast<uintptr_t>(w.scale) & 15) == 0 &&
-                  (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0;
+  // 16 B scale groups: scale rows a multiple of 16 B, both scale arrays 16 B
+  // aligned (the FP8 workspace's are)
+  const bool sv = w.k % 512 == 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
+                  (fp8_workspace || (reinterpret_cast<uintptr_t>(w.scale) & 15) == 0);
   const int wg_cols = tall && fp8_workspace ? 128 : 256;
   const int ncb = (w.n + wg_cols - 1) / wg_cols;
   const dim3 grid((unsigned)((long)L.max_tiles * ncb));
   const uint8_t* bc = w.fp4;
   const uint8_t* bs = w.scale;
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kMoeThreads), 0, st, bc, bs, slot, w.n, w.k, a_codes,
+                       a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+  };
   if (fp8_workspace) {
     // the pages' path: the routed experts unpacked to FP8 into the workspace,
     // then the matmul on the workspace
@@ -626,25 +636,25 @@ hipError_t launch_moe_gemm(const MxExperts& w, bool fp8_workspace, const uint8_t
                        w.scale, w.n, w.k, active, L.max_active, n_active, wc, wsc);
     bc = wc;
     bs = wsc;
-    if (tall)
-      hipLaunchKernelGGL((moe_gemm<false, 8, 2, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+    if (tall && sv)
+      launch(moe_gemm<false, 8, 2, 1, true>);
+    else if (tall)
+      launch(moe_gemm<false, 8, 2, 1, false>);
+    else if (sv)
+      launch(moe_gemm<false, 4, 4, 1, true>);
     else
-      hipLaunchKernelGGL((moe_gemm<false, 4, 4, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+      launch(moe_gemm<false, 4, 4, 1, false>);
   } else {
     if (tall && sv)
-      hipLaunchKernelGGL((moe_gemm<true, 8, 4, 1, true>), grid, dim3(kMoeThreads), 0, st, bc, bs,
-                         slot, w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+      launch(moe_gemm<true, 8, 4, 1, true>);
     else if (tall)
-      hipLaunchKernelGGL((moe_gemm<true, 8, 4, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs,
-                         slot, w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+      launch(moe_gemm<true, 8, 4, 1, false>);
+    else if (ks2 && sv)
+      launch(moe_gemm<true, 4, 4, 2, true>);
     else if (ks2)
-      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 2, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+      launch(moe_gemm<true, 4, 4, 2, false>);
     else
-      hipLaunchKernelGGL((moe_gemm<true, 4, 4, 1, false>), grid, dim3(kMoeThreads), 0, st, bc, bs, slot,
-                         w.n, w.k, a_codes, a_scales, slots, list, te, tp0, tp1, nt, ncb, out);
+      launch(moe_gemm<true, 4, 4, 1, false>);
   }
   return hipGetLastError();
 }

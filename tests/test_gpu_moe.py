@@ -126,6 +126,7 @@ def _check_gemm(dsa, wp, ws, x, route, label):
                                            (9, 64, 128, 5, 8),
                                            (4, 320, 512, 300, 2),   # 150 pairs per expert: 128-row tiles
                                            (4, 256, 2048, 400, 2),  # tall tiles, 16-step K: scale groups
+                                           (6, 128, 1024, 40, 4),   # short tiles, K 1024: scale groups
                                            (8, 64, 128, 1500, 3),   # pairs over several grouping chunks
                                            (2100, 64, 128, 300, 2)])  # more experts than the LDS table
 def test_grouped_gemm_matches_oracle(dsa, e, n, k, t, slots):
