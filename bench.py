@@ -70,15 +70,20 @@ def index_flops(w):
 class Device:
     """One workload on the device, with `nsets` rotating query batches."""
 
-    def __init__(self, w, nsets, qseed0=5000):
+    def __init__(self, w, nsets, qseed0=5000, kv_layout=None):
         import torch
         import dynamic_sparse_attention_paged_amd as dsa
         from dsa_synth import device as synth_dev, workload
 
         self.w = w
+        self.kv_layout = KV_LAYOUT if kv_layout is None else kv_layout
         t = synth_dev.upload(w)
+        if self.kv_layout == dsa.KV_HEAD_MAJOR:  # same values, [P, Hkv, bs, 128]
+            for name in ("k_cache", "v_cache"):
+                t[name] = t[name].permute(0, 2, 1, 3).contiguous()
+            torch.cuda.empty_cache()
         self.kv = dsa.PagedKV(t["k_cache"], t["v_cache"], t["idx_keys"], t["idx_scale"],
-                              t["block_table"], t["seq_lens"])
+                              t["block_table"], t["seq_lens"], kv_layout=self.kv_layout)
         self.sets = [dsa.Queries(t["q"], t["q_idx"], t["w_idx"], t["q_seq"], t["q_pos"])]
         self.hosts = [w]
         for i in range(1, nsets):
@@ -170,6 +175,11 @@ def event_time_ms(fn, n, warmup):
     return a.elapsed_time(b) / n
 
 
+# Order inside a cache block, by its dsa_kv_layout value.
+LAYOUT_NAMES = ["token_major", "head_major"]
+KV_LAYOUT = 1
+
+
 def traffic_from_profile():
     """Measured HBM bytes per launch of the attention kernel, if the counters in
     profiles/ were taken on the current kernel source."""
@@ -177,7 +187,7 @@ def traffic_from_profile():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         src = hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()
-        if t.get("attn_src_sha256") != src:
+        if t.get("attn_src_sha256") != src or t.get("kv_layout") != LAYOUT_NAMES[KV_LAYOUT]:
             return None
         return t.get("bytes_per_launch")
     except (OSError, ValueError):
@@ -230,10 +240,10 @@ def cpu_baseline(w, budget_s):
                        f"timed)", seconds=round(spent, 2))
 
 
-def decode_extra(w, steps, nsets):
+def decode_extra(w, steps, nsets, kv_layout=None):
     """q/s and HBM GB/s of a decode workload through the fused entry point."""
     import torch
-    D = Device(w, nsets)
+    D = Device(w, nsets, kv_layout=kv_layout)
     D.capture()
     ms = event_time_ms(D.replay, steps, 3)
     D.select()
@@ -241,7 +251,8 @@ def decode_extra(w, steps, nsets):
     attn_ms = event_time_ms(D.attn, steps, 3)
     cnt = D.cnt[0].cpu().numpy()
     byts = attn_bytes(w, cnt) + index_bytes(w)
-    res = dict(workload=w.name, queries=w.num_queries, ms_per_step=round(ms, 5),
+    res = dict(workload=w.name, kv_layout=LAYOUT_NAMES[D.kv_layout], queries=w.num_queries,
+               ms_per_step=round(ms, 5),
                queries_per_s=round(w.num_queries / (ms * 1e-3), 1),
                path_gbps=round(byts / (ms * 1e-3) / 1e9, 1),
                path_frac_of_hbm=round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -415,6 +426,9 @@ def main():
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--kv-layout", choices=["head_major", "token_major"], default="head_major",
+                    help="order inside a cache block: [head][token][dim] or the pages' "
+                         "[token][head][dim] (the other one is timed as an extra)")
     ap.add_argument("--extra", choices=["tiny_decode", "million_decode", "ragged_decode",
                                         "chunked_prefill", "write_path", "block_sizes", "moe"],
                     help="run only this secondary workload (for profiling) and print its line")
@@ -428,6 +442,8 @@ def main():
     import torch
     from dsa_synth import workload
 
+    global KV_LAYOUT
+    KV_LAYOUT = LAYOUT_NAMES.index(args.kv_layout)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.extra:
@@ -500,7 +516,8 @@ def main():
         "config": {"workload": w.name, "batch": w.num_queries, "context_tokens": 32768,
                    "block_size": 64, "q_heads": 64, "kv_heads": 8, "head_dim": 128,
                    "idx_heads": 8, "idx_dim": 128, "top_k": w.top_k,
-                   "query_sets": args.query_sets, "entry": "dsa_sparse_decode_fused",
+                   "query_sets": args.query_sets, "kv_layout": args.kv_layout,
+                   "entry": "dsa_sparse_decode_fused",
                    "launch": "eager" if args.no_graph else "hip_graph_replay"},
         "hbm_gbps": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -522,6 +539,9 @@ def main():
                                 ("ragged_decode", workload.ragged_decode, 20)):
             log(f"extra: {name}")
             extras[name] = decode_extra(fn(), steps, 4 if name != "tiny_decode" else 8)
+        other = 1 - KV_LAYOUT
+        log(f"extra: batched decode, {LAYOUT_NAMES[other]} cache")
+        extras["batched_decode_" + LAYOUT_NAMES[other]] = decode_extra(w, 50, 8, kv_layout=other)
         log("extra: chunked_prefill indexer")
         extras["chunked_prefill"] = prefill_indexer_extra(5)
         log("extra: write path")

@@ -20,7 +20,7 @@ from . import _lib
 
 __all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
            "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "index_topk",
-           "workspace_size", "make_workspace", "abi_version", "check_inputs",
+           "workspace_size", "make_workspace", "KV_TOKEN_MAJOR", "KV_HEAD_MAJOR", "abi_version", "check_inputs",
            "kv_write", "index_key_write"]
 
 
@@ -30,37 +30,46 @@ class DSAError(RuntimeError):
         self.status = status
 
 
+KV_TOKEN_MAJOR = 0  # [P, bs, Hkv, 128]: the pages' [block][token][head][dim]
+KV_HEAD_MAJOR = 1   # [P, Hkv, bs, 128]: one contiguous run per (block, head)
+
+
 @dataclass
 class PagedKV:
-    k_cache: torch.Tensor      # bf16 [P, bs, Hkv, 128], bs = 64, 128, 256 or 512
-    v_cache: torch.Tensor      # bf16 [P, bs, Hkv, 128]
+    k_cache: torch.Tensor      # bf16 [P, bs, Hkv, 128] (token-major) or [P, Hkv, bs, 128] (head-major)
+    v_cache: torch.Tensor      # bf16, same shape and layout as k_cache
     idx_keys: torch.Tensor     # uint8 (E4M3 codes) [P, dI]
     idx_scale: torch.Tensor    # f32 [P]
     block_table: torch.Tensor  # int32 [B, max_blocks]
     seq_lens: torch.Tensor     # int32 [B]
     block_size: Optional[int] = None  # tokens per block when k_cache is None (default 64)
+    kv_layout: int = KV_TOKEN_MAJOR   # KV_TOKEN_MAJOR or KV_HEAD_MAJOR (order inside a block)
 
     @property
     def tokens_per_block(self):
         if self.k_cache is None:
             return 64 if self.block_size is None else int(self.block_size)
-        bs = int(self.k_cache.shape[1])
+        bs = int(self.k_cache.shape[2 if self.kv_layout == KV_HEAD_MAJOR else 1])
         if self.block_size is not None and int(self.block_size) != bs:
-            raise ValueError(f"block_size {self.block_size} != k_cache.shape[1] {bs}")
+            raise ValueError(f"block_size {self.block_size} != the cache's {bs} tokens per block")
         return bs
+
+    @property
+    def kv_heads(self):
+        if self.k_cache is None:
+            return 1
+        return int(self.k_cache.shape[1 if self.kv_layout == KV_HEAD_MAJOR else 2])
 
     def struct(self):
         def ptr(t):
             return t.data_ptr() if t is not None else None
         k = self.k_cache
-        P, bs, hkv, d = (k.shape if k is not None else
-                         (self.idx_keys.shape[0], self.tokens_per_block, 1, 128))
-        bs = self.tokens_per_block
+        P, d = (k.shape[0], k.shape[3]) if k is not None else (self.idx_keys.shape[0], 128)
         return _lib.PagedKVStruct(
             ptr(self.k_cache), ptr(self.v_cache), ptr(self.idx_keys), ptr(self.idx_scale),
-            ptr(self.block_table), ptr(self.seq_lens), P, bs, hkv, d,
+            ptr(self.block_table), ptr(self.seq_lens), P, self.tokens_per_block, self.kv_heads, d,
             self.idx_keys.shape[1] if self.idx_keys is not None else 0,
-            self.block_table.shape[0], self.block_table.shape[1])
+            self.block_table.shape[0], self.block_table.shape[1], int(self.kv_layout))
 
 
 @dataclass
@@ -293,7 +302,7 @@ def _check_struct(kv):
                   kv.idx_keys.shape[0] if kv.idx_keys is not None else 1)
     return _lib.PagedKVStruct(None, None, None, None, kv.block_table.data_ptr(),
                               kv.seq_lens.data_ptr(), num_blocks, kv.tokens_per_block, 1, 128, 64,
-                              kv.block_table.shape[0], kv.block_table.shape[1])
+                              kv.block_table.shape[0], kv.block_table.shape[1], 0)
 
 
 def kv_write(kv, k_new, v_new, tok_seq=None, tok_pos=None):

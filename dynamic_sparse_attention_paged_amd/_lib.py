@@ -40,6 +40,7 @@ class PagedKVStruct(ctypes.Structure):
         ("idx_dim", ctypes.c_int32),
         ("num_seqs", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 

@@ -215,8 +215,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint16_t* vs = vs_a[wave];
-  const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
-  const size_t tile_elems = (size_t)kBlockSize * tok_stride;
+  const size_t tok_stride = kv_tok_stride(kv);
   const uint32_t v_off = dma_v_lane_offset(tok_stride, lane);
   const uint32_t k_off = (uint32_t)(((size_t)r * tok_stride + 8 * gq) * 2);
 
@@ -238,7 +237,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       for (int i = 0; i < cn; ++i) {
         const int j = __builtin_amdgcn_readlane(my_j, i);
         const int p = __builtin_amdgcn_readlane(my_p, i);
-        const size_t base = (size_t)p * tile_elems + (size_t)g * kHeadDim;
+        const size_t base = kv_tile_base(kv, p, g);
         // previous block's LDS reads are complete before the DMA overwrites vs
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       i16x8 ka[4][4], kb[4][4];
       auto base_of = [&](int t) {
         const int p = __builtin_amdgcn_readlane(my_p, t);
-        return (size_t)p * tile_elems + (size_t)g * kHeadDim;
+        return kv_tile_base(kv, p, g);
       };
       auto pin_order = [] {
         asm volatile("" ::: "memory");

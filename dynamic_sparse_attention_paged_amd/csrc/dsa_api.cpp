@@ -41,6 +41,9 @@ int tiles_of(const dsa_paged_kv* kv, int top_k) { return top_k << (log2_block(kv
 
 // Token positions and 64-token tile ids of the pool are 32-bit in the kernels.
 dsa_status check_extent(const dsa_paged_kv* kv) {
+  if (kv->kv_layout != DSA_KV_TOKEN_MAJOR && kv->kv_layout != DSA_KV_HEAD_MAJOR)
+    return fail(DSA_ERR_UNSUPPORTED, "kv_layout %d: supported 0 (token-major), 1 (head-major)",
+                kv->kv_layout);
   if ((long long)kv->max_blocks_per_seq * kv->block_size > INT32_MAX ||
       (long long)kv->num_blocks * kv->block_size > INT32_MAX * 64LL)
     return fail(DSA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size (or the pool's 64-token tiles) "
@@ -113,6 +116,7 @@ dsa::KvView kv_view(const dsa_paged_kv* kv) {
   v.num_seqs = kv->num_seqs;
   v.maxb = kv->max_blocks_per_seq;
   v.bs_shift = log2_block(kv->block_size);
+  v.head_major = kv->kv_layout == DSA_KV_HEAD_MAJOR;
   return v;
 }
 

@@ -15,7 +15,7 @@ constexpr int kMaxIdxHeads = 16;
 constexpr int kMaxTopK = 4096;
 
 struct KvView {
-  const uint16_t* k;        // bf16 [P, block size, Hkv, 128]
+  const uint16_t* k;        // bf16 [P, block size, Hkv, 128] or [P, Hkv, block size, 128]
   const uint16_t* v;
   const uint8_t* idx_keys;  // [P, dI]
   const float* idx_scale;   // [P]
@@ -23,7 +23,22 @@ struct KvView {
   const int32_t* seq_lens;  // [B]
   int num_blocks, num_kv_heads, idx_dim, num_seqs, maxb;
   int bs_shift;             // log2(tokens per block): 6, 7, 8 or 9
+  int head_major;           // 0: [P, bs, Hkv, 128]; 1: [P, Hkv, bs, 128]
 };
+
+// Elements between consecutive tokens of one KV head.
+__host__ __device__ inline size_t kv_tok_stride(const KvView& kv) {
+  return kv.head_major ? (size_t)kHeadDim : (size_t)kv.num_kv_heads * kHeadDim;
+}
+
+// Element offset of token 0 of 64-token pool tile `tile` (physical block
+// tile >> (bs_shift - 6), tile within it tile & (2^(bs_shift - 6) - 1)), KV head g.
+__host__ __device__ inline size_t kv_tile_base(const KvView& kv, int tile, int g) {
+  if (!kv.head_major) return ((size_t)tile * 64 * kv.num_kv_heads + g) * kHeadDim;
+  const int ts = kv.bs_shift - 6;
+  const size_t blk = (size_t)(tile >> ts), t = (size_t)(tile & ((1 << ts) - 1));
+  return ((((blk * kv.num_kv_heads + g) << kv.bs_shift) + t * 64) * kHeadDim);
+}
 
 struct QView {
   int nq, hq, hi;

@@ -168,8 +168,8 @@ __global__ __launch_bounds__(kInvThreads) void inv_attend(
   const int r = lane & 15, gq = lane >> 4;
   const int G = Q.hq / kv.num_kv_heads;
   const int e0 = offset[tile_id], e1 = offset[tile_id + 1];
-  const size_t tok_stride = (size_t)kv.num_kv_heads * kHeadDim;
-  const size_t base = (size_t)tile_id * kBlockSize * tok_stride + (size_t)g * kHeadDim;
+  const size_t tok_stride = kv_tok_stride(kv);
+  const size_t base = kv_tile_base(kv, tile_id, g);
 
   // V: wave w brings token rows 16 w .. 16 w + 15 into LDS; K: every wave
   // holds the whole tile in registers for all of its query tiles.

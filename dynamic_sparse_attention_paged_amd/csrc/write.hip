@@ -24,7 +24,8 @@ namespace {
 
 constexpr int kWriteThreads = 256;
 
-// One thread per 16 B of a token's K or V row (num_kv_heads * 128 bf16).
+// One thread per 16 B of a token's K or V row (num_kv_heads * 128 bf16); the
+// chunk c of head c / 16 lands at its place in either block order.
 __global__ __launch_bounds__(kWriteThreads) void kv_write_rows(
     KvView kv, int n, const int32_t* __restrict__ tok_seq, const int32_t* __restrict__ tok_pos,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint4* __restrict__ k_out,
@@ -42,9 +43,13 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_rows(
     if (pos < 0 || (pos >> kv.bs_shift) >= kv.maxb) continue;
     const int p = kv.table[(size_t)s * kv.maxb + (pos >> kv.bs_shift)];
     if (p < 0 || p >= kv.num_blocks) continue;
-    const size_t row = ((size_t)p << kv.bs_shift) + (pos & ((1 << kv.bs_shift) - 1));
+    const size_t t = (size_t)(pos & ((1 << kv.bs_shift) - 1));
+    const size_t dst =
+        kv.head_major
+            ? ((((size_t)p * kv.num_kv_heads + c / 16) << kv.bs_shift) + t) * 16 + (c & 15)
+            : (((size_t)p << kv.bs_shift) + t) * chunks + c;
     const uint4 val = (is_v ? v_new : k_new)[(size_t)i * chunks + c];
-    (is_v ? v_out : k_out)[row * chunks + c] = val;
+    (is_v ? v_out : k_out)[dst] = val;
   }
 }
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -67,10 +67,22 @@ typedef enum {
  * starting from 256 or 512 tokens ([P2] section 2.1, note).  Any of 64, 128,
  * 256, 512 is accepted at run time; max_blocks_per_seq * block_size and
  * num_blocks * block_size / 64 must stay below 2^31 (DSA_ERR_UNSUPPORTED).
+ *
+ * Order inside a physical block (kv_layout): DSA_KV_TOKEN_MAJOR is the
+ * pages' [token_in_block][head][dim] order, where one head's 256 B row of a
+ * token sits num_kv_heads * 256 B from the next token's; DSA_KV_HEAD_MAJOR
+ * stores [head][token_in_block][dim], so each (block, head) is one
+ * contiguous block_size * 256 B run.  Both hold the same values, and every
+ * entry point that reads or writes k_cache / v_cache takes either; any other
+ * value is DSA_ERR_UNSUPPORTED there.
  */
+typedef enum { DSA_KV_TOKEN_MAJOR = 0, DSA_KV_HEAD_MAJOR = 1 } dsa_kv_layout;
+
 typedef struct {
-  const void* k_cache;         /* bf16 [num_blocks, block_size, num_kv_heads, head_dim], 16 B aligned */
-  const void* v_cache;         /* bf16, same shape as k_cache, 16 B aligned                           */
+  const void* k_cache;         /* bf16 [num_blocks, block_size, num_kv_heads, head_dim] (token-major)
+                                  or [num_blocks, num_kv_heads, block_size, head_dim] (head-major),
+                                  16 B aligned                                                         */
+  const void* v_cache;         /* bf16, same shape and layout as k_cache, 16 B aligned                */
   const uint8_t* idx_keys;     /* E4M3 (OCP, bias 7, max 448) codes [num_blocks, idx_dim], 16 B aligned */
   const float* idx_scale;      /* fp32 [num_blocks], > 0: key value = scale * E4M3 value              */
   const int32_t* block_table;  /* int32 [num_seqs, max_blocks_per_seq]: logical -> physical block    */
@@ -82,6 +94,7 @@ typedef struct {
   int32_t idx_dim;             /* coarse key length: 64 or 128                                       */
   int32_t num_seqs;            /* >= 1                                                               */
   int32_t max_blocks_per_seq;  /* row length of block_table, >= 1                                    */
+  int32_t kv_layout;           /* dsa_kv_layout of k_cache and v_cache                               */
 } dsa_paged_kv;
 
 /*

@@ -15,14 +15,18 @@ REL_FLOOR = 0.2
 NEAR_TIE_REL = 1e-6    # allowed index swaps: oracle scores within this relative gap
 
 
-def to_device(w, device="cuda"):
-    """PagedKV / Queries on the device (pools filled by the device filler)."""
+def to_device(w, device="cuda", kv_layout=0):
+    """PagedKV / Queries on the device (pools filled by the device filler).
+    kv_layout 1 stores the same pool values head-major, [P, Hkv, bs, 128]."""
     import dynamic_sparse_attention_paged_amd as dsa
     from dsa_synth import device as synth_dev
 
     t = synth_dev.upload(w, device)
+    if kv_layout == dsa.KV_HEAD_MAJOR:
+        for name in ("k_cache", "v_cache"):
+            t[name] = t[name].permute(0, 2, 1, 3).contiguous()
     kv = dsa.PagedKV(t["k_cache"], t["v_cache"], t["idx_keys"], t["idx_scale"],
-                     t["block_table"], t["seq_lens"])
+                     t["block_table"], t["seq_lens"], kv_layout=kv_layout)
     qs = dsa.Queries(t["q"], t["q_idx"], t["w_idx"], t["q_seq"], t["q_pos"])
     return kv, qs
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
 
 
 FAKE = 0x10000  # a 64 KiB-aligned non-NULL address: never dereferenced on the host
@@ -84,6 +84,9 @@ def test_validation_errors(lib):
     assert _attn(lib, _kv(), _qs(), top_k=0) == E["DSA_ERR_SHAPE"]
     assert _attn(lib, _kv(), _qs(), top_k=5000) == E["DSA_ERR_SHAPE"]
     assert _attn(lib, _kv(k_cache=FAKE + 2), _qs()) == E["DSA_ERR_ALIGN"]
+    for layout in (-1, 2):  # only token-major (0) and head-major (1) blocks
+        assert _attn(lib, _kv(kv_layout=layout), _qs()) == E["DSA_ERR_UNSUPPORTED"]
+        assert _score(lib, _kv(kv_layout=layout), _qs()) == E["DSA_ERR_UNSUPPORTED"]
     assert _attn(lib, _kv(), _qs(), out=None) == E["DSA_ERR_NULL"]
     assert lib.dsa_sparse_attn_prefill(ctypes.byref(_kv()), ctypes.byref(_qs()), FAKE, FAKE, 4,
                                        0.1, FAKE, None, None) == E["DSA_ERR_NULL"]  # q_seq/q_pos

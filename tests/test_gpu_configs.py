@@ -49,8 +49,8 @@ def _check(w, qis, idx, cnt, out, lse, label):
          f"max-rel {worst[1]:.2e}")
 
 
-def _fused(dsa, w):
-    kv, qs = parity.to_device(w)
+def _fused(dsa, w, kv_layout=0):
+    kv, qs = parity.to_device(w, kv_layout=kv_layout)
     nq, K = w.num_queries, w.top_k
     bi = torch.empty(nq, K, dtype=torch.int32, device="cuda")
     bc = torch.empty(nq, dtype=torch.int32, device="cuda")
@@ -79,10 +79,11 @@ def test_topk_variants_long_lists(dsa, lens, top_k):
     assert np.array_equal(bi.cpu().numpy(), idx) and np.array_equal(bc.cpu().numpy(), cnt)
 
 
-def test_batched_decode_full(dsa):
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
+def test_batched_decode_full(dsa, kv_layout):
     w = workload.batched_decode()
-    _say("batched decode 32 x 32768, all queries")
-    idx, cnt, out, lse = _fused(dsa, w)
+    _say(f"batched decode 32 x 32768, all queries, kv_layout {kv_layout}")
+    idx, cnt, out, lse = _fused(dsa, w, kv_layout)
     _check(w, range(w.num_queries), idx, cnt, out, lse, "batched_decode")
 
 

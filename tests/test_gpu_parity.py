@@ -44,8 +44,8 @@ SMALL_DECODE_CASES = [
 ]
 
 
-def _run_all_stages(dsa, w, label):
-    kv, qs = parity.to_device(w)
+def _run_all_stages(dsa, w, label, kv_layout=0):
+    kv, qs = parity.to_device(w, kv_layout=kv_layout)
     maxb = w.block_table.shape[1]
     K = w.top_k
     scores = dsa.index_score(kv, qs)
@@ -89,11 +89,12 @@ def _run_all_stages(dsa, w, label):
     return kv, qs, refs
 
 
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
 @pytest.mark.parametrize("case", SMALL_DECODE_CASES, ids=[str(c["seed"]) for c in SMALL_DECODE_CASES])
-def test_small_decode_stages(dsa, case):
+def test_small_decode_stages(dsa, case, kv_layout):
     w = workload.small_decode(**case)
-    _say(f"small_decode {case}")
-    kv, qs, refs = _run_all_stages(dsa, w, f"small_decode[{case['seed']}]")
+    _say(f"small_decode {case} kv_layout {kv_layout}")
+    kv, qs, refs = _run_all_stages(dsa, w, f"small_decode[{case['seed']}]", kv_layout)
     # fused entry point: same results
     K = w.top_k
     bi = torch.empty(w.num_queries, K, dtype=torch.int32, device="cuda")
@@ -141,10 +142,11 @@ def test_tiny_sweep_stages(dsa, nb, top_k):
 @pytest.mark.parametrize("seed,count,L,top_k", [(2101, 200, 64 * 20 - 5, 6),
                                                 (2102, 130, 64 * 3 + 1, 2),
                                                 (2103, 257, 64 * 40, 64)])
-def test_small_prefill_stages(dsa, seed, count, L, top_k):
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
+def test_small_prefill_stages(dsa, seed, count, L, top_k, kv_layout):
     w = workload.small_prefill(seed=seed, count=count, L=L, top_k=top_k)
-    _say(f"small_prefill seed={seed} count={count} L={L} K={top_k}")
-    _run_all_stages(dsa, w, f"small_prefill[{seed}]")
+    _say(f"small_prefill seed={seed} count={count} L={L} K={top_k} kv_layout {kv_layout}")
+    _run_all_stages(dsa, w, f"small_prefill[{seed}]", kv_layout)
 
 
 # Batches of 256+ prefill queries of one sequence are scored on the int8

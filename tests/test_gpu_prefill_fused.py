@@ -32,8 +32,8 @@ def dsa():
     return m
 
 
-def _run(dsa, w, label):
-    kv, qs = parity.to_device(w)
+def _run(dsa, w, label, kv_layout=0):
+    kv, qs = parity.to_device(w, kv_layout=kv_layout)
     K = w.top_k
     bi = torch.empty(w.num_queries, K, dtype=torch.int32, device="cuda")
     bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
@@ -66,11 +66,12 @@ def test_prefill_fused_head_groups(dsa, hq, hkv):
     _run(dsa, w, f"prefill_fused hq{hq} hkv{hkv}")
 
 
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
 @pytest.mark.parametrize("bs", [64, 128, 256, 512])
-def test_prefill_fused_block_sizes(dsa, bs):
+def test_prefill_fused_block_sizes(dsa, bs, kv_layout):
     w = workload.small_prefill(seed=2820 + bs, L=bs * 11 + 37, count=80, hq=16, hkv=2, hi=8,
                                di=64, top_k=4, bs=bs)
-    _run(dsa, w, f"prefill_fused bs{bs}")
+    _run(dsa, w, f"prefill_fused bs{bs} kv_layout {kv_layout}", kv_layout)
 
 
 def test_prefill_fused_many_queries_int8_scorer(dsa):

@@ -76,6 +76,36 @@ def test_kv_write_matches_oracle(dsa):
     assert np.array_equal(_bits(kd), want_k)
 
 
+@pytest.mark.parametrize("bs", [64, 256])
+def test_kv_write_head_major_matches_oracle(dsa, bs):
+    """The same writes into a head-major pool ([P, Hkv, bs, 128]) land where
+    the oracle's token-major result, transposed, puts them."""
+    rng = np.random.default_rng(12 + bs)
+    P, H = 9, 3
+    table = np.array([[3, 7, 1], [0, 4, 8], [5, 6, 2]], dtype=np.int32)
+    seq_lens = np.array([bs * 2 + 5, bs * 3, 17], dtype=np.int32)
+    k_pool = rng.integers(0, 1 << 16, size=(P, bs, H, 128), dtype=np.uint16)
+    v_pool = rng.integers(0, 1 << 16, size=(P, bs, H, 128), dtype=np.uint16)
+    hm = lambda a: np.ascontiguousarray(a.transpose(0, 2, 1, 3))
+    for tok_seq, tok_pos, n in ((None, None, 3),
+                                (np.array([0, 1, 1, 2, 0], np.int32),
+                                 np.array([0, bs - 1, bs * 3 - 1, 16, bs + 3], np.int32), 5)):
+        kd = _dev(hm(k_pool).view(np.int16), torch.bfloat16)
+        vd = _dev(hm(v_pool).view(np.int16), torch.bfloat16)
+        kv = dsa.PagedKV(kd, vd, None, None, _dev(table), _dev(seq_lens),
+                         kv_layout=dsa.KV_HEAD_MAJOR)
+        assert kv.tokens_per_block == bs and kv.kv_heads == H
+        k_new = rng.integers(0, 1 << 16, size=(n, H, 128), dtype=np.uint16)
+        v_new = rng.integers(0, 1 << 16, size=(n, H, 128), dtype=np.uint16)
+        dsa.kv_write(kv, _dev(k_new.view(np.int16), torch.bfloat16),
+                     _dev(v_new.view(np.int16), torch.bfloat16),
+                     None if tok_seq is None else _dev(tok_seq),
+                     None if tok_pos is None else _dev(tok_pos))
+        torch.cuda.synchronize()
+        want_k, want_v = kv_write(k_pool, v_pool, table, seq_lens, tok_seq, tok_pos, k_new, v_new, bs)
+        assert np.array_equal(_bits(kd), hm(want_k)) and np.array_equal(_bits(vd), hm(want_v)), n
+
+
 @pytest.mark.parametrize("di", [64, 128])
 def test_index_key_write_matches_oracle(dsa, di):
     rng = np.random.default_rng(12 + di)
