@@ -10,10 +10,14 @@ timed region.  Distinct query batches rotate over the same cache so that
 consecutive steps select different blocks (the 256 MiB last-level cache
 cannot serve a step from the previous one).
 
-Printed: one JSON line with queries/s, the roofline of the dominant kernel
-(sparse attention: HBM bytes per launch / its HIP-event duration), and the
-oracle timed on the host on a bounded sample.  Extra fields report the other
-workloads (tiny, ragged, million-token decode; the chunked-prefill indexer).
+Printed: one JSON line with queries/s (K back-to-back steps between two
+synchronizations), per-step HIP-event times (median, p10, p90; back to back
+and after a 1 GiB cache flush), the roofline of the step (algorithmic bytes
+over its event time, against the 8 TB/s spec and the streaming-read ceiling
+measured in the same run), and the oracle timed on the host's cores on a
+bounded sample.  Extra fields report the other workloads (tiny, ragged,
+million-token decode; the chunked-prefill indexer) with their own rooflines,
+and the chip's measured ceilings.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -34,6 +38,8 @@ METRIC = "decode queries/sec + achieved HBM GB/s (% roofline); prefill indexer M
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 INT8_PEAK_TOPS = 5000.0
+# what one fused step of the batched decode launches (the roofline's scope)
+STEP_KERNELS = "index_score_exact + sparse_attn_split (selects its blocks)"
 # the decode attention kernel's sources (the traffic counters are keyed to them)
 ATTN_SRCS = [os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", f)
              for f in ("attn.hip", "attn_tile.h")]
@@ -160,7 +166,7 @@ class Device:
 
 
 def event_time_ms(fn, n, warmup):
-    """Average HIP-event time (ms) of fn(i) over n calls on the current stream."""
+    """Average HIP-event time (ms) of fn(i) over n back-to-back calls on the current stream."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -173,6 +179,55 @@ def event_time_ms(fn, n, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
+
+
+class Flusher:
+    """Writes a 1 GiB scratch buffer (dsa_cache_flush), more than the L2s and the
+    256 MiB last-level cache hold, so that the next step finds none of its
+    inputs cached."""
+
+    def __init__(self, nbytes=1 << 30):
+        import torch
+        from dynamic_sparse_attention_paged_amd import _lib
+        self.lib = _lib.load()
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        import torch
+        self.n += 1
+        rc = self.lib.dsa_cache_flush(self.buf.data_ptr(), self.buf.numel(), self.n,
+                                      torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, "dsa_cache_flush failed"
+
+
+def step_times_ms(fn, n, warmup, flush=None):
+    """Per-call HIP-event times (ms) of fn(i): every call bracketed by its own
+    pair of events on the current stream; with `flush`, an untimed cache flush
+    runs on the same stream before each call."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        if flush is not None:
+            flush()
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def dist(ts):
+    """median / p10 / p90 / mean of a list of times (ms)."""
+    import numpy as np
+    a = np.asarray(ts, dtype=np.float64)
+    return dict(median=round(float(np.median(a)), 5), p10=round(float(np.percentile(a, 10)), 5),
+                p90=round(float(np.percentile(a, 90)), 5), mean=round(float(a.mean()), 5),
+                n=int(a.size))
 
 
 # Order inside a cache block, by its dsa_kv_layout value.
@@ -194,24 +249,20 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle on the host: scoring + selection + attention for as many queries
-    of the batch as fit in ~budget_s (K/V generation excluded from the timing)."""
+def _oracle_decode_loop(w, budget_s, qseed0):
+    """The oracle on decode queries of w for ~budget_s of compute: scoring,
+    selection and attention timed, K/V regeneration (input generation) not.
+    Each pass over the batch takes fresh query seeds.  Returns (queries, s)."""
     import numpy as np
     from oracle import bf16_bits_to_f64, select_blocks, sparse_attention
     from oracle.pipeline import score_query
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover
-        limiter = None
     from dsa_synth import workload
     spent, done = 0.0, 0
     src = w
     for i in range(1 << 30):
         qi = i % w.num_queries
         if i and qi == 0:  # a fresh batch of queries over the same cache
-            src = workload.with_query_seed(w, 7000 + i // w.num_queries)
+            src = workload.with_query_seed(w, qseed0 + i // w.num_queries)
         s, pos = int(w.q_seq[qi]), int(w.q_pos[qi])
         L = int(w.seq_lens[s])
         qidx = bf16_bits_to_f64(src.q_idx_bits[qi])
@@ -232,36 +283,166 @@ def cpu_baseline(w, budget_s):
         done += 1
         if spent >= budget_s:
             break
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return dict(value=done / spent, unit="queries/s", cores=1, kind="oracle",
-                sample=f"{done} decode queries of {w.name} (batches of {w.num_queries} with "
-                       f"fresh query seeds; float64 NumPy, 1 thread; K/V regeneration not "
-                       f"timed)", seconds=round(spent, 2))
+    return done, spent
 
 
-def decode_extra(w, steps, nsets, kv_layout=None):
-    """q/s and HBM GB/s of a decode workload through the fused entry point."""
+def _oracle_worker(args):
+    w, budget_s, qseed0 = args
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _oracle_decode_loop(w, budget_s, qseed0)
+
+
+def host_cores():
+    """CPUs this process may run on (the GPU machine grants 16 per GPU)."""
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, budget_s, prefill_w=None):
+    """The oracle (float64 NumPy, as it stands) timed on the host's cores over a
+    bounded sample of the workload: one process per core, each running decode
+    queries of the batch for ~budget_s of compute (BLAS held to one thread per
+    process), queries/s summed; the same on one thread; and a sample of
+    chunked-prefill queries on one thread."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
+    procs = min(cores, 16)
+    with threadpool_limits(limits=1):
+        d1, s1 = _oracle_decode_loop(w, budget_s / 3, 7000)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        parts = pool.map(_oracle_worker, [(w, budget_s / 3, 9000 + 1000 * i) for i in range(procs)])
+    done = sum(p[0] for p in parts)
+    rate = sum(p[0] / p[1] for p in parts)
+    res = dict(value=round(rate, 2), unit="queries/s", cores=procs, kind="oracle",
+               sample=f"{done} decode queries of {w.name} in {procs} processes (one per core, "
+                      f"BLAS 1 thread each; batches of {w.num_queries} with fresh query seeds; "
+                      f"~{budget_s / 3:.0f} s of compute per process; K/V regeneration not "
+                      f"timed); float64 NumPy",
+               host_cpus=cores,
+               single_thread=dict(value=round(d1 / s1, 2), unit="queries/s", queries=d1,
+                                  seconds=round(s1, 2)))
+    if prefill_w is not None:
+        import numpy as np
+        from oracle import bf16_bits_to_f64, select_blocks, sparse_attention
+        from oracle.pipeline import score_query
+        pw = prefill_w
+        spent, done = 0.0, 0
+        qis = np.linspace(0, pw.num_queries - 1, 64).astype(int)
+        with threadpool_limits(limits=1):
+            for qi in qis:
+                s, pos = int(pw.q_seq[qi]), int(pw.q_pos[qi])
+                L = int(pw.seq_lens[s])
+                t0 = time.perf_counter()
+                cand, sc, loc = score_query(bf16_bits_to_f64(pw.q_idx_bits[qi]), pw.w[qi],
+                                            pw.block_table[s], pos, L, pw.block_size,
+                                            pw.idx_keys, pw.idx_scale)
+                idx, cnt = select_blocks(cand, sc.astype(np.float32), loc, pw.top_k)
+                t1 = time.perf_counter()
+                blk = {int(pw.block_table[s][j]): (bf16_bits_to_f64(pw.k_block_bits(int(pw.block_table[s][j]))),
+                                                   bf16_bits_to_f64(pw.v_block_bits(int(pw.block_table[s][j]))))
+                       for j in idx[:cnt]}
+                t2 = time.perf_counter()
+                sparse_attention(bf16_bits_to_f64(pw.q_bits[qi]), idx[:cnt], pw.block_table[s],
+                                 pos, L, pw.block_size, lambda p: blk[p][0], lambda p: blk[p][1],
+                                 pw.softmax_scale, pw.num_kv_heads)
+                t3 = time.perf_counter()
+                spent += (t1 - t0) + (t3 - t2)
+                done += 1
+                if spent >= budget_s / 3:
+                    break
+        res["prefill_single_thread"] = dict(
+            value=round(done / spent, 2), unit="queries/s", queries=done, seconds=round(spent, 2),
+            sample=f"{done} queries spread over the {pw.num_queries}-query chunk of {pw.name}")
+    return res
+
+
+def hbm_roofline(nbytes, ms, kernel, scope, ceil_gbps=None, traffic=None):
+    """Roofline object for an HBM-bound launch sequence: algorithmic bytes per
+    step over the step's HIP-event time."""
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    r = {"kernel": kernel, "scope": scope, "bound": "hbm", "achieved": round(gbps, 1),
+         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+         "traffic": traffic, "bytes_per_launch": int(nbytes), "avg_launch_ms": round(ms, 5)}
+    if ceil_gbps:
+        r["measured_ceiling"] = round(ceil_gbps, 1)
+        r["frac_of_measured_ceiling"] = round(gbps / ceil_gbps, 4)
+    return r
+
+
+def decode_extra(w, steps, nsets, kv_layout=None, ceil_gbps=None):
+    """q/s and HBM GB/s of a decode workload through the fused entry point:
+    per-step HIP-event times (median, p10, p90), back to back and after a cache
+    flush, the roofline of the whole step against its algorithmic bytes, and
+    the attention kernel alone on the same selection."""
     import torch
     D = Device(w, nsets, kv_layout=kv_layout)
     D.capture()
-    ms = event_time_ms(D.replay, steps, 3)
+    b2b = step_times_ms(D.replay, steps, 3)
+    fl = step_times_ms(D.replay, max(5, steps // 2), 1, flush=Flusher())
     D.select()
     torch.cuda.synchronize()
-    attn_ms = event_time_ms(D.attn, steps, 3)
+    attn = step_times_ms(D.attn, steps, 3)
     cnt = D.cnt[0].cpu().numpy()
-    byts = attn_bytes(w, cnt) + index_bytes(w)
+    a_bytes = attn_bytes(w, cnt)
+    byts = a_bytes + index_bytes(w)
+    ms = dist(b2b)["mean"]
     res = dict(workload=w.name, kv_layout=LAYOUT_NAMES[D.kv_layout], queries=w.num_queries,
-               ms_per_step=round(ms, 5),
+               ms_per_step=ms, step_ms=dist(b2b), step_ms_flushed=dist(fl),
                queries_per_s=round(w.num_queries / (ms * 1e-3), 1),
-               path_gbps=round(byts / (ms * 1e-3) / 1e9, 1),
-               path_frac_of_hbm=round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-               attn_kernel_ms=round(attn_ms, 5),
-               attn_kernel_gbps=round(attn_bytes(w, cnt) / (attn_ms * 1e-3) / 1e9, 1),
-               attn_kernel_frac_of_hbm=round(attn_bytes(w, cnt) / (attn_ms * 1e-3) / 1e9 /
-                                             HBM_PEAK_GBPS, 4))
+               roofline=hbm_roofline(byts, ms, "dsa_sparse_decode_fused (every launch of the step)",
+                                     "step", ceil_gbps),
+               attention_kernel=hbm_roofline(a_bytes, dist(attn)["mean"],
+                                             "sparse_attn_split (given lists)", "kernel",
+                                             ceil_gbps))
+    res["attention_kernel"]["step_ms"] = dist(attn)
     del D
     torch.cuda.empty_cache()
+    return res
+
+
+def ceilings_extra(quick=False):
+    """What the chip sustains, from the library's support probes: a streaming
+    read of 4 GiB (plain and non-temporal loads, several grid sizes) and
+    back-to-back MFMAs (FP8 scaled 16x16x128, int8 16x16x64, bf16 16x16x32)."""
+    import torch
+    from dynamic_sparse_attention_paged_amd import _lib
+    lib = _lib.load()
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(16384 * 256, dtype=torch.int32, device="cuda")
+    rows = []
+    grids = (512, 1024) if quick else (256, 512, 768, 1024, 2048, 8192)
+    for var in (0, 1):
+        for grid in grids:
+            def f(i, var=var, grid=grid):
+                assert lib.dsa_probe_stream_read(buf.data_ptr(), nbytes, var, sink.data_ptr(), grid,
+                                                 st) == 0
+            ts = step_times_ms(f, 6, 2)
+            med = dist(ts)["median"]
+            rows.append(dict(loads="nt" if var else "plain", grid=grid, ms=med,
+                             gbps=round(nbytes / (med * 1e-3) / 1e9, 1)))
+    del buf
+    torch.cuda.empty_cache()
+    best = max(rows, key=lambda r: r["gbps"])
+    res = dict(stream_read=rows, stream_read_best_gbps=best["gbps"],
+               stream_read_best_frac_of_spec=round(best["gbps"] / HBM_PEAK_GBPS, 4))
+    if not quick:
+        sinkf = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+        mf = {}
+        for kind, name, fl, peak in ((0, "fp8_16x16x128", 65536, FP8_PEAK_TFLOPS),
+                                     (1, "i8_16x16x64", 32768, INT8_PEAK_TOPS),
+                                     (2, "bf16_16x16x32", 16384, 2500.0)):
+            grid, iters = 1024, 2000
+
+            def f(i, kind=kind):
+                assert lib.dsa_probe_mfma_rate(kind, iters, grid, sinkf.data_ptr(), st) == 0
+            med = dist(step_times_ms(f, 4, 1))["median"]
+            tf = grid * 4 * iters * 8 * fl / (med * 1e-3) / 1e12
+            mf[name] = dict(tflops=round(tf, 1), frac_of_spec=round(tf / peak, 4))
+        res["mfma"] = mf
     return res
 
 
@@ -380,7 +561,8 @@ def prefill_indexer_extra(steps):
     from dsa_synth import workload
     w = workload.chunked_prefill()
     D = Device(w, 1)
-    ms = event_time_ms(D.score, steps, 2)
+    sc_t = step_times_ms(D.score, steps, 2)
+    ms = dist(sc_t)["mean"]
     fl = index_flops(w)
     tk_ms = event_time_ms(D.topk, steps, 2)
     at_ms = event_time_ms(D.attn, max(2, steps // 4), 1)
@@ -394,7 +576,14 @@ def prefill_indexer_extra(steps):
                     "base-128 digit products (the FP8 MFMA accumulation is inexact on gfx950); "
                     "frac_of_fp8_mfma_peak counts the algorithmic FP8 flops, "
                     "frac_of_int8_mfma_peak the digit products issued for them",
-               topk_ms=round(tk_ms, 4), attention_ms=round(at_ms, 3))
+               topk_ms=round(tk_ms, 4), attention_ms=round(at_ms, 3),
+               score_kernel_step_ms=dist(sc_t),
+               roofline={"kernel": "index_score_i8 (dsa_index_score)", "scope": "kernel",
+                         "bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 2),
+                         "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                         "traffic": None, "flops_per_launch": int(fl),
+                         "avg_launch_ms": round(ms, 5)})
     # the one-call prefill: scoring, selection and the block-inverted attention
     from dynamic_sparse_attention_paged_amd import _lib
     ws = D.dsa.make_workspace(_lib.OP_PREFILL_FUSED, D.kv, D.sets[0], w.top_k)
@@ -419,7 +608,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--query-sets", type=int, default=8)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -430,7 +619,8 @@ def main():
                     help="order inside a cache block: [head][token][dim] or the pages' "
                          "[token][head][dim] (the other one is timed as an extra)")
     ap.add_argument("--extra", choices=["tiny_decode", "million_decode", "ragged_decode",
-                                        "chunked_prefill", "write_path", "block_sizes", "moe"],
+                                        "chunked_prefill", "write_path", "block_sizes", "moe",
+                                        "ceilings"],
                     help="run only this secondary workload (for profiling) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -455,11 +645,16 @@ def main():
             res = block_size_extra(args.steps)
         elif args.extra == "moe":
             res = moe_extra(args.steps)
+        elif args.extra == "ceilings":
+            res = ceilings_extra()
         else:
             fn = getattr(workload, args.extra)
             res = decode_extra(fn(), args.steps, 4 if args.extra != "tiny_decode" else 8)
         print(json.dumps(res), flush=True)
         return
+    log("ceilings: streaming read")
+    ceil = ceilings_extra(quick=True)
+    ceil_gbps = ceil["stream_read_best_gbps"]
     w = workload.batched_decode()
     log(f"workload {w.name}: pool {w.num_blocks} blocks, {args.query_sets} query sets")
     D = Device(w, args.query_sets)
@@ -479,17 +674,20 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     log(f"fused step {ms_step * 1e3:.1f} us")
+    # the same steps, each bracketed by its own HIP events on the launch stream,
+    # back to back and after a 1 GiB cache flush
+    b2b = step_times_ms(step, args.steps, 2)
+    flushed = step_times_ms(step, args.steps, 2, flush=Flusher())
 
-    # dominant kernel (attention) on the same stream, HIP events over the loop
+    # the attention kernel alone on the step's selection, and the stages
     D.select()
     torch.cuda.synchronize()
-    attn_ms = event_time_ms(D.attn, args.steps, 3)
+    attn_t = step_times_ms(D.attn, args.steps, 3)
     score_ms = event_time_ms(D.score, args.steps, 3)
     topk_ms = event_time_ms(D.topk, args.steps, 3)
     cnt = D.cnt[0].cpu().numpy()
     a_bytes = attn_bytes(w, cnt)
     path_bytes = a_bytes + index_bytes(w)
-    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
     traffic = traffic_from_profile()
 
     if args.copy_probe:
@@ -500,6 +698,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    step_mean = dist(b2b)["mean"]
     result = {
         "metric": METRIC,
         "value": round(w.num_queries / (ms_step * 1e-3), 1),
@@ -521,14 +720,16 @@ def main():
                    "launch": "eager" if args.no_graph else "hip_graph_replay"},
         "hbm_gbps": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": "sparse_attn_split", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "bytes_per_launch": a_bytes,
-                     "avg_launch_ms": round(attn_ms, 5)},
+        "step_ms": dist(b2b),
+        "step_ms_flushed": dist(flushed),
+        "roofline": hbm_roofline(path_bytes, step_mean, STEP_KERNELS, "step", ceil_gbps, traffic),
+        "attention_kernel": hbm_roofline(a_bytes, dist(attn_t)["mean"],
+                                         "sparse_attn_split (given lists)", "kernel", ceil_gbps),
         "stages_ms": {"index_score": round(score_ms, 5), "topk": round(topk_ms, 5),
-                      "sparse_attn": round(attn_ms, 5)},
+                      "sparse_attn": dist(attn_t)["mean"]},
+        "ceilings": ceil,
     }
+    result["attention_kernel"]["step_ms"] = dist(attn_t)
     del D
     torch.cuda.empty_cache()
 
@@ -538,10 +739,12 @@ def main():
                                 ("million_decode", workload.million_decode, 50),
                                 ("ragged_decode", workload.ragged_decode, 20)):
             log(f"extra: {name}")
-            extras[name] = decode_extra(fn(), steps, 4 if name != "tiny_decode" else 8)
+            extras[name] = decode_extra(fn(), steps, 4 if name != "tiny_decode" else 8,
+                                        ceil_gbps=ceil_gbps)
         other = 1 - KV_LAYOUT
         log(f"extra: batched decode, {LAYOUT_NAMES[other]} cache")
-        extras["batched_decode_" + LAYOUT_NAMES[other]] = decode_extra(w, 50, 8, kv_layout=other)
+        extras["batched_decode_" + LAYOUT_NAMES[other]] = decode_extra(w, 50, 8, kv_layout=other,
+                                                                       ceil_gbps=ceil_gbps)
         log("extra: chunked_prefill indexer")
         extras["chunked_prefill"] = prefill_indexer_extra(5)
         log("extra: write path")
@@ -549,11 +752,14 @@ def main():
         extras["block_sizes"] = block_size_extra(20)
         log("extra: MXFP4 expert layer")
         extras["moe_mxfp4"] = moe_extra(10)
+        log("extra: ceilings (stream read, matrix cores)")
+        extras["ceilings"] = ceilings_extra()
         result["extras"] = extras
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
+                                              prefill_w=workload.chunked_prefill())
     print(json.dumps(result), flush=True)
 
 

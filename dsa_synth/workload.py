@@ -300,3 +300,19 @@ def with_query_seed(w, qseed):
     v.q_bits, v.q_idx_bits, v.w = q, qi, ww
     v.meta = dict(w.meta, query_seed=qseed)
     return v
+
+
+def with_q_scale(w, log2_factor):
+    """A copy of ``w`` whose attention queries are multiplied by 2^log2_factor
+    (exact in bf16 for these magnitudes).  Large factors make the softmax
+    peaked: the logits spread over hundreds of units and the weights become
+    nearly one-hot."""
+    import copy
+    f = gen.bf16_bits_to_f32(w.q_bits).astype(np.float32) * np.float32(2.0 ** log2_factor)
+    assert np.all(np.isfinite(f))
+    v = copy.copy(w)
+    v.q_bits = gen.f32_to_bf16_bits(f)
+    assert np.array_equal(gen.bf16_bits_to_f32(v.q_bits), f), "scaling must be exact"
+    v.name = f"{w.name}_qx{2 ** log2_factor}"
+    v.meta = dict(w.meta, q_log2_scale=log2_factor)
+    return v

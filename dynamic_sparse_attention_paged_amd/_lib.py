@@ -20,6 +20,10 @@ EXPORTS = ["dsa_index_score", "dsa_topk_blocks", "dsa_sparse_attn_decode",
            "dsa_workspace_size", "dsa_check_inputs", "dsa_kv_write", "dsa_index_key_write",
            "dsa_mx_quantize", "dsa_mxfp4_to_fp8", "dsa_moe_workspace_size", "dsa_moe_grouped_gemm",
            "dsa_status_str", "dsa_last_error", "dsa_abi_version"]
+# include/dsa_support.h: measurement support (ceilings, cache flush, FP8 MFMA probe)
+SUPPORT_EXPORTS = ["dsa_probe_stream_read", "dsa_cache_flush", "dsa_probe_mfma_rate",
+                   "dsa_probe_fp8_mfma", "dsa_support_last_error"]
+PROBE_MFMA_FP8, PROBE_MFMA_I8, PROBE_MFMA_BF16 = 0, 1, 2
 CHECK_FLAGS = {1: "seq_len", 2: "table", 4: "q_seq", 8: "q_pos", 16: "block_list"}
 MOE_FP8_WORKSPACE = 0
 MOE_FP4_DIRECT = 1
@@ -98,6 +102,10 @@ def load():
         "dsa_mxfp4_to_fp8": [mxp, vp, i32, vp, vp, vp],
         "dsa_moe_workspace_size": [mxp, i32, i32, i32, P(sz)],
         "dsa_moe_grouped_gemm": [mxp, vp, vp, i32, vp, i32, i32, vp, vp, sz, vp],
+        "dsa_probe_stream_read": [vp, sz, ctypes.c_int, vp, ctypes.c_int, vp],
+        "dsa_cache_flush": [vp, sz, ctypes.c_uint, vp],
+        "dsa_probe_mfma_rate": [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp],
+        "dsa_probe_fp8_mfma": [vp, vp, vp, ctypes.c_int, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -107,6 +115,8 @@ def load():
     lib.dsa_status_str.restype = ctypes.c_char_p
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_support_last_error.argtypes = []
+    lib.dsa_support_last_error.restype = ctypes.c_char_p
     lib.dsa_abi_version.argtypes = []
     lib.dsa_abi_version.restype = ctypes.c_int
     _lib = lib

@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <atomic>
+
 #include "attn_tile.h"
 #include "cand_common.h"
 #include "dsa_internal.h"
@@ -36,7 +38,6 @@
 namespace dsa {
 namespace {
 
-constexpr int kNumCUs = 256;   // MI355X
 constexpr int kMaxSelectBlocks = 2048;  // selection inside attention: up to 2048 blocks
 constexpr int kMaxScoredBlocks = 256;  // scoring inside attention: up to 256 blocks
 // where the attention kernel gets its blocks from (see sparse_attn_split)
@@ -64,7 +65,11 @@ using namespace tile;
 // With kAttnSelect / kAttnScore, workgroup (0, q, 0) also writes the
 // selection to idx_out / cnt_out when those are given.  DI and HP (index
 // key length, indexer heads rounded up to 4, 8 or 16) matter for kAttnScore only.
-template <int kAttnWaves, int kVBufs, int kMode, int DI, int HP>
+//
+// kNT: the K/V tiles are read with the non-temporal cache policy (decode: each
+// selected block is streamed once per call); prefill keeps plain loads, since
+// the blocks its queries select overlap and are served again from the caches.
+template <int kAttnWaves, int kVBufs, int kMode, int DI, int HP, bool kNT>
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
     KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     const float* __restrict__ scores, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
@@ -241,9 +246,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
         // previous block's LDS reads are complete before the DMA overwrites vs
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
-        dma_v(kv.v + base, tok_stride, v_off, vs);
+        dma_v<kNT>(kv.v + base, tok_stride, v_off, vs);
         i16x8 kf[4][4];
-        load_k(kv.k + base, tok_stride, k_off, kf);
+        load_k<kNT>(kv.k + base, tok_stride, k_off, kf);
         __builtin_amdgcn_s_waitcnt(0);  // V in LDS and K in registers
         __builtin_amdgcn_wave_barrier();
         attend_block(kf, qf, scale2, j * kBlockSize, lim, vs, st);
@@ -273,11 +278,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       __builtin_amdgcn_wave_barrier();
       auto prime = [&](uint16_t* __restrict__ v0) {
         const size_t b = base_of(0);
-        load_k(kv.k + b, tok_stride, k_off, ka);
+        load_k<kNT>(kv.k + b, tok_stride, k_off, ka);
         pin_order();
-        dma_v(kv.v + b, tok_stride, v_off, v0);
+        dma_v<kNT>(kv.v + b, tok_stride, v_off, v0);
         pin_order();
-        if (cn > 1) load_k(kv.k + base_of(1), tok_stride, k_off, kb);
+        if (cn > 1) load_k<kNT>(kv.k + base_of(1), tok_stride, k_off, kb);
         pin_order();
       };
       // a block with a successor
@@ -290,9 +295,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
         f32x4 sc[4];
         block_logits(kcur, qf, sc);
         // vnext was last read by block t - 1's P V, finished at the wait above
-        dma_v(kv.v + base_of(t + 1), tok_stride, v_off, vnext);
+        dma_v<kNT>(kv.v + base_of(t + 1), tok_stride, v_off, vnext);
         pin_order();
-        if (t + 2 < cn) load_k(kv.k + base_of(t + 2), tok_stride, k_off, kcur);
+        if (t + 2 < cn) load_k<kNT>(kv.k + base_of(t + 2), tok_stride, k_off, kcur);
         pin_order();
         block_softmax_pv(sc, scale2, j * kBlockSize, lim, vcur, st);
       };
@@ -383,7 +388,23 @@ __global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict
 
 }  // namespace
 
+int device_cu_count() {
+  // queried once per device; a device that cannot be queried (no GPU) plans
+  // for MI355X's 256 compute units
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 AttnPlan attn_plan(int nq, int hkv, int tiles, bool prefill) {
+  const int kNumCUs = device_cu_count();
   AttnPlan a;
   const long units = (long)nq * hkv;
   // Enough (query, KV head) pairs to give every CU a workgroup: no split.
@@ -394,6 +415,7 @@ AttnPlan attn_plan(int nq, int hkv, int tiles, bool prefill) {
   // queries, whose gather is latency-bound).
   a.waves = 4;
   a.splits = 1;
+  a.stream = !prefill;
   if (!prefill && tiles <= 8 && units < kNumCUs) {
     // at most eight 64-token tiles: one per wave of one eight-wave
     // workgroup, with no split partials and no merge launch
@@ -429,11 +451,17 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   // so the blocks that many queries select stay in the last-level cache.
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
   if (plan.waves == 8) {
-    hipLaunchKernelGGL((sparse_attn_split<8, 1, kAttnGiven, 0, 0>), grid, dim3(512), 0, st, kv, Q, idx, cnt,
-                       nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse, partials);
+    hipLaunchKernelGGL((sparse_attn_split<8, 1, kAttnGiven, 0, 0, true>), grid, dim3(512), 0, st, kv,
+                       Q, idx, cnt, nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse,
+                       partials);
+  } else if (plan.stream) {
+    hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnGiven, 0, 0, true>), grid, dim3(256), 0, st, kv,
+                       Q, idx, cnt, nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse,
+                       partials);
   } else {
-    hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnGiven, 0, 0>), grid, dim3(256), 0, st, kv, Q, idx, cnt,
-                       nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse, partials);
+    hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnGiven, 0, 0, false>), grid, dim3(256), 0, st, kv,
+                       Q, idx, cnt, nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse,
+                       partials);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
@@ -452,7 +480,7 @@ hipError_t launch_sparse_attn_select(const KvView& kv, const QView& Q, const flo
                                      int32_t* cnt_out, hipStream_t st) {
   const float scale2 = scale * kLog2e;
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
-  hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnSelect, 0, 0>), grid, dim3(256), 0, st, kv, Q, nullptr,
+  hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnSelect, 0, 0, true>), grid, dim3(256), 0, st, kv, Q, nullptr,
                      nullptr, scores, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
                      partials);
   hipError_t e = hipGetLastError();
@@ -468,15 +496,15 @@ hipError_t launch_scored_di(const KvView& kv, const QView& Q, int top_k, float s
                             int32_t* idx_out, int32_t* cnt_out, hipStream_t st) {
   const dim3 grid(splits, Q.nq, kv.num_kv_heads), block(64 * kWaves);
   if (Q.hi <= 4) {
-    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 4>), grid, block, 0, st,
+    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 4, true>), grid, block, 0, st,
                        kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2, splits,
                        out, lse, partials);
   } else if (Q.hi <= 8) {
-    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 8>), grid, block, 0, st,
+    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 8, true>), grid, block, 0, st,
                        kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2, splits,
                        out, lse, partials);
   } else {
-    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 16>), grid, block, 0,
+    hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 16, true>), grid, block, 0,
                        st, kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2,
                        splits, out, lse, partials);
   }
@@ -493,7 +521,8 @@ bool attn_score_supported(const KvView& kv, const QView& Q, int top_k, const Att
   // The block-table row, the scores (in the V staging area) and the selection
   // live in LDS.
   const long wgs = (long)Q.nq * kv.num_kv_heads * plan.splits;
-  return (plan.waves == 4 || plan.waves == 8) && kv.maxb <= kMaxScoredBlocks && wgs <= kNumCUs &&
+  return (plan.waves == 4 || plan.waves == 8) && kv.maxb <= kMaxScoredBlocks &&
+         wgs <= device_cu_count() &&
          top_k <= kMaxSelectBlocks && (kv.idx_dim == 64 || kv.idx_dim == 128) && Q.hi >= 1 &&
          Q.hi <= 16 && Q.nq >= 1 && !index_score_mfma_supported(kv, Q);
 }
@@ -532,7 +561,7 @@ hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& Q, float* ws, 
                                    hipStream_t st) {
   const float scale2 = scale * kLog2e;
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
-  hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnCand, 0, 0>), grid, dim3(256), 0, st, kv, Q,
+  hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnCand, 0, 0, true>), grid, dim3(256), 0, st, kv, Q,
                      nullptr, nullptr, ws, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
                      partials);
   hipError_t e = hipGetLastError();

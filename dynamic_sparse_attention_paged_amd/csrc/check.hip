@@ -9,7 +9,7 @@
 // Top-K blocks, padded for ragged batches; [P5] "Day-0 Readiness for
 // Trillion-Parameter Models...", "Index Selection Path" and "KV Cache
 // Layout": ids in gather order, one table row per sequence): a query at
-// position pos sees logical blocks j with j * 64 <= pos; a list holds cnt
+// position pos sees logical blocks j with j * block_size <= pos; a list holds cnt
 // ascending visible ids ending with the local block pos / block_size, then -1.
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -79,7 +79,11 @@ hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, in
 struct AttnPlan {
   int waves;   // waves per workgroup (4 or 8)
   int splits;  // workgroups per (query, KV head)
+  bool stream; // K/V read with the non-temporal cache policy (decode)
 };
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount,
+// cached per device; 256 when no device can be queried).
+int device_cu_count();
 // tiles: 64-token tiles per query (top_k * block_size / 64)
 AttnPlan attn_plan(int nq, int hkv, int tiles, bool prefill);
 size_t attn_partials_bytes(int nq, int hq, int splits);

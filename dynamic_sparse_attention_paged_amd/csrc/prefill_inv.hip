@@ -204,9 +204,13 @@ __global__ __launch_bounds__(kInvThreads) void inv_attend(
     const int my_e = e + ce;
     return entries[(col_ok && my_e < e1) ? my_e : sentinel];
   };
+  // Columns past the group's heads (hl >= G, only with kQPT = 1 and G not a
+  // power of two) read head G - 1 of the group: rows g * G .. g * G + G - 1
+  // lie inside query qq's Hq heads, so no read leaves the caller's Q buffer.
+  const int hl_q = min(hl, G - 1);
   auto load_q = [&](const int4& en, i16x8 (&qf)[4]) {
     const int qq = min(en.x, Q.nq - 1);
-    const uint16_t* qp = Q.q + ((size_t)qq * Q.hq + g * G + hl) * kHeadDim + 8 * gq;
+    const uint16_t* qp = Q.q + ((size_t)qq * Q.hq + g * G + hl_q) * kHeadDim + 8 * gq;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qf[c] = *reinterpret_cast<const i16x8*>(qp + 32 * c);
   };

@@ -20,8 +20,8 @@ def lib():
     return _lib.load()
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+def _declared(header="dsa.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
@@ -32,6 +32,30 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
     assert lib.dsa_abi_version() == 2
+
+
+def test_every_header_is_exported(lib):
+    """Every function declared in any include/*.h is exported by libdsa.so."""
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert "dsa_support.h" in headers
+    for h in headers:
+        for n in _declared(h):
+            assert hasattr(lib, n), f"{h}: {n}"
+    assert set(_lib.SUPPORT_EXPORTS) == set(_declared("dsa_support.h"))
+
+
+def test_support_calls_reject_bad_arguments(lib):
+    """The measurement-support calls validate before launching anything."""
+    assert lib.dsa_probe_stream_read(None, 1 << 20, 0, FAKE, 8, None) == -1
+    assert lib.dsa_probe_stream_read(FAKE + 4, 1 << 20, 0, FAKE, 8, None) == -4
+    assert lib.dsa_probe_stream_read(FAKE, (1 << 20) + 8, 0, FAKE, 8, None) == -4
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 0, FAKE, 0, None) == -1
+    assert lib.dsa_cache_flush(None, 1 << 20, 1, None) == -1
+    assert lib.dsa_cache_flush(FAKE, 100, 1, None) == -4
+    assert lib.dsa_probe_mfma_rate(7, 10, 8, FAKE, None) == -3
+    assert lib.dsa_probe_mfma_rate(0, 0, 8, FAKE, None) == -1
+    assert lib.dsa_probe_fp8_mfma(FAKE, FAKE, FAKE, 0, FAKE, None) == -1
+    assert lib.dsa_probe_fp8_mfma(FAKE + 8, FAKE, FAKE, 1, FAKE, None) == -4
 
 
 FAKE = 0x10000  # a 64 KiB-aligned non-NULL address: never dereferenced on the host

@@ -87,38 +87,61 @@ def test_batched_decode_full(dsa, kv_layout):
     _check(w, range(w.num_queries), idx, cnt, out, lse, "batched_decode")
 
 
-def test_million_decode_full(dsa):
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
+def test_million_decode_full(dsa, kv_layout):
     w = workload.million_decode()
-    _say("million-token decode 4 x 1048576, all queries")
-    idx, cnt, out, lse = _fused(dsa, w)
+    _say(f"million-token decode 4 x 1048576, all queries, kv_layout {kv_layout}")
+    idx, cnt, out, lse = _fused(dsa, w, kv_layout)
     _check(w, range(w.num_queries), idx, cnt, out, lse, "million_decode")
 
 
-def test_ragged_decode_sampled(dsa):
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
+def test_ragged_decode_sampled(dsa, kv_layout):
     w = workload.ragged_decode()
-    _say(f"ragged decode 128 seqs, pool {w.num_blocks} blocks, 16 sampled queries")
-    idx, cnt, out, lse = _fused(dsa, w)
+    _say(f"ragged decode 128 seqs, pool {w.num_blocks} blocks, 16 sampled queries, "
+         f"kv_layout {kv_layout}")
+    idx, cnt, out, lse = _fused(dsa, w, kv_layout)
     order = np.argsort(w.seq_lens)
     qis = sorted(set(order[:4].tolist() + order[-4:].tolist() + list(range(0, 128, 16))))
     _check(w, qis, idx, cnt, out, lse, "ragged_decode")
 
 
-def test_chunked_prefill_sampled(dsa):
+# tile edges (queries 63/64/65, 127/128), the first and last queries, the
+# middle of the chunk, and a stride through the rest
+PREFILL_SAMPLE = [0, 1, 63, 64, 65, 127, 128, 4095, 4096, 8190, 8191] + list(range(700, 8192, 1013))
+
+
+@pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
+def test_chunked_prefill_sampled(dsa, kv_layout):
+    """The full 8192-query chunk through both prefill paths, as bench.py times
+    them: index_score -> topk -> the per-query prefill kernel, and the one-call
+    block-inverted prefill (dsa_sparse_prefill_fused: ~256 queries per pool
+    tile list, a 17 GB partial-state region, byte offsets past 2^31).  Sampled
+    queries against the oracle, each computed on its own."""
     w = workload.chunked_prefill()
-    _say("chunked prefill 8192 queries, 20 sampled")
-    kv, qs = parity.to_device(w)
+    _say(f"chunked prefill 8192 queries, {len(PREFILL_SAMPLE)} sampled, kv_layout {kv_layout}")
+    kv, qs = parity.to_device(w, kv_layout=kv_layout)
     K = w.top_k
     scores = dsa.index_score(kv, qs)
     idx, cnt = dsa.topk_blocks(scores, kv, qs, K)
     out, lse = dsa.sparse_attn_prefill(kv, qs, idx, cnt, K, w.softmax_scale)
     torch.cuda.synchronize()
-    qis = [0, 1, 63, 64, 65, 127, 128, 4095, 4096, 8190, 8191] + list(range(700, 8192, 1013))
-    _check(w, qis, idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy(),
-           "chunked_prefill")
-    # the scores themselves are the oracle's float64 score rounded to fp32, bit for bit
     sh = scores.cpu().numpy()
-    for qi in qis[:6]:
+    idx_h, cnt_h, out_h, lse_h = idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy(), \
+        lse.cpu().numpy()
+    del scores, out, lse
+    bi = torch.empty_like(idx)
+    bc = torch.empty_like(cnt)
+    fo, fl, _, _ = dsa.prefill_fused(kv, qs, K, w.softmax_scale, block_idx=bi, block_cnt=bc)
+    torch.cuda.synchronize()
+    bi_h, bc_h, fo_h, fl_h = bi.cpu().numpy(), bc.cpu().numpy(), fo.cpu().numpy(), fl.cpu().numpy()
+    del kv, qs, idx, cnt, bi, bc, fo, fl
+    torch.cuda.empty_cache()
+    # the one-call prefill selects exactly what the stage-wise path selects, for every query
+    assert np.array_equal(bi_h, idx_h) and np.array_equal(bc_h, cnt_h)
+    _check(w, PREFILL_SAMPLE, idx_h, cnt_h, out_h, lse_h, "chunked_prefill per-query")
+    _check(w, PREFILL_SAMPLE, bi_h, bc_h, fo_h, fl_h, "chunked_prefill fused (block-inverted)")
+    # the scores themselves are the oracle's float64 score rounded to fp32, bit for bit
+    for qi in PREFILL_SAMPLE[:6]:
         r = parity.oracle_query(w, qi)
         assert parity.check_scores_exact(sh[qi], r, w.block_table.shape[1]).size == 0
-    del kv, qs, scores, idx, cnt, out, lse
-    torch.cuda.empty_cache()

@@ -91,11 +91,13 @@ def test_mxfp8_matches_torch_encoder_and_range():
 
 
 def _brute(x_codes, x_scales, w_packed, w_scales, route, k):
-    """Scalar loops: nibbles, E2M1 table, scales read element by element."""
+    """Scalar loops: nibbles, E2M1 table, scales read element by element.
+    Returns (sum_k xv * w, sum_k |xv * w|) per (token, slot, column)."""
     table = GOLD["e2m1_values_by_code"]
     t_n, slots = route.shape
     n = w_scales.shape[1]
     out = np.zeros((t_n, slots, n))
+    mag = np.zeros((t_n, slots, n))
     for t in range(t_n):
         for j in range(slots):
             e = int(route[t, j])
@@ -103,6 +105,7 @@ def _brute(x_codes, x_scales, w_packed, w_scales, route, k):
                 continue
             for c in range(n):
                 acc = 0.0
+                acc_abs = 0.0
                 for i in range(k):
                     byte = int(w_packed[e, c, i // 2])
                     nib = (byte >> 4) if i % 2 else (byte & 15)
@@ -110,8 +113,10 @@ def _brute(x_codes, x_scales, w_packed, w_scales, route, k):
                     xv = float(e4m3_decode(np.array([x_codes[t, i]]))[0]) * \
                         2.0 ** (int(x_scales[t, i // 32]) - 127)
                     acc += xv * w
+                    acc_abs += abs(xv * w)
                 out[t, j, c] = acc
-    return out
+                mag[t, j, c] = acc_abs
+    return out, mag
 
 
 def _moe_case(seed, t_n=3, slots=2, e_n=3, n=4, k=64):
@@ -128,8 +133,22 @@ def test_grouped_gemm_brute_force():
     for seed in range(3):
         xc, xs, wp, ws, route = _moe_case(seed)
         got = grouped_gemm(xc, xs, wp, ws, route)
-        want = _brute(xc, xs, wp, ws, route, 64)
+        want, _ = _brute(xc, xs, wp, ws, route, 64)
         assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+        assert not got[route < 0].any()
+
+
+def test_grouped_gemm_abs_brute_force():
+    """The error scale of the matmul's parity bar, sum_k |xq w|, against the
+    scalar loops: activation and weight block scales each enter it once."""
+    for seed in range(3):
+        xc, xs, wp, ws, route = _moe_case(seed)
+        # activation blocks with different scales, so a dropped scale shows
+        xs = xs.copy()
+        xs[:, 1] = np.clip(xs[:, 1].astype(np.int64) + 3, 1, 254).astype(np.uint8)
+        got = grouped_gemm_abs(xc, xs, wp, ws, route)
+        _, want = _brute(xc, xs, wp, ws, route, 64)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-300)
         assert not got[route < 0].any()
 
 

@@ -30,7 +30,8 @@ _real = {name: getattr(D, name, None) or getattr(F, name, None) or getattr(P, na
                       "attention_partial", "merge_partials", "sparse_attention",
                       "dense_attention", "score_query", "quantize_coarse_key", "kv_write")}
 _real.update({name: getattr(M, name) for name in ("e2m1_decode", "unpack_fp4", "mxfp4_dequant",
-                                                    "mx_quantize_e4m3", "mx_dequant_e4m3")})
+                                                    "mx_quantize_e4m3", "mx_dequant_e4m3",
+                                                    "grouped_gemm_abs")})
 
 
 def _patch(monkeypatch, name, fn):
@@ -237,6 +238,17 @@ def mx_dequant_ignores_scale(codes, scales):
     return F.e4m3_decode(codes)
 
 
+def gemm_abs_ignores_activation_scales(x_codes, x_scales, w_packed, w_scales, route):
+    xq = np.abs(F.e4m3_decode(x_codes))
+    route = np.asarray(route)
+    out = np.zeros(route.shape + (np.asarray(w_scales).shape[1],))
+    for e in np.unique(route[route >= 0]):
+        w = np.abs(M.mxfp4_dequant(w_packed[e], w_scales[e]))
+        tt, jj = np.nonzero(route == e)
+        out[tt, jj] = xq[tt] @ w.T
+    return out
+
+
 CASES = [
     ("e4m3_decode", decode_wrong_bias, ["TF.test_spot_codes"]),
     ("e4m3_encode", encode_ties_away, ["TF.test_encode_ties_to_even",
@@ -275,6 +287,8 @@ CASES = [
     ("mx_quantize_e4m3", mx_quantize_ceil_log2, ["TM.test_mxfp8_hand_example",
                                                  "TM.test_mxfp8_matches_torch_encoder_and_range"]),
     ("mx_dequant_e4m3", mx_dequant_ignores_scale, ["TM.test_grouped_gemm_brute_force"]),
+    ("grouped_gemm_abs", gemm_abs_ignores_activation_scales,
+     ["TM.test_grouped_gemm_abs_brute_force"]),
 ]
 
 
