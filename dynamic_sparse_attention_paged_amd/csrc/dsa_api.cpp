@@ -157,6 +157,10 @@ AttnLayout attn_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k,
 dsa_status select_blocks(const dsa::KvView& kvv, const dsa::QView& qv, int top_k, int32_t* idx,
                          int32_t* cnt, float* scores, hipStream_t stream, const char* who) {
   char what[96];
+  if (dsa::index_topk_fp8_supported(kvv, qv)) {
+    snprintf(what, sizeof what, "%s: fp8 index_topk launch", who);
+    return hip_status(dsa::launch_index_topk_fp8(kvv, qv, top_k, idx, cnt, stream), what);
+  }
   if (dsa::index_topk_fused_supported(kvv, qv)) {
     snprintf(what, sizeof what, "%s: index_topk fused launch", who);
     return hip_status(dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream), what);

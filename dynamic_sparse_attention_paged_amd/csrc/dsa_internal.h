@@ -72,6 +72,14 @@ hipError_t launch_index_topk_fused(const KvView& kv, const QView& q, int top_k, 
                                    int32_t* cnt, hipStream_t s);
 hipError_t launch_topk(const float* scores, const KvView& kv, const QView& q, int top_k,
                        int32_t* idx, int32_t* cnt, hipStream_t s);
+// Scoring and Top-K of many queries (a prefill chunk) in one launch:
+// approximate scores on the FP8 matrix cores with an error bound, exact
+// scores only for the blocks the bound leaves undecided (the same indices as
+// launch_index_score followed by launch_topk), for sequences of at most 2048
+// blocks.
+bool index_topk_fp8_supported(const KvView& kv, const QView& q);
+hipError_t launch_index_topk_fp8(const KvView& kv, const QView& q, int top_k, int32_t* idx,
+                                 int32_t* cnt, hipStream_t s);
 
 // Split-K sparse attention.  num_splits == 1 writes out/lse directly;
 // otherwise partial softmax states go to `partials` and a merge kernel follows

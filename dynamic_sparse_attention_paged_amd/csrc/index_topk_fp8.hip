@@ -1,0 +1,615 @@
+// Indexer scoring and Top-K selection of many queries (a prefill chunk) in one
+// launch, with the scores kept in LDS: approximate scores on the FP8 matrix
+// cores, a bound on their error, and exact scores only for the few blocks
+// that the bound cannot place on either side of the Top-K boundary.
+//
+// What is computed ([P1] "Day-0 Adaptation for Massive LLMs...", section 4(1)
+// "Index Selection" and section 4(3): prefill scoring is compute-intensive
+// and the inner product should not write intermediates to memory; [P3]
+// "Day-0 Adaptation for Trillion-Parameter Models...", section 4.1: Top-K
+// fused with the scoring before it; [P5] "Day-0 Readiness...", "Index
+// Selection Path": low-precision scoring inputs) is exactly what
+// index_score.hip followed by topk.hip compute: for query q at position pos
+// and each visible block j < l = pos / block_size,
+//   S[j] = sum_h w[h] max(0, (sq[h] ks[p]) D[h, j])  (float64, rounded to fp32),
+//   D[h, j] = <q8[h, :], k8[p, :]> exact,  p = table[s][j],
+// then the local block l plus the K - 1 best others (equal fp32 scores to the
+// lower id), ids ascending.
+//
+// How.  One workgroup holds kQB = 8 queries.
+//  1. Every (query, head) row of E4M3 codes q8 becomes FP8 MFMA operand rows.
+//     A 16 x 16 x 128 tile of v_mfma_scale_f32_16x16x128_f8f6f4 (unit
+//     scales) has rows (query 4 g + r / 4, head 4 t + r % 4) for row tile t of
+//     query group g, so that lane (column c, group r / 4) receives heads
+//     4 t .. 4 t + 3 of one query in every row tile of the group: the head sum
+//     stays inside the lane.  Columns are 16 blocks, k the 128 key dims.
+//  2. Approximate score  S^[j] = ks[p] sum_h a[h] max(0, D^[h, j]),  a[h] =
+//     w[h] sq[h], into LDS.
+//  3. Error bound.  The matrix unit's products of E4M3 values are exact; it
+//     sums them in groups of eight, each group aligned to its largest product
+//     and truncated toward zero 13 bits below that product's exponent, and
+//     combines the group sums at fp32 precision or better (characterized with
+//     dsa_probe_fp8_mfma: structured cases land exactly on this rule and 1.5
+//     million random outputs never exceed it).  For one instruction,
+//       |D^ - D| <= 16 groups x 7 truncated products x 2^(e_max - 13)
+//                   + 2^-13 max|q8| max|k8|  <  2^-6 max|q8[h]| max|k8[p]|,
+//     e_max the exponent of the largest product, max|k8| <= 448.  With fp32
+//     epilogue rounding (2^-12 of the same scale) the approximate score obeys
+//       |S^[j] - S[j]| <= E = 448 ks_max (2^-6 + 2^-12) sum_h |a[h]| max|q8[h]|,
+//     ks_max the largest key scale among the blocks the workgroup scores.
+//  4. Selection.  T = the (K-1)-th largest S^ (wave radix select).  A block
+//     with S^ > T + 2E (+ slack) beats every block that can beat it except at
+//     most K - 2, so it is kept; one with S^ < T - 2E (- slack) is beaten by
+//     at least K - 1 blocks, so it is dropped.  The slack keeps both sides at
+//     least a few fp32 ulps apart, so rounding the scores to fp32 cannot turn
+//     a strict order into a tie.  Only the blocks in between ("uncertain":
+//     a handful per query at the chunked-prefill shape) are scored exactly,
+//     on the int8 matrix cores from base-128 digit planes (digit_mfma.h,
+//     bit-exact fp32 scores), and the remaining picks are made among them by
+//     (exact score desc, id asc).  The result is therefore the exact
+//     selection whatever the approximate scores were, as long as the bound
+//     holds.
+//  A workgroup whose queries belong to several sequences scores once per
+//  sequence (the key columns follow that sequence's table row).
+#include <float.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "dsa_internal.h"
+#include "score_i8_lds.h"
+#include "select_common.h"
+
+namespace dsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQB = 8;            // queries per workgroup (two groups of four)
+constexpr int kMaxBlocks = 2048;  // blocks per sequence: scores of kQB queries in LDS
+constexpr int kPitch = kMaxBlocks + 16;  // rows 16 banks apart
+constexpr int kListCap = 256;     // undecided blocks ranked from a list (more: every block rescored)
+constexpr int kChunk = 4;         // column tiles per pipeline step
+// 2^-6 (the matrix unit) + 2^-12 (fp32 epilogue), as a fraction of
+// 448 ks max|q8| |a| summed over heads
+constexpr float kErrFrac = 0.015625f + 0.000244140625f;
+
+// max(x, 0) in one instruction (v_med3_f32) for finite x
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, FLT_MAX); }
+
+__device__ __forceinline__ float key_float(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __builtin_bit_cast(float, u);
+}
+
+// E4M3 codes of one row's 32 values x[0 .. 32) scaled by 2^-e, four a word.
+__device__ __forceinline__ void codes_of(const float (&x)[32], int e, int (&c)[8]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float y = ldexpf(x[4 * w + b], -e);  // exact
+      v |= ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu) << (8 * b);
+    }
+    c[w] = (int)v;
+  }
+}
+
+// Exact scores of blocks j by one wave, written to row[j]: j = list[e] for e
+// in [0, n) (list != nullptr), or j = e (list == nullptr).  The int8
+// digit-plane products of score_i8_lds.h over 16-block tiles gathered from
+// the list; the scores are the oracle's float64 values rounded to fp32.
+template <int DI, int HP>
+__device__ void rescore_list(const KvView& kv, const i32x4 (&qa)[DI / 64][3], int lane,
+                             const uint16_t* list, int n, const int32_t* trow,
+                             const uint32_t* lut, const double* wsq, float* row) {
+  constexpr int KC = DI / 64;
+  constexpr int kGroups = HP / 4;
+  const int gq = lane >> 4, r = lane & 15;
+  double wh[4];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) wh[i4] = wsq[(4 * gq + i4) & 15];
+  // four 16-block tiles at a time: list entries, then table entries, then key
+  // rows, each level's loads all in flight together
+  constexpr int kTiles = 4;
+  for (int t0 = 0; t0 < n; t0 += 16 * kTiles) {
+    int j[kTiles], p[kTiles];
+    // (columns past the list repeat its last entry: every load is in range
+    // and unconditional, and their results are not stored)
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      const int e = min(t0 + 16 * u + r, n - 1);
+      j[u] = list ? (int)list[e] : e;
+    }
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) p[u] = trow[j[u]];
+    uint4 kw[kTiles][KC];
+    float ks[kTiles];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      const uint4* krow = reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)p[u] * DI + 16 * gq);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kw[u][kc] = krow[4 * kc];
+      ks[u] = kv.idx_scale[p[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      if (t0 + 16 * u >= n) break;  // uniform
+      i32x4 kb[KC][3];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) planes_of(lut, kw[u][kc], kb[kc]);
+      // hi = G2 + 2^7 (G3 + 2^7 G4), lo = G0 + 2^7 G1: exact in int32
+      i32x4 h = i32x4{0, 0, 0, 0}, l = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) h = mfma_i8(qa[kc][2], kb[kc][2], h);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) l = mfma_i8(qa[kc][0], kb[kc][1], l);
+      h = h * 128;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        h = mfma_i8(qa[kc][1], kb[kc][2], h);
+        h = mfma_i8(qa[kc][2], kb[kc][1], h);
+        l = mfma_i8(qa[kc][1], kb[kc][0], l);
+      }
+      h = h * 128;
+      l = l * 128;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        h = mfma_i8(qa[kc][0], kb[kc][2], h);
+        h = mfma_i8(qa[kc][1], kb[kc][1], h);
+        h = mfma_i8(qa[kc][2], kb[kc][0], h);
+        l = mfma_i8(qa[kc][0], kb[kc][0], l);
+      }
+      // the float64 epilogue in ascending head order, as the oracle evaluates it
+      const double ksd = (double)ks[u];
+      double acc = 0.0;
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        double run = 0.0;
+        if (g > 0) run = __shfl(acc, (lane + 48) & 63, 64);  // the same column, group g - 1
+        if (gq == g) {
+#pragma clang fp contract(off)
+          acc = run;
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const double D = fma((double)h[i4], 16384.0, (double)l[i4]);
+            const double y = ksd * D;
+            const double rr = y > 0.0 ? y : 0.0;
+            acc = acc + wh[i4] * rr;
+          }
+        }
+      }
+      if (gq == kGroups - 1 && t0 + 16 * u + r < n) row[j[u]] = (float)acc;
+    }
+  }
+}
+
+// grid (ceil(Nq / kQB)), block 256.  HP (4, 8 or 16) >= HI heads a query.
+template <int DI, int HP>
+__global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q, int top_k,
+                                                              int32_t* __restrict__ out_idx,
+                                                              int32_t* __restrict__ out_cnt) {
+  constexpr int NT = HP / 4;         // row tiles per query group
+  constexpr int NRT = (kQB / 4) * NT;  // row tiles per workgroup
+  constexpr int KC = DI / 64;
+  // score rows, then one slot per lane for the stores of columns that hold no
+  // candidate (so that the epilogue needs no branch)
+  __shared__ float sc[kQB * kPitch + kThreads];
+  __shared__ uint16_t list_s[kWaves][kListCap];
+  __shared__ uint4 hist4[kWaves][64];  // radix histograms (wave_select)
+  __shared__ uint32_t bins_s[kWaves][64];
+  __shared__ uint32_t lut[256];
+  __shared__ float a_s[kQB][16], am_s[kQB][16];
+  __shared__ double wsq_s[kWaves][16];
+  __shared__ float cq_s[kQB], ksmax_s[kWaves];
+  __shared__ int seq_s[kQB], n_s[kQB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, kg = lane >> 4;
+  const int q0 = blockIdx.x * kQB;
+
+  if (tid < kQB) {
+    const int q = q0 + tid;
+    int s = -1, n = -1;
+    if (q < Q.nq) {
+      s = query_seq(Q, q);
+      const int len = kv.seq_lens[s];
+      const int pos = Q.q_pos ? Q.q_pos[q] : len - 1;
+      n = pos >> kv.bs_shift;  // the local block; candidates 0 .. n - 1
+    }
+    seq_s[tid] = s;
+    n_s[tid] = n;
+  }
+  for (int c = tid; c < 256; c += kThreads) lut[c] = digits_of_code((uint32_t)c);
+
+  // ---- 1. query rows as FP8 operands: wave w quantizes row tiles w, w + 4,
+  // .. and stages them in LDS (the start of the score rows, which the main
+  // loop writes only after every wave has its operands)
+  i32x8* a_stage = reinterpret_cast<i32x8*>(sc);  // [NRT][64 lanes]
+  static_assert(NRT * 64 * 32 <= kQB * kPitch * 4, "operand staging fits the score rows");
+  for (int rt = wave; rt < NRT; rt += kWaves) {
+    const int g4 = rt / NT, t = rt % NT;
+    const int ql = 4 * g4 + (r >> 2), h = 4 * t + (r & 3);
+    const int q = q0 + ql;
+    const bool live = q < Q.nq && h < Q.hi;
+    float x[32];
+    uint4 raw[2][2];
+    const uint4* src =
+        reinterpret_cast<const uint4*>(Q.q_idx + ((size_t)(live ? q : 0) * Q.hi + (live ? h : 0)) * DI);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const bool ok = live && (hf * 64 < DI);
+      raw[hf][0] = ok ? src[8 * hf + 2 * kg] : make_uint4(0u, 0u, 0u, 0u);
+      raw[hf][1] = ok ? src[8 * hf + 2 * kg + 1] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t wv[8] = {raw[hf][0].x, raw[hf][0].y, raw[hf][0].z, raw[hf][0].w,
+                              raw[hf][1].x, raw[hf][1].y, raw[hf][1].z, raw[hf][1].w};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[16 * hf + e] = bf16f((uint16_t)(wv[e >> 1] >> (16 * (e & 1))));
+        amax = fmaxf(amax, fabsf(x[16 * hf + e]));
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int ex = 0;
+    if (amax != 0.f) {
+      int E;
+      const float f = frexpf(amax, &E);  // amax = f 2^E, f in [0.5, 1)
+      ex = (f <= 0.875f) ? E - 9 : E - 8;  // the smallest e with amax <= 448 2^e
+    }
+    int c[8];
+    codes_of(x, ex, c);
+    a_stage[rt * 64 + lane] = i32x8{c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7]};
+    if (kg == 0) {
+      const float a = live ? ldexpf(Q.w[(size_t)q * Q.hi + h], ex) : 0.f;
+      // max |q8| <= amax 2^-e rounded to nearest: at most 2^-4 above it
+      const float mq = ldexpf(amax, -ex) * 1.0625f;
+      a_s[ql][h] = a;
+      am_s[ql][h] = fabsf(a) * mq;
+    }
+  }
+  __syncthreads();
+  i32x8 A[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) A[rt] = a_stage[rt * 64 + lane];
+  __syncthreads();
+  if (tid < kQB) {
+    float t = 0.f;
+    for (int h = 0; h < HP; ++h) t += am_s[tid][h];
+    cq_s[tid] = t * (448.f * kErrFrac * 1.0001f);
+  }
+  // epilogue weights of the lane's query in each group
+  float aw[kQB / 4][HP];
+#pragma unroll
+  for (int g4 = 0; g4 < kQB / 4; ++g4)
+#pragma unroll
+    for (int h = 0; h < HP; ++h) aw[g4][h] = a_s[4 * g4 + kg][h];
+
+  // ---- 2. approximate scores into LDS, one pass per sequence of the workgroup
+  float ksmax = 0.f;
+  uint32_t done = 0u;
+  for (;;) {
+    int sq_seq = -1, nmax = 0;
+    uint32_t pass = 0u;
+#pragma unroll
+    for (int ql = 0; ql < kQB; ++ql) {
+      const int s = seq_s[ql];
+      if (s < 0 || ((done >> ql) & 1u)) continue;
+      if (sq_seq < 0) sq_seq = s;
+      if (s == sq_seq) {
+        pass |= 1u << ql;
+        nmax = max(nmax, n_s[ql]);
+      }
+    }
+    if (sq_seq < 0) break;
+    done |= pass;
+    const int32_t* trow = kv.table + (size_t)sq_seq * kv.maxb;
+    const int nct = (nmax + 15) >> 4;  // column tiles holding candidates
+    const int nt_w = nct > wave ? (nct - wave + kWaves - 1) / kWaves : 0;
+    if (nt_w == 0) continue;           // uniform over the wave (nmax >= 1 below)
+    const int nch = (nt_w + kChunk - 1) / kChunk;
+    const int jlast = nmax - 1;
+    // Loads are unconditional: columns past the candidates (and the tiles a
+    // pipeline step fetches beyond the last one) read the last candidate's
+    // entry, and their results are discarded.  Straight-line loads let the
+    // compiler wait for exactly the ones a step consumes.
+    auto load_tab = [&](int ch, int (&tb)[kChunk]) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int i = ch * kChunk + u;
+        tb[u] = trow[min(16 * (wave + kWaves * i) + r, jlast)];
+      }
+    };
+    auto load_keys = [&](const int (&tb)[kChunk], i32x8 (&B)[kChunk], float (&ks)[kChunk]) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const uint8_t* kr = kv.idx_keys + (size_t)tb[u] * DI;
+        const uint4 lo = *reinterpret_cast<const uint4*>(kr + 16 * kg);
+        const uint4 hi = DI == 128 ? *reinterpret_cast<const uint4*>(kr + 64 + 16 * kg)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+        B[u] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        ks[u] = kv.idx_scale[tb[u]];
+      }
+    };
+    auto mfmas = [&](const i32x8& B, f32x4 (&acc)[NRT]) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            A[rt], B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+    };
+    auto epilogue = [&](int i, float ks, const f32x4 (&acc)[NRT]) {
+      const int j = 16 * (wave + kWaves * i) + r;
+      const bool ok = i < nt_w && j < nmax;
+      ksmax = fmaxf(ksmax, ok ? ks : 0.f);
+#pragma unroll
+      for (int g4 = 0; g4 < kQB / 4; ++g4) {
+        float tsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            tsum = fmaf(aw[g4][4 * t + i4], relu(acc[g4 * NT + t][i4]), tsum);
+        const int ql = 4 * g4 + kg;
+        const bool st = ok && ((pass >> ql) & 1u);
+        sc[st ? ql * kPitch + j : kQB * kPitch + tid] = ks * tsum;
+      }
+    };
+    // the MFMAs of tile u + 1 are issued before the epilogue of tile u, so the
+    // matrix cores run while the vector units finish the previous tile
+    auto compute = [&](int ch, const i32x8 (&B)[kChunk], const float (&ks)[kChunk]) {
+      f32x4 acc0[NRT], acc1[NRT];
+      mfmas(B[0], acc0);
+#pragma unroll
+      for (int u = 0; u < kChunk; u += 2) {
+        if (u + 1 < kChunk) mfmas(B[u + 1], acc1);
+        epilogue(ch * kChunk + u, ks[u], acc0);
+        if (u + 1 >= kChunk) break;
+        if (u + 2 < kChunk) mfmas(B[u + 2], acc0);
+        epilogue(ch * kChunk + u + 1, ks[u + 1], acc1);
+      }
+    };
+    // Software pipeline, three stages: table entries three chunks ahead, key
+    // rows two chunks ahead (eight column tiles in flight: the key rows are
+    // scattered and their latency is long).  Vector-memory loads complete in
+    // order, so each step issues the table loads of chunk c + 3 before the
+    // key loads of chunk c + 2 (whose table entries came a step earlier):
+    // waiting for those entries then never waits for keys still in use.
+    int tbA[kChunk], tbB[kChunk], tbC[kChunk];
+    i32x8 BA[kChunk], BB[kChunk], BC[kChunk];
+    float ksA[kChunk], ksB[kChunk], ksC[kChunk];
+    load_tab(0, tbA);
+    load_tab(1, tbB);
+    load_tab(2, tbC);
+    load_keys(tbA, BA, ksA);
+    load_keys(tbB, BB, ksB);
+    for (int ch = 0; ch < nch; ch += 3) {
+      load_tab(ch + 3, tbA);
+      load_keys(tbC, BC, ksC);
+      compute(ch, BA, ksA);
+      if (ch + 1 >= nch) break;
+      load_tab(ch + 4, tbB);
+      load_keys(tbA, BA, ksA);
+      compute(ch + 1, BB, ksB);
+      if (ch + 2 >= nch) break;
+      load_tab(ch + 5, tbC);
+      load_keys(tbB, BB, ksB);
+      compute(ch + 2, BC, ksC);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ksmax = fmaxf(ksmax, __shfl_xor(ksmax, off, 64));
+  if (lane == 0) ksmax_s[wave] = ksmax;
+  __syncthreads();
+  float ksm = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ksm = fmaxf(ksm, ksmax_s[w]);
+
+  // ---- 3. selection, one query at a time per wave
+  for (int ql = wave; ql < kQB; ql += kWaves) {
+    const int q = q0 + ql;
+    if (q >= Q.nq) break;
+    const int s = seq_s[ql], n = n_s[ql], local = n;
+    const int need = top_k - 1;
+    int32_t* out = out_idx + (size_t)q * top_k;
+    if (n <= need) {
+      for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
+      if (lane == 0) out_cnt[q] = local + 1;
+      continue;
+    }
+    if (need == 0) {
+      if (lane == 0) {
+        out[0] = local;
+        out_cnt[q] = 1;
+      }
+      continue;
+    }
+    // the query rows of the exact rescoring, requested now so that they arrive
+    // during the selection
+    QueryRows<DI> qr;
+    qr.fetch(Q, q, lane);
+    const int32_t* trow = kv.table + (size_t)s * kv.maxb;
+    float* row = sc + ql * kPitch;
+    // candidate c = 64 m + lane: every LDS read of the row is one wave-wide
+    // contiguous read, and a decision over all candidates is 32 ballots
+    float v[32];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      const int c = 64 * m + lane;
+      v[m] = c < n ? row[c] : -INFINITY;
+      mx = fmaxf(mx, v[m]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    // ---- bracket the need-th largest S^: a histogram of 64 bins of width
+    // delta below the maximum (bin = floor((max - S^) / delta)); the bin b
+    // holding rank `need` gives T_lo = max - (b + 1) delta and T_hi = max -
+    // b delta, each widened by eps for the rounding of the bin arithmetic, so
+    // that #{S^ >= T_lo} >= need and #{S^ > T_hi} <= need - 1.
+    const float E = cq_s[ql] * ksm;  // |S^ - S| <= E for every candidate
+    float delta = fmaxf(0.5f * E, fmaxf(fabsf(mx) * 1.1920929e-07f, 1e-30f));
+    int b_star = -1;
+    float T_lo = 0.f, T_hi = 0.f;
+    for (int tries = 0; tries < 40; ++tries) {  // delta x8 a try: ends once 64 bins hold rank need
+      bins_s[wave][lane] = 0u;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      const float inv = 1.f / delta;
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        const float b = (mx - v[m]) * inv;  // +inf for the padding
+        if (b < 64.f) atomicAdd(&bins_s[wave][(int)b], 1u);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t cum = wave_incl_scan(bins_s[wave][lane]);
+      const unsigned long long hit = __ballot(cum >= (uint32_t)need);
+      if (hit) {
+        b_star = __builtin_ffsll((long long)hit) - 1;
+        const float eps = (fabsf(mx) + 65.f * delta) * 9.5367431640625e-07f;  // 2^-20
+        T_lo = mx - (float)(b_star + 1) * delta - eps;
+        T_hi = mx - (float)b_star * delta + eps;
+        break;
+      }
+      delta *= 8.f;
+    }
+    // (b_star < 0 only if delta overflowed: then every candidate is undecided)
+    const float slack = (fabsf(mx) + fabsf(T_lo) + 2.f * E) * 9.5367431640625e-07f + 1e-30f;
+    const float hi_thr = b_star >= 0 ? T_hi + 2.f * E + slack : INFINITY;
+    const float lo_thr = b_star >= 0 ? T_lo - 2.f * E - slack : -INFINITY;
+    // ---- certainly in: S^ > hi_thr; undecided: lo_thr <= S^ <= hi_thr.  The
+    // undecided ids go to the list in ascending order.
+    int n_in = 0, n_unc = 0;
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      const bool ok = 64 * m + lane < n;
+      n_in += __builtin_popcountll(__ballot(ok && v[m] > hi_thr));
+      const bool u = ok && v[m] >= lo_thr && !(v[m] > hi_thr);
+      const unsigned long long um = __ballot(u);
+      // (a list longer than kListCap is not used: its last slot may hold any id)
+      const int at = n_unc + __builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
+      if (u) list_s[wave][min(at, kListCap - 1)] = (uint16_t)(64 * m + lane);
+      n_unc += __builtin_popcountll(um);
+    }
+    const int r_need = need - n_in;
+    i32x4 qa[KC][3];
+    if (r_need < n_unc) {
+      qr.build(lut, lane, true, wsq_s[wave], qa);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): wsq and the list written
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (r_need < n_unc && n_unc > kListCap) {
+      // Degenerate scores (for instance all equal, or all zero): too many
+      // undecided blocks for the list.  Score every candidate exactly and
+      // select from the exact scores alone.
+      for (int base = 0; base < n; base += 1024)
+        rescore_list<DI, HP>(kv, qa, lane, nullptr, min(1024, n - base), trow + base, lut,
+                             wsq_s[wave], row + base);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      uint32_t k[32], valid = 0u;
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {  // lane-major: candidate 32 lane + m
+        const int c = 32 * lane + m;
+        k[m] = c < n ? order_key(row[c]) : 0u;
+        valid |= (c < n) ? (1u << m) : 0u;
+      }
+      uint32_t T, take_eq, o;
+      wave_select<32>(k, valid, (uint32_t)need, hist4[wave], T, take_eq);
+      const uint32_t keep = wave_keep<32>(k, valid, T, take_eq, &o);
+#pragma unroll
+      for (int m = 0; m < 32; ++m)
+        if ((keep >> m) & 1u) out[o++] = 32 * lane + m;
+      if (lane == 0) {
+        out[need] = local;
+        out_cnt[q] = top_k;
+      }
+      continue;
+    }
+    if (r_need < n_unc) {
+      // exact scores of the listed blocks into the row, then the r_need best
+      // of them by (exact score desc, id asc): chosen ones marked +inf, the
+      // others -inf
+      rescore_list<DI, HP>(kv, qa, lane, list_s[wave], n_unc, trow, lut, wsq_s[wave], row);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      uint32_t k2[4], valid2 = 0u;
+      int c2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // lane l: list entries 4 l .. 4 l + 3 (ascending ids)
+        const int e = 4 * lane + i;
+        c2[i] = e < n_unc ? (int)list_s[wave][e] : 0;
+        k2[i] = e < n_unc ? order_key(row[c2[i]]) : 0u;
+        valid2 |= (e < n_unc) ? (1u << i) : 0u;
+      }
+      uint32_t T2, take2, o2;
+      wave_select<4>(k2, valid2, (uint32_t)r_need, hist4[wave], T2, take2);
+      const uint32_t keep2 = wave_keep<4>(k2, valid2, T2, take2, &o2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((valid2 >> i) & 1u) row[c2[i]] = ((keep2 >> i) & 1u) ? INFINITY : -INFINITY;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
+    // ---- output: the kept candidates in ascending id, then the local block.
+    // Kept: S^ > hi_thr (certainly in), or marked +inf, or -- when every
+    // undecided block is needed -- undecided.
+    const bool take_unc = r_need >= n_unc;
+    int at = 0;
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      const int c = 64 * m + lane;
+      const float x = c < n ? row[c] : -INFINITY;
+      const bool kp = c < n && (x > hi_thr || (take_unc && x >= lo_thr));
+      const unsigned long long km = __ballot(kp);
+      if (kp)
+        out[at + __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u))] = c;
+      at += __builtin_popcountll(km);
+    }
+    if (lane == 0) {
+      out[need] = local;  // the largest visible id: last in ascending order
+      out_cnt[q] = top_k;
+    }
+  }
+}
+
+template <int DI>
+hipError_t launch_di(const KvView& kv, const QView& Q, int top_k, int32_t* idx, int32_t* cnt,
+                     hipStream_t st) {
+  const dim3 grid((Q.nq + kQB - 1) / kQB), block(kThreads);
+  if (Q.hi <= 4)
+    hipLaunchKernelGGL((index_topk_fp8<DI, 4>), grid, block, 0, st, kv, Q, top_k, idx, cnt);
+  else if (Q.hi <= 8)
+    hipLaunchKernelGGL((index_topk_fp8<DI, 8>), grid, block, 0, st, kv, Q, top_k, idx, cnt);
+  else
+    hipLaunchKernelGGL((index_topk_fp8<DI, 16>), grid, block, 0, st, kv, Q, top_k, idx, cnt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool index_topk_fp8_supported(const KvView& kv, const QView& Q) {
+  // many queries (a prefill chunk): a workgroup per 8 queries, every
+  // sequence's scores in LDS
+  return Q.nq >= 256 && kv.maxb <= kMaxBlocks && (kv.idx_dim == 64 || kv.idx_dim == 128) &&
+         Q.hi >= 1 && Q.hi <= 16;
+}
+
+hipError_t launch_index_topk_fp8(const KvView& kv, const QView& Q, int top_k, int32_t* idx,
+                                 int32_t* cnt, hipStream_t st) {
+  return kv.idx_dim == 64 ? launch_di<64>(kv, Q, top_k, idx, cnt, st)
+                          : launch_di<128>(kv, Q, top_k, idx, cnt, st);
+}
+
+}  // namespace dsa

@@ -53,6 +53,20 @@ def oracle_query(w, qi, top_k=None, sel_override=None):
     return dict(cand=cand, scores=sc, idx=idx, cnt=cnt, out=out, lse=lse, local=loc)
 
 
+def oracle_select(w, qi, top_k=None):
+    """Oracle scores and selection (no attention) for query qi of workload w."""
+    from oracle import bf16_bits_to_f64, select_blocks
+    from oracle.pipeline import score_query
+
+    s = int(w.q_seq[qi])
+    pos = int(w.q_pos[qi])
+    k = w.top_k if top_k is None else top_k
+    cand, sc, loc = score_query(bf16_bits_to_f64(w.q_idx_bits[qi]), w.w[qi], w.block_table[s],
+                                pos, int(w.seq_lens[s]), w.block_size, w.idx_keys, w.idx_scale)
+    idx, cnt = select_blocks(cand, sc.astype(np.float32), loc, k)
+    return dict(cand=cand, scores=sc, idx=idx, cnt=cnt, local=loc)
+
+
 def check_scores_exact(gpu_row, ref, maxb):
     """GPU fp32 scores equal the oracle's float64 score rounded to fp32; -inf elsewhere."""
     row = np.asarray(gpu_row)
