@@ -19,7 +19,8 @@ import torch
 from . import _lib
 
 __all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
-           "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "index_topk",
+           "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "decode_fused_noalloc",
+           "index_topk",
            "workspace_size", "make_workspace", "KV_TOKEN_MAJOR", "KV_HEAD_MAJOR", "abi_version", "check_inputs",
            "kv_write", "index_key_write"]
 
@@ -231,6 +232,27 @@ def decode_fused(kv, qs, top_k, softmax_scale, out=None, lse=None, block_idx=Non
         lse.data_ptr(), block_idx.data_ptr() if block_idx is not None else None,
         block_cnt.data_ptr() if block_cnt is not None else None, workspace.data_ptr(),
         workspace.numel(), _stream(dev)))
+    return out, lse, block_idx, block_cnt
+
+
+def decode_fused_noalloc(kv, qs, top_k, softmax_scale, out=None, lse=None, block_idx=None,
+                         block_cnt=None):
+    """decode_fused without a workspace: the library's own per-GPU scratch
+    (dsa_sparse_decode_fused_noalloc; calls on one GPU must not overlap).
+    Returns (out, lse, block_idx, block_cnt) as decode_fused does."""
+    lib = _lib.load()
+    _check_tensors(block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.k_cache.device
+    nq, hq = qs.q.shape[0], qs.q.shape[1]
+    if out is None:
+        out = torch.empty(nq, hq, 128, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(nq, hq, dtype=torch.float32, device=dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_sparse_decode_fused_noalloc(
+        ctypes.byref(kvs), ctypes.byref(qss), top_k, float(softmax_scale), out.data_ptr(),
+        lse.data_ptr(), block_idx.data_ptr() if block_idx is not None else None,
+        block_cnt.data_ptr() if block_cnt is not None else None, _stream(dev)))
     return out, lse, block_idx, block_cnt
 
 

@@ -13,9 +13,11 @@ OP_ATTN_DECODE = 1
 OP_DECODE_FUSED = 2
 OP_INDEX_TOPK = 3
 OP_PREFILL_FUSED = 4
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # DSA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["dsa_index_score", "dsa_topk_blocks", "dsa_sparse_attn_decode",
-           "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_sparse_prefill_fused",
+           "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_sparse_decode_fused_noalloc",
+           "dsa_sparse_prefill_fused",
            "dsa_index_topk",
            "dsa_workspace_size", "dsa_check_inputs", "dsa_kv_write", "dsa_index_key_write",
            "dsa_mx_quantize", "dsa_mxfp4_to_fp8", "dsa_moe_workspace_size", "dsa_moe_grouped_gemm",
@@ -92,6 +94,7 @@ def load():
         "dsa_sparse_attn_decode": [kvp, qp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
         "dsa_sparse_attn_prefill": [kvp, qp, vp, vp, i32, f32, vp, vp, vp],
         "dsa_sparse_decode_fused": [kvp, qp, i32, f32, vp, vp, vp, vp, vp, sz, vp],
+        "dsa_sparse_decode_fused_noalloc": [kvp, qp, i32, f32, vp, vp, vp, vp, vp],
         "dsa_sparse_prefill_fused": [kvp, qp, i32, f32, vp, vp, vp, vp, vp, sz, vp],
         "dsa_index_topk": [kvp, qp, i32, vp, vp, vp, sz, vp],
         "dsa_workspace_size": [ctypes.c_int, kvp, qp, i32, P(sz)],

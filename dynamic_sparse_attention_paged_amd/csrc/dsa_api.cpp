@@ -5,6 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
 
@@ -212,6 +216,102 @@ FusedLayout fused_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_
   return f;
 }
 
+// Arguments of the fused decode, checked on the host (no GPU call).
+dsa_status check_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                              float* out, int32_t* block_idx_out, int32_t* block_cnt_out) {
+  dsa_status st = check_common(kv, qs, kNeedAttn | kNeedIndex);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!out) return fail(DSA_ERR_NULL, "out NULL");
+  if (!aligned(out, 4)) return fail(DSA_ERR_ALIGN, "out needs 4 B alignment");
+  if ((block_idx_out && !aligned(block_idx_out, 4)) || (block_cnt_out && !aligned(block_cnt_out, 4)))
+    return fail(DSA_ERR_ALIGN, "block_idx_out/block_cnt_out need 4 B alignment");
+  return DSA_OK;
+}
+
+// The fused decode on a checked call and a workspace of f.total bytes.
+dsa_status decode_fused_on(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
+                           float softmax_scale, float* out, float* lse, int32_t* block_idx_out,
+                           int32_t* block_cnt_out, const FusedLayout& f, char* ws,
+                           hipStream_t stream) {
+  float* scores = reinterpret_cast<float*>(ws + f.scores);
+  int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + f.idx);
+  int32_t* cnt = block_cnt_out ? block_cnt_out : reinterpret_cast<int32_t*>(ws + f.cnt);
+  const dsa::KvView kvv = kv_view(kv);
+  const dsa::QView qv = q_view(qs);
+  const bool split = f.attn.plan.splits > 1;
+  float* partials = split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr;
+  hipError_t e;
+  if (dsa::attn_score_supported(kvv, qv, top_k, f.attn.plan)) {
+    // short contexts, small grids: every attention workgroup scores and
+    // selects its query's blocks itself, in one launch
+    e = dsa::launch_sparse_attn_score(kvv, qv, top_k, softmax_scale, out, lse, partials,
+                                      f.attn.plan, block_idx_out, block_cnt_out, stream);
+    return hip_status(e, "fused: score + select + attention launch");
+  }
+  if (dsa::index_topk_fused_supported(kvv, qv)) {
+    // short contexts: scoring and selection in one kernel
+    e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
+  } else if (dsa::index_cand_topk_supported(kvv, qv, top_k)) {
+    // long contexts, small K: per-workgroup candidates, merged by the
+    // attention workgroups themselves, or else by a merging kernel first
+    if (dsa::attn_cand_supported(kvv, qv, top_k, f.attn.plan)) {
+      e = dsa::launch_index_cand_scores(kvv, qv, top_k, scores, stream);
+      if (e != hipSuccess) return hip_status(e, "fused: candidate scoring launch");
+      e = dsa::launch_sparse_attn_cand(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
+                                       f.attn.plan, block_idx_out, block_cnt_out, stream);
+      return hip_status(e, "fused: candidate merge + attention launch");
+    }
+    e = dsa::launch_index_cand_topk(kvv, qv, top_k, scores, idx, cnt, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: index_cand_topk launch");
+  } else {
+    e = dsa::launch_index_score(kvv, qv, scores, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
+    if (dsa::attn_select_supported(kvv, qv, top_k, f.attn.plan)) {
+      // the attention workgroups select their query's blocks themselves
+      e = dsa::launch_sparse_attn_select(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
+                                         f.attn.plan, block_idx_out, block_cnt_out, stream);
+      return hip_status(e, "fused: select + attention launch");
+    }
+    e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
+    if (e != hipSuccess) return hip_status(e, "fused: topk launch");
+  }
+  e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse, partials,
+                              f.attn.plan, stream);
+  return hip_status(e, "fused: attention launch");
+}
+
+// Scratch of dsa_sparse_decode_fused_noalloc: one array per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is a stand-in, not a device address): it uses the address
+// hipGetSymbolAddress returns for the current device, resolved once per
+// device and kept.
+static __device__ __align__(256) char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status scratch_of_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "noalloc: device %d beyond the %d this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DSA_ERR_HIP, "noalloc: scratch has no device address");
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -347,65 +447,34 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
                                    float softmax_scale, float* out, float* lse,
                                    int32_t* block_idx_out, int32_t* block_cnt_out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  dsa_status st = check_common(kv, qs, kNeedAttn | kNeedIndex);
+  dsa_status st = check_decode_fused(kv, qs, top_k, out, block_idx_out, block_cnt_out);
   if (st != DSA_OK) return st;
-  if ((st = check_topk(top_k)) != DSA_OK) return st;
-  if (!out) return fail(DSA_ERR_NULL, "out NULL");
-  if (!aligned(out, 4)) return fail(DSA_ERR_ALIGN, "out needs 4 B alignment");
-  if ((block_idx_out && !aligned(block_idx_out, 4)) || (block_cnt_out && !aligned(block_cnt_out, 4)))
-    return fail(DSA_ERR_ALIGN, "block_idx_out/block_cnt_out need 4 B alignment");
   const FusedLayout f = fused_layout(kv, qs, top_k);
   if (!workspace || workspace_bytes < f.total)
     return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, f.total);
   if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
   if (qs->num_queries == 0) return ok();
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + f.scores);
-  int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + f.idx);
-  int32_t* cnt = block_cnt_out ? block_cnt_out : reinterpret_cast<int32_t*>(ws + f.cnt);
-  const dsa::KvView kvv = kv_view(kv);
-  const dsa::QView qv = q_view(qs);
-  const bool split = f.attn.plan.splits > 1;
-  float* partials = split ? reinterpret_cast<float*>(ws + f.attn.partials) : nullptr;
-  hipError_t e;
-  if (dsa::attn_score_supported(kvv, qv, top_k, f.attn.plan)) {
-    // short contexts, small grids: every attention workgroup scores and
-    // selects its query's blocks itself, in one launch
-    e = dsa::launch_sparse_attn_score(kvv, qv, top_k, softmax_scale, out, lse, partials,
-                                      f.attn.plan, block_idx_out, block_cnt_out, stream);
-    return hip_status(e, "fused: score + select + attention launch");
-  }
-  if (dsa::index_topk_fused_supported(kvv, qv)) {
-    // short contexts: scoring and selection in one kernel
-    e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
-    if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
-  } else if (dsa::index_cand_topk_supported(kvv, qv, top_k)) {
-    // long contexts, small K: per-workgroup candidates, merged by the
-    // attention workgroups themselves, or else by a merging kernel first
-    if (dsa::attn_cand_supported(kvv, qv, top_k, f.attn.plan)) {
-      e = dsa::launch_index_cand_scores(kvv, qv, top_k, scores, stream);
-      if (e != hipSuccess) return hip_status(e, "fused: candidate scoring launch");
-      e = dsa::launch_sparse_attn_cand(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
-                                       f.attn.plan, block_idx_out, block_cnt_out, stream);
-      return hip_status(e, "fused: candidate merge + attention launch");
-    }
-    e = dsa::launch_index_cand_topk(kvv, qv, top_k, scores, idx, cnt, stream);
-    if (e != hipSuccess) return hip_status(e, "fused: index_cand_topk launch");
-  } else {
-    e = dsa::launch_index_score(kvv, qv, scores, stream);
-    if (e != hipSuccess) return hip_status(e, "fused: index_score launch");
-    if (dsa::attn_select_supported(kvv, qv, top_k, f.attn.plan)) {
-      // the attention workgroups select their query's blocks themselves
-      e = dsa::launch_sparse_attn_select(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
-                                         f.attn.plan, block_idx_out, block_cnt_out, stream);
-      return hip_status(e, "fused: select + attention launch");
-    }
-    e = dsa::launch_topk(scores, kvv, qv, top_k, idx, cnt, stream);
-    if (e != hipSuccess) return hip_status(e, "fused: topk launch");
-  }
-  e = dsa::launch_sparse_attn(kvv, qv, idx, cnt, top_k, softmax_scale, out, lse, partials,
-                              f.attn.plan, stream);
-  return hip_status(e, "fused: attention launch");
+  return decode_fused_on(kv, qs, top_k, softmax_scale, out, lse, block_idx_out, block_cnt_out, f,
+                         static_cast<char*>(workspace), stream);
+}
+
+dsa_status dsa_sparse_decode_fused_noalloc(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                           int32_t top_k, float softmax_scale, float* out,
+                                           float* lse, int32_t* block_idx_out,
+                                           int32_t* block_cnt_out, hipStream_t stream) {
+  dsa_status st = check_decode_fused(kv, qs, top_k, out, block_idx_out, block_cnt_out);
+  if (st != DSA_OK) return st;
+  const FusedLayout f = fused_layout(kv, qs, top_k);
+  if (f.total > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "the call needs %zu B of scratch, more than the %d B this entry point holds; "
+                "use dsa_sparse_decode_fused with a workspace",
+                f.total, DSA_NOALLOC_SCRATCH_BYTES);
+  if (qs->num_queries == 0) return ok();
+  char* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != DSA_OK) return st;
+  return decode_fused_on(kv, qs, top_k, softmax_scale, out, lse, block_idx_out, block_cnt_out, f,
+                         ws, stream);
 }
 
 dsa_status dsa_index_topk(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,

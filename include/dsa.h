@@ -29,7 +29,9 @@
  *     seq_lens[s] <= max_blocks_per_seq * block_size, q_pos < seq_lens[q_seq],
  *     and all floating inputs must be finite.  Violations are undefined.
  *   - Entry points keep no state between calls and are thread-safe; calls
- *     sharing a workspace buffer must be ordered on one stream.
+ *     sharing a workspace buffer must be ordered on one stream.  The one
+ *     exception is dsa_sparse_decode_fused_noalloc, whose scratch lives in the
+ *     library (see its declaration).
  */
 #ifndef DSA_H
 #define DSA_H
@@ -201,6 +203,26 @@ dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs
                                    float softmax_scale, float* out, float* lse,
                                    int32_t* block_idx_out, int32_t* block_cnt_out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_decode_fused without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid it.  The same results
+ * as dsa_sparse_decode_fused.  Its scratch (split partials, scores or
+ * candidate lists, the selection) is one array of DSA_NOALLOC_SCRATCH_BYTES
+ * in the library's device memory, one per GPU, held until the process ends;
+ * a call needing more (dsa_workspace_size(DSA_OP_DECODE_FUSED) larger than
+ * that) returns DSA_ERR_UNSUPPORTED before anything is enqueued.  Every call
+ * on a GPU uses that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be made.
+ * The first call on a device looks up the array's address there (a host
+ * query); nothing is ever allocated, freed, copied or cleared.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+dsa_status dsa_sparse_decode_fused_noalloc(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                           int32_t top_k, float softmax_scale, float* out,
+                                           float* lse, int32_t* block_idx_out,
+                                           int32_t* block_cnt_out, hipStream_t stream);
 
 /*
  * One-call chunked prefill ([P1] section 4(3): prefill is compute-intensive,

@@ -268,3 +268,15 @@ def test_moe_validation(lib):
     assert lib.dsa_mxfp4_to_fp8(ctypes.byref(w), None, 2, FAKE, FAKE, None) == E["DSA_ERR_NULL"]
     assert lib.dsa_mxfp4_to_fp8(ctypes.byref(w), FAKE, 0, None, None, None) == 0
 
+
+
+def test_noalloc_rejects_oversized_scratch(lib):
+    """The fused decode without a workspace refuses, before touching the GPU, a
+    call whose scratch would exceed the library's per-GPU array."""
+    kv = _kv(num_seqs=4096, max_blocks_per_seq=8192)
+    qs = _qs(num_queries=4096, num_q_heads=16, idx_heads=8)
+    rc = lib.dsa_sparse_decode_fused_noalloc(ctypes.byref(kv), ctypes.byref(qs), 8, 0.1, FAKE,
+                                             FAKE, None, None, None)
+    assert rc == -3
+    assert b"scratch" in lib.dsa_last_error()
+    assert _lib.NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024
