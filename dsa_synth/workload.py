@@ -248,6 +248,21 @@ def small_decode(seed=2001, lens=(64 * 7 - 17, 64 * 65, 64 * 130 - 63, 64, 1),
                  top_k=top_k, bs=bs)
 
 
+def shared_pool_decode(seed=2301, n_seqs=32, L=64 * 2100 + 5, pool_blocks=2300, hq=64, hkv=8,
+                       hi=8, di=128, top_k=32):
+    """Decode of n_seqs long sequences whose block tables all map into one
+    pool of pool_blocks blocks, each sequence through a permutation of its own
+    (blocks shared between sequences, as with a common prefix): a wide batch
+    without a pool per sequence."""
+    nb = -(-L // 64)
+    assert nb <= pool_blocks
+    table = np.zeros((n_seqs, nb), dtype=np.int64)
+    for s in range(n_seqs):
+        table[s] = gen.permutation(seed + 7 * s, gen.TAG_TABLE, pool_blocks)[:nb]
+    return build(f"shared_pool_decode_s{seed}", seed, [L] * n_seqs, table, pool_blocks, hq=hq,
+                 hkv=hkv, hi=hi, di=di, top_k=top_k)
+
+
 def small_prefill(seed=2101, L=64 * 20 - 5, count=200, hq=16, hkv=2, hi=4, di=128,
                   top_k=6, extra=3, bs=64):
     nb = -(-L // bs)

@@ -32,12 +32,16 @@
 #include "attn_tile.h"
 #include "cand_common.h"
 #include "dsa_internal.h"
+#include "score_common.h"
 #include "score_i8_lds.h"
 #include "select_common.h"
 
 namespace dsa {
 namespace {
 
+// split partials: one record per (query, head, split): m, l, o[128], two
+// floats of padding (16-byte records)
+constexpr int kPartStride = kHeadDim + 4;
 constexpr int kMaxSelectBlocks = 2048;  // selection inside attention: up to 2048 blocks
 constexpr int kMaxScoredBlocks = 256;  // scoring inside attention: up to 256 blocks
 // where the attention kernel gets its blocks from (see sparse_attn_split)
@@ -45,7 +49,7 @@ constexpr int kAttnGiven = 0, kAttnSelect = 1, kAttnScore = 2, kAttnCand = 3;
 
 using namespace tile;
 
-// grid (splits, Nq, Hkv), block 64 W.  splits > 1: partials [Nq][Hq][splits] x {m, l, o[128]}
+// grid (splits, Nq, Hkv), block 64 W.  splits > 1: partials [Nq][Hq][splits] records
 // kVBufs = 2: each wave double-buffers V in LDS, and the next block's K and V
 // are requested as soon as the current block's K has gone through the
 // logits MFMAs, so they arrive while the softmax and P V run.
@@ -69,12 +73,17 @@ using namespace tile;
 // kNT: the K/V tiles are read with the non-temporal cache policy (decode: each
 // selected block is streamed once per call); prefill keeps plain loads, since
 // the blocks its queries select overlap and are served again from the caches.
-template <int kAttnWaves, int kVBufs, int kMode, int DI, int HP, bool kNT>
-__global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
-    KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+//
+// attn_unit is one workgroup's work, split sp of query qi and KV head g.
+// kAttnGiven: the selection is given_sel[0 .. given_n).  kCohOut: the split
+// partials are written with agent-coherent stores (another workgroup of the
+// same launch merges them).
+template <int kAttnWaves, int kVBufs, int kMode, int DI, int HP, bool kNT, bool kCohOut = false>
+__device__ __forceinline__ void attn_unit(
+    const KvView& kv, const QView& Q, const int32_t* given_sel, int given_n,
     const float* __restrict__ scores, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
     int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, const int sp, const int qi, const int g) {
   constexpr bool kSelects = kMode != kAttnGiven;
   constexpr bool kScores = kMode == kAttnScore;
   // V staging: vs_a, and with kVBufs = 2 vs_b, one 16 KiB block per wave each
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   __shared__ int tab[kScores ? kMaxScoredBlocks : 1];
   __shared__ int cnt_lds;
 
-  const int sp = blockIdx.x, qi = blockIdx.y, g = blockIdx.z;
+  uint16_t* const vbase = &vs_a[0][0];  // kAttnWaves x 64 x 128 bf16
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform addresses
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, gq = lane >> 4;
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   if (kScores) {
     // Scoring scratch (digit table, scores, head weights) lives in the V
     // staging area, which is free until the gather starts.
-    uint32_t* lut = reinterpret_cast<uint32_t*>(&vs_a[0][0]);
+    uint32_t* lut = reinterpret_cast<uint32_t*>(vbase);
     float* sc = reinterpret_cast<float*>(lut + 256);
     double* wsq = reinterpret_cast<double*>(sc + kMaxScoredBlocks);
     const int local = pos >> kv.bs_shift;  // <= maxb - 1 < kMaxScoredBlocks (host check)
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       }
     } else {
       // merge scratch in the V staging area, free until the gather starts
-      uint32_t* ck = reinterpret_cast<uint32_t*>(&vs_a[0][0]);
+      uint32_t* ck = reinterpret_cast<uint32_t*>(vbase);
       int32_t* cj = reinterpret_cast<int32_t*>(ck + kMergeMaxCand);
       int* off = cj + kMergeMaxCand;
       uint32_t* k2 = reinterpret_cast<uint32_t*>(off + kMergeMaxCand + 4);
@@ -160,9 +169,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       int32_t* cpos = j2 + kMergeMaxCand;
       int* n2 = cpos + kMergeMaxCand;
       uint4* h4 = reinterpret_cast<uint4*>(n2 + 16);
-      static_assert((6 * kMergeMaxCand + 4 + 16) * 4 + kAttnWaves * 64 * 16 <=
-                        (int)sizeof(vs_a), "merge scratch fits the V staging area");
-      const CandScratch S{ck, cj, off, k2, j2, cpos, n2, h4};
+      int* rc = reinterpret_cast<int*>(h4 + kAttnWaves * 64);
+      static_assert((6 * kMergeMaxCand + 4 + 16 + kCandScratchExtraWords) * 4 +
+                            kAttnWaves * 64 * 16 <= kAttnWaves * 64 * kHeadDim * 2,
+                    "merge scratch fits the V staging area");
+      const CandScratch S{ck, cj, off, k2, j2, cpos, n2, h4, rc};
       const int nwg = (kv.maxb + kCandBlocks - 1) / kCandBlocks;
       const int c = merge_candidate_lists<kAttnWaves>(const_cast<float*>(scores), nwg, need, qi,
                                                       S, sel_lds);
@@ -185,8 +196,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       if (threadIdx.x == 0) cnt_out[qi] = n_sel;
     }
   } else {
-    n_sel = cnt[qi];
-    sel = idx + (size_t)qi * top_k;
+    n_sel = given_n;
+    sel = given_sel;
   }
   // A block of 64 m tokens (m = 1, 2, 4, 8) is m tiles of 64 tokens; the
   // splits and the waves share tiles.  The last selected block (the query's
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* vs = vs_a[wave];
+  uint16_t* vs = vbase + wave * 64 * kHeadDim;
   const size_t tok_stride = kv_tok_stride(kv);
   const uint32_t v_off = dma_v_lane_offset(tok_stride, lane);
   const uint32_t k_off = (uint32_t)(((size_t)r * tok_stride + 8 * gq) * 2);
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       my_j = (jb << sub_shift) | h;
       my_p = (trow[jb] << sub_shift) | h;
     }
-    if (kVBufs == 1) {
+    if constexpr (kVBufs == 1) {
       for (int i = 0; i < cn; ++i) {
         const int j = __builtin_amdgcn_readlane(my_j, i);
         const int p = __builtin_amdgcn_readlane(my_p, i);
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
 
   // ---- merge the four waves through LDS (reusing the V staging area)
   __syncthreads();
-  float* wo = reinterpret_cast<float*>(&vs_a[0][0]);  // [wave][16 heads][128]
+  float* wo = reinterpret_cast<float*>(vbase);  // [wave][16 heads][128]
   if (gq == 0) {
     wm[wave][r] = st.m;
     wl[wave][r] = st.l;
@@ -356,13 +367,92 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
       out[((size_t)qi * Q.hq + hg) * kHeadDim + d] = O / L;
       if (lse && d == 0) lse[(size_t)qi * Q.hq + hg] = (M + log2f(L)) * kLn2;
     } else {
-      float* pp = partials + (((size_t)qi * Q.hq + hg) * splits + sp) * (kHeadDim + 2);
-      pp[2 + d] = (L > 0.f) ? O / L : 0.f;
+      float* pp = partials + (((size_t)qi * Q.hq + hg) * splits + sp) * kPartStride;
+      st_maybe_coh<kCohOut>(pp + 2 + d, (L > 0.f) ? O / L : 0.f);
       if (d == 0) {
-        pp[0] = M;
-        pp[1] = L;
+        st_maybe_coh<kCohOut>(pp, M);
+        st_maybe_coh<kCohOut>(pp + 1, L);
       }
     }
+  }
+}
+
+__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// this wave's stores are complete, and no memory access moves across
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// (m, l) pairs of a fused split merge held in LDS: G heads x splits
+constexpr int kFusedMergeMaxGS = 512;
+
+// done != nullptr (splits > 1, G splits <= kFusedMergeMaxGS): the split
+// partials are merged in this launch, by the last of a (query, KV head)'s
+// splits to finish: each split writes its partials with agent-coherent
+// stores, waits for them to complete and adds one to the pair's counter (a
+// 256-byte line of its own, zeroed before the launch); the one that brings
+// it to splits reads the partials back with coherent loads and writes out /
+// lse with the merge_splits rule, then zeroes the counter.  No workgroup
+// waits for another.
+template <int kAttnWaves, int kVBufs, int kMode, int DI, int HP, bool kNT>
+__global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
+    KvView kv, QView Q, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    const float* __restrict__ scores, int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out,
+    int top_k, float scale2, int splits, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ partials, uint32_t* __restrict__ done) {
+  const int qi = blockIdx.y, g = blockIdx.z;
+  const int32_t* given_sel = kMode == kAttnGiven ? idx + (size_t)qi * top_k : nullptr;
+  const int given_n = kMode == kAttnGiven ? cnt[qi] : 0;
+  constexpr bool kFuse = kMode == kAttnCand;
+  attn_unit<kAttnWaves, kVBufs, kMode, DI, HP, kNT, kFuse>(kv, Q, given_sel, given_n, scores,
+                                                           idx_out, cnt_out, top_k, scale2, splits,
+                                                           out, lse, partials, blockIdx.x, qi, g);
+  if (!kFuse || done == nullptr || splits == 1) return;
+  __shared__ float ml[2 * kFusedMergeMaxGS];
+  __shared__ int last_s;
+  const int tid = threadIdx.x;
+  uint32_t* ctr = done + ((size_t)qi * kv.num_kv_heads + g) * kDoneLineWords;
+  stores_done();
+  __syncthreads();
+  if (tid == 0) last_s = add_agent(ctr, 1u) == (uint32_t)(splits - 1);
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(last_s)) return;
+  const int G = Q.hq / kv.num_kv_heads;
+  const float* grp = partials + ((size_t)qi * Q.hq + g * G) * splits * kPartStride;
+  // every (head, split)'s m and l at once
+  for (int t = tid; t < G * splits; t += 64 * kAttnWaves) {
+    ml[2 * t] = ld_maybe_coh<true>(grp + (size_t)t * kPartStride);
+    ml[2 * t + 1] = ld_maybe_coh<true>(grp + (size_t)t * kPartStride + 1);
+  }
+  __syncthreads();
+  if (tid == 0) st_maybe_coh<true>(ctr, 0u);
+  for (int e = tid; e < G * kHeadDim; e += 64 * kAttnWaves) {
+    const int h = e / kHeadDim, d = e % kHeadDim;
+    const float* hm = ml + 2 * h * splits;
+    const float* po = grp + ((size_t)h * splits) * kPartStride + 2 + d;
+    float M = -INFINITY;
+    for (int i = 0; i < splits; ++i) M = fmaxf(M, hm[2 * i]);
+    float L = 0.f, O = 0.f;
+    // eight splits' o values in flight at a time
+    for (int i0 = 0; i0 < splits; i0 += 8) {
+      float o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        o[u] = i0 + u < splits ? ld_maybe_coh<true>(po + (size_t)(i0 + u) * kPartStride) : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u < splits) {
+          const float m = hm[2 * (i0 + u)];
+          const float f = (m == -INFINITY) ? 0.f : hm[2 * (i0 + u) + 1] * exp2f(m - M);
+          L += f;
+          O += f * o[u];
+        }
+      }
+    }
+    const int hg = g * G + h;
+    out[((size_t)qi * Q.hq + hg) * kHeadDim + d] = O / L;
+    if (lse && d == 0) lse[(size_t)qi * Q.hq + hg] = (M + log2f(L)) * kLn2;
   }
 }
 
@@ -372,12 +462,12 @@ __global__ __launch_bounds__(kHeadDim) void merge_splits(const float* __restrict
                                                          float* __restrict__ lse) {
   const int qh = blockIdx.x;
   const int d = threadIdx.x;
-  const float* pp = partials + (size_t)qh * splits * (kHeadDim + 2);
+  const float* pp = partials + (size_t)qh * splits * kPartStride;
   float M = -INFINITY;
-  for (int i = 0; i < splits; ++i) M = fmaxf(M, pp[i * (kHeadDim + 2)]);
+  for (int i = 0; i < splits; ++i) M = fmaxf(M, pp[i * kPartStride]);
   float L = 0.f, O = 0.f;
   for (int i = 0; i < splits; ++i) {
-    const float* q = pp + i * (kHeadDim + 2);
+    const float* q = pp + i * kPartStride;
     const float f = (q[0] == -INFINITY) ? 0.f : q[1] * exp2f(q[0] - M);
     L += f;
     O += f * q[2 + d];
@@ -433,7 +523,7 @@ AttnPlan attn_plan(int nq, int hkv, int tiles, bool prefill) {
 
 size_t attn_partials_bytes(int nq, int hq, int splits) {
   if (splits <= 1) return 0;
-  return (size_t)nq * hq * splits * (kHeadDim + 2) * sizeof(float);
+  return (size_t)nq * hq * splits * kPartStride * sizeof(float);
 }
 
 hipError_t launch_merge(const QView& Q, const float* partials, int splits, float* out, float* lse,
@@ -453,15 +543,15 @@ hipError_t launch_sparse_attn(const KvView& kv, const QView& Q, const int32_t* i
   if (plan.waves == 8) {
     hipLaunchKernelGGL((sparse_attn_split<8, 1, kAttnGiven, 0, 0, true>), grid, dim3(512), 0, st, kv,
                        Q, idx, cnt, nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse,
-                       partials);
+                       partials, nullptr);
   } else if (plan.stream) {
     hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnGiven, 0, 0, true>), grid, dim3(256), 0, st, kv,
                        Q, idx, cnt, nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse,
-                       partials);
+                       partials, nullptr);
   } else {
     hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnGiven, 0, 0, false>), grid, dim3(256), 0, st, kv,
                        Q, idx, cnt, nullptr, nullptr, nullptr, top_k, scale2, plan.splits, out, lse,
-                       partials);
+                       partials, nullptr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
@@ -482,7 +572,7 @@ hipError_t launch_sparse_attn_select(const KvView& kv, const QView& Q, const flo
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
   hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnSelect, 0, 0, true>), grid, dim3(256), 0, st, kv, Q, nullptr,
                      nullptr, scores, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
-                     partials);
+                     partials, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   return launch_merge(Q, partials, plan.splits, out, lse, st);
@@ -498,15 +588,15 @@ hipError_t launch_scored_di(const KvView& kv, const QView& Q, int top_k, float s
   if (Q.hi <= 4) {
     hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 4, true>), grid, block, 0, st,
                        kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2, splits,
-                       out, lse, partials);
+                       out, lse, partials, nullptr);
   } else if (Q.hi <= 8) {
     hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 8, true>), grid, block, 0, st,
                        kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2, splits,
-                       out, lse, partials);
+                       out, lse, partials, nullptr);
   } else {
     hipLaunchKernelGGL((sparse_attn_split<kWaves, kVBufs, kAttnScore, DI, 16, true>), grid, block, 0,
                        st, kv, Q, nullptr, nullptr, nullptr, idx_out, cnt_out, top_k, scale2,
-                       splits, out, lse, partials);
+                       splits, out, lse, partials, nullptr);
   }
   return hipGetLastError();
 }
@@ -555,17 +645,26 @@ bool attn_cand_supported(const KvView& kv, const QView& Q, int top_k, const Attn
   return plan.waves == 4 && top_k <= kMaxSelectBlocks && index_cand_topk_supported(kv, Q, top_k);
 }
 
+size_t attn_done_bytes(int nq, int hkv) {
+  return (size_t)nq * hkv * kDoneLineWords * sizeof(uint32_t);
+}
+
+bool attn_fused_merge(const QView& Q, int hkv, const AttnPlan& plan) {
+  return plan.splits > 1 && (long)(Q.hq / hkv) * plan.splits <= kFusedMergeMaxGS;
+}
+
 hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& Q, float* ws, int top_k,
                                    float scale, float* out, float* lse, float* partials,
                                    AttnPlan plan, int32_t* idx_out, int32_t* cnt_out,
-                                   hipStream_t st) {
+                                   uint32_t* done, hipStream_t st) {
   const float scale2 = scale * kLog2e;
   const dim3 grid(plan.splits, Q.nq, kv.num_kv_heads);
+  const bool fused = done != nullptr && attn_fused_merge(Q, kv.num_kv_heads, plan);
   hipLaunchKernelGGL((sparse_attn_split<4, 2, kAttnCand, 0, 0, true>), grid, dim3(256), 0, st, kv, Q,
                      nullptr, nullptr, ws, idx_out, cnt_out, top_k, scale2, plan.splits, out, lse,
-                     partials);
+                     partials, fused ? done : nullptr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.splits == 1) return e;
+  if (e != hipSuccess || plan.splits == 1 || fused) return e;
   return launch_merge(Q, partials, plan.splits, out, lse, st);
 }
 

@@ -202,7 +202,7 @@ PrefillLayout prefill_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int 
 
 struct FusedLayout {
   AttnLayout attn;
-  size_t scores, idx, cnt, total;
+  size_t scores, idx, cnt, sync, total;
 };
 
 FusedLayout fused_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_k) {
@@ -212,7 +212,9 @@ FusedLayout fused_layout(const dsa_paged_kv* kv, const dsa_queries* qs, int top_
   f.scores = align_up(f.attn.total);
   f.idx = align_up(f.scores + nq * kv->max_blocks_per_seq * sizeof(float));
   f.cnt = align_up(f.idx + nq * top_k * sizeof(int32_t));
-  f.total = align_up(f.cnt + nq * sizeof(int32_t));
+  f.sync = align_up(f.cnt + nq * sizeof(int32_t));
+  // split counters of the long-context path's attention launch
+  f.total = align_up(f.sync + dsa::attn_done_bytes(qs->num_queries, kv->num_kv_heads));
   return f;
 }
 
@@ -254,13 +256,15 @@ dsa_status decode_fused_on(const dsa_paged_kv* kv, const dsa_queries* qs, int32_
     e = dsa::launch_index_topk_fused(kvv, qv, top_k, idx, cnt, stream);
     if (e != hipSuccess) return hip_status(e, "fused: index_topk launch");
   } else if (dsa::index_cand_topk_supported(kvv, qv, top_k)) {
-    // long contexts, small K: per-workgroup candidates, merged by the
-    // attention workgroups themselves, or else by a merging kernel first
+    // long contexts, small K: per-chunk candidates, merged by the attention
+    // workgroups themselves (which also merge their splits), or else by a
+    // merging kernel first
     if (dsa::attn_cand_supported(kvv, qv, top_k, f.attn.plan)) {
-      e = dsa::launch_index_cand_scores(kvv, qv, top_k, scores, stream);
+      uint32_t* done = reinterpret_cast<uint32_t*>(ws + f.sync);
+      e = dsa::launch_index_cand_scores(kvv, qv, top_k, scores, done, stream);
       if (e != hipSuccess) return hip_status(e, "fused: candidate scoring launch");
       e = dsa::launch_sparse_attn_cand(kvv, qv, scores, top_k, softmax_scale, out, lse, partials,
-                                       f.attn.plan, block_idx_out, block_cnt_out, stream);
+                                       f.attn.plan, block_idx_out, block_cnt_out, done, stream);
       return hip_status(e, "fused: candidate merge + attention launch");
     }
     e = dsa::launch_index_cand_topk(kvv, qv, top_k, scores, idx, cnt, stream);

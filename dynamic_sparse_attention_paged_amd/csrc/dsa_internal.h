@@ -62,9 +62,11 @@ hipError_t launch_index_score_mfma(const KvView& kv, const QView& q, float* scor
 bool index_cand_topk_supported(const KvView& kv, const QView& q, int top_k);
 hipError_t launch_index_cand_topk(const KvView& kv, const QView& q, int top_k, float* ws,
                                   int32_t* idx, int32_t* cnt, hipStream_t s);
-// Only the scoring kernel of launch_index_cand_topk: the candidate lists in ws.
+// Only the scoring kernel of launch_index_cand_topk: the candidate lists in ws;
+// when done is given, it also zeroes the split counters (attn_done_bytes)
+// of the launch_sparse_attn_cand that follows.
 hipError_t launch_index_cand_scores(const KvView& kv, const QView& q, int top_k, float* ws,
-                                    hipStream_t s);
+                                    uint32_t* done, hipStream_t s);
 // Scoring and Top-K of one query per workgroup, scores kept on chip (same
 // results as launch_index_score followed by launch_topk).
 bool index_topk_fused_supported(const KvView& kv, const QView& q);
@@ -119,11 +121,16 @@ hipError_t launch_sparse_attn_score(const KvView& kv, const QView& q, int top_k,
 // Decode attention that first merges each query's candidate lists (as left
 // by launch_index_cand_scores in ws) into its selection, the same as
 // launch_index_cand_topk's; for the lists launch_index_cand_topk takes.
+// done (attn_done_bytes, zeroed by launch_index_cand_scores given the same
+// pointer): the split partials are merged inside this launch when
+// attn_fused_merge holds; nullptr: by a merging launch after it.
 bool attn_cand_supported(const KvView& kv, const QView& q, int top_k, const AttnPlan& plan);
+size_t attn_done_bytes(int nq, int hkv);
+bool attn_fused_merge(const QView& q, int hkv, const AttnPlan& plan);
 hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& q, float* ws, int top_k,
                                    float scale, float* out, float* lse, float* partials,
                                    AttnPlan plan, int32_t* idx_out, int32_t* cnt_out,
-                                   hipStream_t s);
+                                   uint32_t* done, hipStream_t s);
 
 // Paged write path (write.hip): token K/V rows into their blocks; per-block
 // coarse keys quantized to E4M3 with scale max|x| / 448.

@@ -29,6 +29,7 @@
 #include "dsa_internal.h"
 #include "score_common.h"
 #include "cand_common.h"
+#include "score_i8_lds.h"
 #include "select_common.h"
 
 namespace dsa {
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void topk_merge_candidates(
   __shared__ int off[kMergeMaxCand + 1];
   __shared__ int n2[kMergeWaves];
   __shared__ uint4 hist4[kMergeWaves * 64];
+  __shared__ int rc[kCandScratchExtraWords];
   const int tid = threadIdx.x, lane = tid & 63;
   const int qi = blockIdx.x;
   const int s = query_seq(Q, qi);
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void topk_merge_candidates(
     }
     return;
   }
-  const CandScratch S{ck, cj, off, k2, j2, pos, n2, hist4};
+  const CandScratch S{ck, cj, off, k2, j2, pos, n2, hist4, rc};
   const int c = merge_candidate_lists<kMergeWaves>(ws, nwg, need, qi, S, out);
   if (tid >= 64) return;
   if (lane == 0) {
@@ -79,127 +81,49 @@ __global__ __launch_bounds__(64 * kMergeWaves) void topk_merge_candidates(
 }
 
 // Lanes: 4 per block (dims DI/4 each); a lane holds NB blocks (16 apart), so a
-// wave covers 16 NB blocks and a workgroup 64 NB.
-//
-// kCand: instead of the score row, the workgroup writes its Top-K
-// candidates: the need best of its blocks below the local block (equal
-// scores to the lower id), as order-preserving keys and ids in increasing id
-// order, with their count (layout: cand_layout below).
-template <int DI, int HP, int NB, bool kCand>
+// wave covers 16 NB blocks and a workgroup 64 NB (score_chunk).  Blocks past
+// the local block score -inf.
+template <int DI, int HP, int NB>
 __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QView Q,
-                                                                   float* __restrict__ scores,
-                                                                   int need) {
+                                                                   float* __restrict__ scores) {
   __shared__ double qv[DI * HP];
-  __shared__ float scw[kCand ? 64 * NB : 1];
-  __shared__ uint4 hist4[kCand ? 64 : 1];
   __shared__ double sq[HP], wq[HP];
   __shared__ int expo[HP];
-  constexpr int kBlocksPerWg = 64 * NB;
-
-  const int qi = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gq = lane >> 4;
-  const int j0 = blockIdx.x * kBlocksPerWg + wave * 16 * NB + (lane & 15);
-  const int s = query_seq(Q, qi);
-  float* row = scores + (size_t)qi * kv.maxb;
-
-  // Block-table entries, key quarters and scales are requested first, before
-  // the query position is known (physical ids clamped into the pool, so the
-  // speculative reads stay in bounds), so that the table -> key chain
-  // overlaps the position read and the query prologue.
-  KeyQuarter<DI> kq[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int j = min(j0 + 16 * b, kv.maxb - 1);
-    kq[b].p = min(max(kv.table[(size_t)s * kv.maxb + j], 0), kv.num_blocks - 1);
-    const uint4* krow =
-        reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)kq[b].p * DI + gq * (DI / 4));
-#pragma unroll
-    for (int i = 0; i < DI / 64; ++i) kq[b].w[i] = krow[i];
-    kq[b].ks = gq == 0 ? kv.idx_scale[kq[b].p] : 0.f;
-  }
-  const int len = kv.seq_lens[s];
-  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
-  const int local = pos >> kv.bs_shift;
-
-  // Workgroups whose blocks are all invisible only write -inf (or no candidates).
-  if (blockIdx.x * kBlocksPerWg > local) {
-    if (kCand) {
-      if (threadIdx.x == 0) cand_count(scores, gridDim.x, need, qi)[blockIdx.x] = 0;
-      return;
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int j = j0 + 16 * b;
-      if (gq == 0 && j < kv.maxb) row[j] = -INFINITY;
-    }
-    return;
-  }
-  // invisible blocks score zero key words (their result is replaced by -inf)
+  const int qi = blockIdx.y, chunk = blockIdx.x;
+  float S[NB];
   bool visible[NB];
+  int local;
+  const bool any = score_chunk<DI, HP, NB>(kv, Q, qi, chunk, qv, sq, wq, expo, S, visible, local);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = chunk * 64 * NB + wave * 16 * NB + (lane & 15);
+  float* row = scores + (size_t)qi * kv.maxb;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int j = j0 + 16 * b;
-    visible[b] = j <= local && j < kv.maxb;
-    if (!visible[b]) {
-#pragma unroll
-      for (int i = 0; i < DI / 64; ++i) kq[b].w[i] = make_uint4(0u, 0u, 0u, 0u);
-      kq[b].ks = 0.f;
-    }
+    if ((lane >> 4) == 0 && j < kv.maxb) row[j] = (any && visible[b]) ? S[b] : -INFINITY;
   }
-  load_query<DI, HP>(Q, qi, qv, sq, wq, expo);
-  float S[NB];
-  score_quarters<DI, HP, NB>(kq, gq, qv, sq, wq, S);
-  if (!kCand) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int j = j0 + 16 * b;
-      if (gq == 0 && j < kv.maxb) row[j] = visible[b] ? S[b] : -INFINITY;
-    }
-    return;
-  }
-  // ---- candidates of this workgroup: blocks jbase + o, o < c (below local)
-  if (gq == 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) scw[wave * 16 * NB + (lane & 15) + 16 * b] = S[b];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const int jbase = blockIdx.x * kBlocksPerWg;
-  const int c = min(max(local - jbase, 0), kBlocksPerWg);
-  int32_t* cnt_out = cand_count(scores, gridDim.x, need, qi);
-  uint32_t* keys_out = cand_keys(scores, gridDim.x, need, qi) + (size_t)blockIdx.x * need;
-  int32_t* ids_out = cand_ids(scores, gridDim.x, need, qi) + (size_t)blockIdx.x * need;
-  uint32_t k[NB], valid = 0u;
-#pragma unroll
-  for (int m = 0; m < NB; ++m) {
-    const int o = lane * NB + m;
-    k[m] = order_key(scw[o]);
-    valid |= (o < c) ? (1u << m) : 0u;
-  }
-  if (c <= need) {  // all of them
-#pragma unroll
-    for (int m = 0; m < NB; ++m) {
-      const int o = lane * NB + m;
-      if (o < c) {
-        keys_out[o] = k[m];
-        ids_out[o] = jbase + o;
-      }
-    }
-    if (lane == 0) cnt_out[blockIdx.x] = c;
-    return;
-  }
-  uint32_t T, take_eq, o;
-  wave_select<NB>(k, valid, (uint32_t)need, hist4, T, take_eq);
-  const uint32_t keep = wave_keep<NB>(k, valid, T, take_eq, &o);
-#pragma unroll
-  for (int m = 0; m < NB; ++m)
-    if (((keep >> m) & 1u) && o < (uint32_t)need) {
-      keys_out[o] = k[m];
-      ids_out[o] = jbase + lane * NB + m;
-      ++o;
-    }
-  if (lane == 0) cnt_out[blockIdx.x] = need;
+}
+
+// grid (nwg, Nq), block 256: chunk `blockIdx.x` of query blockIdx.y scored on
+// the int8 matrix cores (score_chunk_i8: the same scores as above, bit for
+// bit), then its candidate list (chunk_candidates_lds; layout in
+// cand_common.h).  The chunk-0 workgroup of each query also zeroes that
+// query's split counters of the attention launch that follows (done:
+// nq x hkv counters, one per 256-byte line; nullptr when none follows).
+template <int DI, int HP>
+__global__ __launch_bounds__(256) void index_cand_scores(KvView kv, QView Q, float* __restrict__ ws,
+                                                         int need, uint32_t* __restrict__ done) {
+  __shared__ uint32_t lut[256];
+  __shared__ double wsq[16];
+  __shared__ float scw[256];
+  __shared__ uint4 hist4[64];
+  const int qi = blockIdx.y, chunk = blockIdx.x;
+  if (done && chunk == 0 && (int)threadIdx.x < kv.num_kv_heads)
+    done[((size_t)qi * kv.num_kv_heads + threadIdx.x) * kDoneLineWords] = 0u;
+  int local;
+  const bool any = score_chunk_i8<DI, HP>(kv, Q, qi, chunk, lut, wsq, scw, local);
+  if (any) __syncthreads();  // uniform: the scores are visible to wave 0
+  chunk_candidates_lds<4>(any, local, scw, hist4, ws, gridDim.x, need, qi, chunk);
 }
 
 template <int DI, int HP>
@@ -210,32 +134,30 @@ hipError_t launch_t(const KvView& kv, const QView& Q, float* scores, hipStream_t
   const long pairs = (long)Q.nq * kv.maxb;
   if (pairs >= 256L * 256) {
     dim3 grid((kv.maxb + 255) / 256, Q.nq);
-    hipLaunchKernelGGL((index_score_exact<DI, HP, 4, false>), grid, dim3(kScoreThreads), 0, st, kv,
-                       Q, scores, 0);
+    hipLaunchKernelGGL((index_score_exact<DI, HP, 4>), grid, dim3(kScoreThreads), 0, st, kv, Q,
+                       scores);
   } else {
     dim3 grid((kv.maxb + 63) / 64, Q.nq);
-    hipLaunchKernelGGL((index_score_exact<DI, HP, 1, false>), grid, dim3(kScoreThreads), 0, st, kv,
-                       Q, scores, 0);
+    hipLaunchKernelGGL((index_score_exact<DI, HP, 1>), grid, dim3(kScoreThreads), 0, st, kv, Q,
+                       scores);
   }
   return hipGetLastError();
 }
 
 template <int DI, int HP>
-hipError_t launch_cand_t(const KvView& kv, const QView& Q, int need, float* ws, hipStream_t st) {
-  static_assert(64 * 4 == kCandBlocks, "NB = 4: one list per 256-block workgroup");
+hipError_t launch_cand_t(const KvView& kv, const QView& Q, int need, float* ws, uint32_t* done,
+                         hipStream_t st) {
   dim3 grid((kv.maxb + kCandBlocks - 1) / kCandBlocks, Q.nq);
-  hipLaunchKernelGGL((index_score_exact<DI, HP, 4, true>), grid, dim3(kScoreThreads), 0, st, kv, Q,
-                     ws, need);
+  hipLaunchKernelGGL((index_cand_scores<DI, HP>), grid, dim3(256), 0, st, kv, Q, ws, need, done);
   return hipGetLastError();
 }
 
 template <int DI>
-hipError_t launch_cand_di(const KvView& kv, const QView& Q, int need, float* ws, hipStream_t st) {
-  if (Q.hi <= 1) return launch_cand_t<DI, 1>(kv, Q, need, ws, st);
-  if (Q.hi <= 2) return launch_cand_t<DI, 2>(kv, Q, need, ws, st);
-  if (Q.hi <= 4) return launch_cand_t<DI, 4>(kv, Q, need, ws, st);
-  if (Q.hi <= 8) return launch_cand_t<DI, 8>(kv, Q, need, ws, st);
-  return launch_cand_t<DI, 16>(kv, Q, need, ws, st);
+hipError_t launch_cand_di(const KvView& kv, const QView& Q, int need, float* ws, uint32_t* done,
+                          hipStream_t st) {
+  if (Q.hi <= 4) return launch_cand_t<DI, 4>(kv, Q, need, ws, done, st);
+  if (Q.hi <= 8) return launch_cand_t<DI, 8>(kv, Q, need, ws, done, st);
+  return launch_cand_t<DI, 16>(kv, Q, need, ws, done, st);
 }
 
 template <int DI>
@@ -260,16 +182,16 @@ bool index_cand_topk_supported(const KvView& kv, const QView& Q, int top_k) {
 }
 
 hipError_t launch_index_cand_scores(const KvView& kv, const QView& Q, int top_k, float* ws,
-                                    hipStream_t st) {
+                                    uint32_t* done, hipStream_t st) {
   const int need = top_k - 1;
-  return kv.idx_dim == 64 ? launch_cand_di<64>(kv, Q, need, ws, st)
-                          : launch_cand_di<128>(kv, Q, need, ws, st);
+  return kv.idx_dim == 64 ? launch_cand_di<64>(kv, Q, need, ws, done, st)
+                          : launch_cand_di<128>(kv, Q, need, ws, done, st);
 }
 
 hipError_t launch_index_cand_topk(const KvView& kv, const QView& Q, int top_k, float* ws,
                                   int32_t* idx, int32_t* cnt, hipStream_t st) {
   const int nwg = (kv.maxb + kCandBlocks - 1) / kCandBlocks;
-  hipError_t e = launch_index_cand_scores(kv, Q, top_k, ws, st);
+  hipError_t e = launch_index_cand_scores(kv, Q, top_k, ws, nullptr, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_merge_candidates, dim3(Q.nq), dim3(64 * kMergeWaves), 0, st, ws, kv, Q,
                      top_k, nwg, idx, cnt);

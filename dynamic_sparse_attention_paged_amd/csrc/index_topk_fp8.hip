@@ -463,6 +463,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       bins_s[wave][lane] = 0u;
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
+      wave_lds_fence();
       const float inv = 1.f / delta;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {
@@ -471,6 +472,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
+      wave_lds_fence();
       const uint32_t cum = wave_incl_scan(bins_s[wave][lane]);
       const unsigned long long hit = __ballot(cum >= (uint32_t)need);
       if (hit) {
@@ -507,6 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       qr.build(lut, lane, true, wsq_s[wave], qa);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): wsq and the list written
       __builtin_amdgcn_wave_barrier();
+      wave_lds_fence();
     }
     if (r_need < n_unc && n_unc > kListCap) {
       // Degenerate scores (for instance all equal, or all zero): too many
@@ -517,6 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
                              wsq_s[wave], row + base);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
+      wave_lds_fence();
       uint32_t k[32], valid = 0u;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {  // lane-major: candidate 32 lane + m
@@ -543,6 +547,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       rescore_list<DI, HP>(kv, qa, lane, list_s[wave], n_unc, trow, lut, wsq_s[wave], row);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
+      wave_lds_fence();
       uint32_t k2[4], valid2 = 0u;
       int c2[4];
 #pragma unroll
@@ -560,6 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
         if ((valid2 >> i) & 1u) row[c2[i]] = ((keep2 >> i) & 1u) ? INFINITY : -INFINITY;
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
+      wave_lds_fence();
     }
     // ---- output: the kept candidates in ascending id, then the local block.
     // Kept: S^ > hi_thr (certainly in), or marked +inf, or -- when every

@@ -155,4 +155,56 @@ __device__ __forceinline__ void score_quarters(const KeyQuarter<DI> (&kq)[NB], i
   }
 }
 
+// Exact scores of chunk `chunk` of query qi: logical blocks chunk 64 NB ..
+// + 64 NB, by a workgroup of four waves.  Lanes: four per block (key
+// quarters), each lane holding NB blocks 16 apart, so that wave w covers
+// blocks 16 NB w .. + 16 NB of the chunk and lane l's block b is
+// j(b) = chunk 64 NB + 16 NB w + l % 16 + 16 b.  Block-table entries, key
+// quarters and scales are requested first, before the query position is
+// known (physical ids clamped into the pool, so the speculative reads stay in
+// bounds), so that the table -> key chain overlaps the position read and the
+// query prologue.  Returns false, uniformly and before any LDS use, when the
+// whole chunk lies past the query's local block; otherwise S[b] (meaningful
+// in lane group 0) is block j(b)'s score and visible[b] whether j(b) is at or
+// below the local block (and inside the table row).  qv, sq, wq, expo: LDS
+// of load_query.
+template <int DI, int HP, int NB>
+__device__ __forceinline__ bool score_chunk(const KvView& kv, const QView& Q, int qi, int chunk,
+                                            double* qv, double* sq, double* wq, int* expo,
+                                            float (&S)[NB], bool (&visible)[NB], int& local) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gq = lane >> 4;
+  const int j0 = chunk * 64 * NB + wave * 16 * NB + (lane & 15);
+  const int s = query_seq(Q, qi);
+  KeyQuarter<DI> kq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = min(j0 + 16 * b, kv.maxb - 1);
+    kq[b].p = min(max(kv.table[(size_t)s * kv.maxb + j], 0), kv.num_blocks - 1);
+    const uint4* krow =
+        reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)kq[b].p * DI + gq * (DI / 4));
+#pragma unroll
+    for (int i = 0; i < DI / 64; ++i) kq[b].w[i] = krow[i];
+    kq[b].ks = gq == 0 ? kv.idx_scale[kq[b].p] : 0.f;
+  }
+  const int len = kv.seq_lens[s];
+  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  local = pos >> kv.bs_shift;
+  if (chunk * 64 * NB > local) return false;
+  // invisible blocks score zero key words (their result is ignored)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = j0 + 16 * b;
+    visible[b] = j <= local && j < kv.maxb;
+    if (!visible[b]) {
+#pragma unroll
+      for (int i = 0; i < DI / 64; ++i) kq[b].w[i] = make_uint4(0u, 0u, 0u, 0u);
+      kq[b].ks = 0.f;
+    }
+  }
+  load_query<DI, HP>(Q, qi, qv, sq, wq, expo);
+  score_quarters<DI, HP, NB>(kq, gq, qv, sq, wq, S);
+  return true;
+}
+
 }  // namespace dsa

@@ -90,6 +90,67 @@ struct QueryRows {
   }
 };
 
+// The exact scores of one 16-block column tile: kw / ks hold this lane's
+// key words (dims 16 gq .. +16 of every 64-wide chunk) and scale of block
+// column r, qa the query's digit planes, wh[i4] = wsq[4 gq + i4].  Returns,
+// in lane group HP / 4 - 1, the float64 score of column r (the ascending head
+// sum runs through the lane groups in order).
+template <int DI, int HP>
+__device__ __forceinline__ double tile_score_i8(const i32x4 (&qa)[DI / 64][3],
+                                                const uint4 (&kw)[DI / 64], float ks,
+                                                const uint32_t* lut, const double (&wh)[4],
+                                                int lane) {
+  constexpr int KC = DI / 64;
+  constexpr int kGroups = HP / 4;  // lane groups holding heads
+  const int gq = lane >> 4;
+  i32x4 kb[KC][3];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) planes_of(lut, kw[kc], kb[kc]);
+  // hi = G2 + 2^7 (G3 + 2^7 G4), lo = G0 + 2^7 G1 (exact in int32, |D| 2^18 < 2^44)
+  i32x4 h = i32x4{0, 0, 0, 0}, l = i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) h = mfma_i8(qa[kc][2], kb[kc][2], h);
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) l = mfma_i8(qa[kc][0], kb[kc][1], l);
+  h = h * 128;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    h = mfma_i8(qa[kc][1], kb[kc][2], h);
+    h = mfma_i8(qa[kc][2], kb[kc][1], h);
+    l = mfma_i8(qa[kc][1], kb[kc][0], l);
+  }
+  h = h * 128;
+  l = l * 128;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    h = mfma_i8(qa[kc][0], kb[kc][2], h);
+    h = mfma_i8(qa[kc][1], kb[kc][1], h);
+    h = mfma_i8(qa[kc][2], kb[kc][0], h);
+    l = mfma_i8(qa[kc][0], kb[kc][0], l);
+  }
+  // Lane (gq, r) holds heads 4 gq .. +3 of block column r; ks of that block
+  // sits in every lane of column r.  Group g continues the sum of group g - 1.
+  const double ksd = (double)ks;
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    double run = 0.0;
+    if (g > 0) run = __shfl(acc, (lane + 48) & 63, 64);  // the same column, group g - 1
+    if (gq == g) {
+#pragma clang fp contract(off)
+      acc = run;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const double D = fma((double)h[i4], 16384.0, (double)l[i4]);
+        const double y = ksd * D;
+        const double rr = y > 0.0 ? y : 0.0;
+        acc = acc + wh[i4] * rr;
+      }
+    }
+  }
+  return acc;
+}
+
 // Scores of blocks 0 .. local into sc[sc_slot(j)], by kWaves waves: 16-block
 // column tiles, tile t on wave t % kWaves.  tab[0 .. local] holds the
 // sequence's block-table row, lut the digit table and wsq the head weights
@@ -99,7 +160,7 @@ __device__ __forceinline__ void score_tiles_i8(const KvView& kv, const i32x4 (&q
                                                int wave, int lane, int local, const uint32_t* lut,
                                                const int* tab, const double* wsq, float* sc) {
   constexpr int KC = DI / 64;
-  constexpr int kGroups = HP / 4;  // lane groups holding heads
+  constexpr int kGroups = HP / 4;
   const int gq = lane >> 4, r = lane & 15;
   const int ntiles = local / 16 + 1;
   double wh[4];
@@ -125,52 +186,7 @@ __device__ __forceinline__ void score_tiles_i8(const KvView& kv, const i32x4 (&q
   };
   auto score_tile = [&](int i, const uint4 (&kw)[KC], float ks) {
     const int j = 16 * (wave + kWaves * i) + r;
-    i32x4 kb[KC][3];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) planes_of(lut, kw[kc], kb[kc]);
-    // hi = G2 + 2^7 (G3 + 2^7 G4), lo = G0 + 2^7 G1 (exact in int32, |D| 2^18 < 2^44)
-    i32x4 h = i32x4{0, 0, 0, 0}, l = i32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) h = mfma_i8(qa[kc][2], kb[kc][2], h);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) l = mfma_i8(qa[kc][0], kb[kc][1], l);
-    h = h * 128;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      h = mfma_i8(qa[kc][1], kb[kc][2], h);
-      h = mfma_i8(qa[kc][2], kb[kc][1], h);
-      l = mfma_i8(qa[kc][1], kb[kc][0], l);
-    }
-    h = h * 128;
-    l = l * 128;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      h = mfma_i8(qa[kc][0], kb[kc][2], h);
-      h = mfma_i8(qa[kc][1], kb[kc][1], h);
-      h = mfma_i8(qa[kc][2], kb[kc][0], h);
-      l = mfma_i8(qa[kc][0], kb[kc][0], l);
-    }
-    // Lane (gq, r) holds heads 4 gq .. +3 of block j (column r); ks of block
-    // j sits in every lane of column r.  The ascending head sum runs through
-    // the lane groups in order: group g continues the sum of group g - 1.
-    const double ksd = (double)ks;
-    double acc = 0.0;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      double run = 0.0;
-      if (g > 0) run = __shfl(acc, (lane + 48) & 63, 64);  // the same column, group g - 1
-      if (gq == g) {
-#pragma clang fp contract(off)
-        acc = run;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const double D = fma((double)h[i4], 16384.0, (double)l[i4]);
-          const double y = ksd * D;
-          const double rr = y > 0.0 ? y : 0.0;
-          acc = acc + wh[i4] * rr;
-        }
-      }
-    }
+    const double acc = tile_score_i8<DI, HP>(qa, kw, ks, lut, wh, lane);
     if (gq == kGroups - 1 && i < nt_w && j <= local) sc[sc_slot(j)] = (float)acc;
   };
   uint4 kwA[kPre][KC], kwB[kPre][KC];
@@ -188,6 +204,62 @@ __device__ __forceinline__ void score_tiles_i8(const KvView& kv, const i32x4 (&q
 #pragma unroll
     for (int u = 0; u < kPre; ++u) score_tile(i0 + kPre + u, kwB[u], ksB[u]);
   }
+}
+
+// Exact scores of chunk `chunk` of query qi, logical blocks chunk 256 ..
+// + 256, by a workgroup of four waves on the int8 matrix cores, into
+// sc[j - chunk 256] (LDS, 256 floats; entries of blocks past the local block
+// are not meaningful).  Wave w scores the 16-block tiles w, w + 4, w + 8,
+// w + 12 of the chunk; each lane reads the block-table entries of its four
+// columns itself (clamped into the row and the pool, so that reads of
+// invisible blocks stay in bounds), before the query's position is known.
+// lut (256 words) and wsq (16 doubles) are LDS scratch.  Returns false,
+// uniformly, when the whole chunk lies past the local block (sc untouched);
+// every thread must call it.
+template <int DI, int HP>
+__device__ __forceinline__ bool score_chunk_i8(const KvView& kv, const QView& Q, int qi, int chunk,
+                                               uint32_t* lut, double* wsq, float* sc, int& local) {
+  constexpr int KC = DI / 64;
+  constexpr int kGroups = HP / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gq = lane >> 4, r = lane & 15;
+  const int s = query_seq(Q, qi);
+  QueryRows<DI> qr;
+  qr.fetch(Q, qi, lane);
+  const int len = kv.seq_lens[s];
+  const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
+  const int32_t* trow = kv.table + (size_t)s * kv.maxb;
+  int p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = chunk * 256 + 16 * (wave + 4 * i) + r;
+    p[i] = min(max(trow[min(j, kv.maxb - 1)], 0), kv.num_blocks - 1);
+  }
+  uint4 kw[4][KC];
+  float ks[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4* krow = reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)p[i] * DI + 16 * gq);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) kw[i][kc] = krow[4 * kc];
+    ks[i] = kv.idx_scale[p[i]];
+  }
+  for (int c = threadIdx.x; c < 256; c += blockDim.x) lut[c] = digits_of_code((uint32_t)c);
+  __syncthreads();
+  local = pos >> kv.bs_shift;
+  if (chunk * 256 > local) return false;
+  i32x4 qa[KC][3];
+  qr.build(lut, lane, wave == 0, wsq, qa);
+  __syncthreads();
+  double wh[4];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) wh[i4] = wsq[(4 * gq + i4) & 15];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double acc = tile_score_i8<DI, HP>(qa, kw[i], ks[i], lut, wh, lane);
+    if (gq == kGroups - 1) sc[16 * (wave + 4 * i) + r] = (float)acc;
+  }
+  return true;
 }
 
 }  // namespace dsa

@@ -18,6 +18,16 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A hand-off of LDS data between the lanes of one wave: a fence at
+// wavefront scope.  The hardware completes a wave's LDS operations in order
+// (the fence emits at most a wait), but without it the compiler may move or
+// forward LDS accesses across the hand-off whenever it can assume that no
+// other lane writes the memory (seen: a histogram read sunk into the lanes
+// that had added to it, the other lanes reading back their own zeros).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave with DPP: Hillis-Steele
 // within each 16-lane row (row_shr 1, 2, 4, 8), then the row totals are
 // carried forward (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2
@@ -35,8 +45,9 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // Radix selection within one wave.  Lane l holds keys k[0..M) of candidate
 // positions l*M + m; bit m of `valid` marks real candidates.  Requires
 // need < number of valid keys.  Up to four 8-bit MSB-first passes over a
-// wave-private 256-bin LDS histogram `hist4` (64 x uint4; one wave, so LDS
-// operations complete in order and no barrier is needed).  Returns the key T
+// wave-private 256-bin LDS histogram `hist4` (64 x uint4; one wave: its LDS
+// operations complete in order, and wave_lds_fence orders them for the
+// compiler).  Returns the key T
 // of the need-th largest candidate and how many keys equal to T are kept.
 template <int M>
 __device__ __forceinline__ void wave_select(const uint32_t (&k)[M], uint32_t valid, uint32_t need,
@@ -75,10 +86,12 @@ __device__ __forceinline__ void wave_select(const uint32_t (&k)[M], uint32_t val
     const int width = shift < 0 ? 8 + shift : 8;
     const uint32_t wmask = ((1u << width) - 1u) << sh;
     hist4[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_fence();
 #pragma unroll
     for (int m = 0; m < M; ++m)
       if (((valid >> m) & 1u) && (k[m] & mask) == T)
         atomicAdd(&hist[(k[m] & wmask) >> sh], 1u);
+    wave_lds_fence();
     const uint4 h = hist4[lane];
     const uint32_t mine = h.x + h.y + h.z + h.w;
     const uint32_t incl = wave_incl_scan(mine);
