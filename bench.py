@@ -40,9 +40,11 @@ FP8_PEAK_TFLOPS = 5000.0
 INT8_PEAK_TOPS = 5000.0
 # what one fused step of the batched decode launches (the roofline's scope)
 STEP_KERNELS = "index_score_exact + sparse_attn_split (selects its blocks)"
-# the decode attention kernel's sources (the traffic counters are keyed to them)
+# the sources of the batched-decode step's kernels (the traffic counters are keyed to them)
 ATTN_SRCS = [os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", f)
-             for f in ("attn.hip", "attn_tile.h")]
+             for f in ("attn.hip", "attn_tile.h", "cand_common.h", "select_common.h",
+                       "score_common.h", "score_i8_lds.h", "digit_mfma.h", "dsa_internal.h",
+                       "index_score.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_attn_split_batched_decode.json")
 
 
@@ -242,17 +244,19 @@ KV_LAYOUT = 1
 
 
 def traffic_from_profile():
-    """Measured HBM bytes per launch of the attention kernel, if the counters in
-    profiles/ were taken on the current kernel source."""
+    """Measured HBM bytes (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on a
+    device copy) of the batched-decode step and of the given-list attention
+    kernel, if the counters in profiles/ were taken on the current sources:
+    (step_bytes, given_list_bytes), else (None, None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         src = hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()
-        if t.get("attn_src_sha256") != src or t.get("kv_layout") != LAYOUT_NAMES[KV_LAYOUT]:
-            return None
-        return t.get("bytes_per_launch")
+        if t.get("src_sha256") != src or t.get("kv_layout") != LAYOUT_NAMES[KV_LAYOUT]:
+            return None, None
+        return t.get("step_bytes"), t.get("given_list_bytes")
     except (OSError, ValueError):
-        return None
+        return None, None
 
 
 def _oracle_decode_loop(w, budget_s, qseed0):
@@ -700,7 +704,7 @@ def main():
     cnt = D.cnt[0].cpu().numpy()
     a_bytes = attn_bytes(w, cnt)
     path_bytes = a_bytes + index_bytes(w)
-    traffic = traffic_from_profile()
+    traffic, traffic_given = traffic_from_profile()
 
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -736,7 +740,8 @@ def main():
         "step_ms_flushed": dist(flushed),
         "roofline": hbm_roofline(path_bytes, step_mean, STEP_KERNELS, "step", ceil_gbps, traffic),
         "attention_kernel": hbm_roofline(a_bytes, dist(attn_t)["mean"],
-                                         "sparse_attn_split (given lists)", "kernel", ceil_gbps),
+                                         "sparse_attn_split (given lists)", "kernel", ceil_gbps,
+                                         traffic_given),
         "stages_ms": {"index_score": round(score_ms, 5), "topk": round(topk_ms, 5),
                       "sparse_attn": dist(attn_t)["mean"]},
         "ceilings": ceil,
