@@ -382,13 +382,17 @@ def hbm_roofline(nbytes, ms, kernel, scope, ceil_gbps=None, traffic=None):
 
 
 def decode_extra(w, steps, nsets, kv_layout=None, ceil_gbps=None):
-    """q/s and HBM GB/s of a decode workload through the fused entry point:
-    per-step HIP-event times (median, p10, p90), back to back and after a cache
-    flush, the roofline of the whole step against its algorithmic bytes, and
-    the attention kernel alone on the same selection."""
+    """q/s and HBM GB/s of a decode workload through the fused entry point.
+    The rate (ms_per_step, queries_per_s, the step roofline) comes from `steps`
+    back-to-back replays between two HIP events, as the headline figure does;
+    step_ms and step_ms_flushed are per-call HIP-event times (each replay
+    bracketed by its own events, so they include the launch gap a lone call
+    pays; the second after a cache flush).  The attention kernel is timed
+    alone on the same selection."""
     import torch
     D = Device(w, nsets, kv_layout=kv_layout)
     D.capture()
+    ms = event_time_ms(D.replay, steps, 3)
     b2b = step_times_ms(D.replay, steps, 3)
     fl = step_times_ms(D.replay, max(5, steps // 2), 1, flush=Flusher())
     D.select()
@@ -397,9 +401,8 @@ def decode_extra(w, steps, nsets, kv_layout=None, ceil_gbps=None):
     cnt = D.cnt[0].cpu().numpy()
     a_bytes = attn_bytes(w, cnt)
     byts = a_bytes + index_bytes(w)
-    ms = dist(b2b)["mean"]
     res = dict(workload=w.name, kv_layout=LAYOUT_NAMES[D.kv_layout], queries=w.num_queries,
-               ms_per_step=ms, step_ms=dist(b2b), step_ms_flushed=dist(fl),
+               ms_per_step=round(ms, 5), step_ms=dist(b2b), step_ms_flushed=dist(fl),
                queries_per_s=round(w.num_queries / (ms * 1e-3), 1),
                roofline=hbm_roofline(byts, ms, "dsa_sparse_decode_fused (every launch of the step)",
                                      "step", ceil_gbps),

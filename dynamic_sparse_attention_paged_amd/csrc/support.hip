@@ -17,6 +17,8 @@
 //     operands, unit scales) so that the host can compare its sums with the
 //     exact ones.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 #include <stdio.h>
 
@@ -63,38 +65,41 @@ __global__ __launch_bounds__(kThreads) void flush_write(u32x4* __restrict__ p, s
 }
 
 // kKind 0: FP8 scaled 16x16x128 (65536 flop); 1: int8 16x16x64 (32768 op);
-// 2: bf16 16x16x32 (16384 flop).  Eight independent accumulators per wave.
+// 2: bf16 16x16x32 (16384 flop).  Eight independent accumulators per wave,
+// of the instruction's own type only: with a second, unused accumulator set
+// live the compiler shuttles the accumulators between register files every
+// iteration and the loop measures those copies instead.
 template <int kKind>
 __global__ __launch_bounds__(kThreads) void mfma_rate(int iters, float* __restrict__ sink) {
+  using E = typename std::conditional<kKind == 1, int, float>::type;
+  using Acc = typename std::conditional<kKind == 1, i32x4, f32x4>::type;
   const int lane = threadIdx.x & 63;
-  f32x4 accf[8];
-  i32x4 acci[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    accf[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acci[u] = i32x4{0, 0, 0, 0};
-  }
   const int x = 0x38383838 ^ (lane << 3);  // E4M3 1.0-ish bytes, lane-varied
+  // distinct starting values: eight equal constants let the compiler merge
+  // and then re-split the accumulators with copies inside the loop
+  Acc acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = Acc{(E)(lane + u), (E)lane, (E)u, (E)1};
   const i32x8 a8 = {x, x, x, x, x, x, x, x};
   const i32x4 a4 = {x, x, x, x};
   const i16x8 ab = {(short)x, (short)x, (short)x, (short)x, (short)x, (short)x, (short)x, (short)x};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (kKind == 0)
-        accf[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, a8, accf[u], 0, 0, 0, 127, 0,
-                                                                     127);
-      else if (kKind == 1)
-        acci[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a4, a4, acci[u], 0, 0, 0);
+      if constexpr (kKind == 0)
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, a8, acc[u], 0, 0, 0, 127, 0,
+                                                                    127);
+      else if constexpr (kKind == 1)
+        acc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a4, a4, acc[u], 0, 0, 0);
       else
-        accf[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ab),
-                                                          __builtin_bit_cast(bf16x8, ab), accf[u],
-                                                          0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ab),
+                                                         __builtin_bit_cast(bf16x8, ab), acc[u], 0,
+                                                         0, 0);
     }
   }
   float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) s += accf[u][0] + (float)acci[u][0];
+  for (int u = 0; u < 8; ++u) s += (float)acc[u][0];
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
