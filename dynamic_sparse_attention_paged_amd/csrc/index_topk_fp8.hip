@@ -84,6 +84,25 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __builtin_bit_cast(float, u);
 }
 
+// Score rows in LDS are read lane-major (lane l: candidates 32 l .. 32 l + 31,
+// eight 16 B reads).  Block j is stored at slot j with its 16 B quad index
+// (bits 2-4) XORed with bits 5-7, so that the eight lanes of a 128 B group
+// read eight different quads of the 32 banks at every step.
+__device__ __forceinline__ int row_slot(int j) { return j ^ (((j >> 5) & 7) << 2); }
+
+// v[m] = score of candidate 32 lane + m (slots as row_slot; row 16 B aligned)
+__device__ __forceinline__ void read_row_lanes(const float* row, int lane, float (&v)[32]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 x =
+        *reinterpret_cast<const float4*>(row + 32 * lane + 4 * (k ^ (lane & 7)));
+    v[4 * k] = x.x;
+    v[4 * k + 1] = x.y;
+    v[4 * k + 2] = x.z;
+    v[4 * k + 3] = x.w;
+  }
+}
+
 // E4M3 codes of one row's 32 values x[0 .. 32) scaled by 2^-e, four a word.
 __device__ __forceinline__ void codes_of(const float (&x)[32], int e, int (&c)[8]) {
 #pragma unroll
@@ -98,8 +117,9 @@ __device__ __forceinline__ void codes_of(const float (&x)[32], int e, int (&c)[8
   }
 }
 
-// Exact scores of blocks j by one wave, written to row[j]: j = list[e] for e
-// in [0, n) (list != nullptr), or j = e (list == nullptr).  The int8
+// Exact scores of blocks j by one wave, written to row[row_slot(j)]: j =
+// list[e] for e in [0, n) (list != nullptr), or j = e (list == nullptr; row
+// then starts at a multiple of 256 blocks, so slots stay relative to it).  The int8
 // digit-plane products of score_i8_lds.h over 16-block tiles gathered from
 // the list; the scores are the oracle's float64 values rounded to fp32.
 template <int DI, int HP>
@@ -182,7 +202,7 @@ __device__ void rescore_list(const KvView& kv, const i32x4 (&qa)[DI / 64][3], in
           }
         }
       }
-      if (gq == kGroups - 1 && t0 + 16 * u + r < n) row[j[u]] = (float)acc;
+      if (gq == kGroups - 1 && t0 + 16 * u + r < n) row[row_slot(j[u])] = (float)acc;
     }
   }
 }
@@ -360,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
             tsum = fmaf(aw[g4][4 * t + i4], relu(acc[g4 * NT + t][i4]), tsum);
         const int ql = 4 * g4 + kg;
         const bool st = ok && ((pass >> ql) & 1u);
-        sc[st ? ql * kPitch + j : kQB * kPitch + tid] = ks * tsum;
+        sc[st ? ql * kPitch + row_slot(j) : kQB * kPitch + tid] = ks * tsum;
       }
     };
     // the MFMAs of tile u + 1 are issued before the epilogue of tile u, so the
@@ -438,14 +458,18 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
     qr.fetch(Q, q, lane);
     const int32_t* trow = kv.table + (size_t)s * kv.maxb;
     float* row = sc + ql * kPitch;
-    // candidate c = 64 m + lane: every LDS read of the row is one wave-wide
-    // contiguous read, and a decision over all candidates is 32 ballots
+    // lane l owns candidates 32 l .. 32 l + 31: decisions become per-lane bit
+    // masks (bit m: candidate 32 l + m), and one wave prefix sum over their
+    // counts places each lane's ids, which keeps every list ascending
+    const int c0 = 32 * lane;
+    const uint32_t valid_m =
+        n - c0 >= 32 ? 0xFFFFFFFFu : (n - c0 <= 0 ? 0u : (1u << (n - c0)) - 1u);
     float v[32];
+    read_row_lanes(row, lane, v);
     float mx = -INFINITY;
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const int c = 64 * m + lane;
-      v[m] = c < n ? row[c] : -INFINITY;
+      v[m] = ((valid_m >> m) & 1u) ? v[m] : -INFINITY;
       mx = fmaxf(mx, v[m]);
     }
 #pragma unroll
@@ -488,20 +512,26 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
     const float slack = (fabsf(mx) + fabsf(T_lo) + 2.f * E) * 9.5367431640625e-07f + 1e-30f;
     const float hi_thr = b_star >= 0 ? T_hi + 2.f * E + slack : INFINITY;
     const float lo_thr = b_star >= 0 ? T_lo - 2.f * E - slack : -INFINITY;
-    // ---- certainly in: S^ > hi_thr; undecided: lo_thr <= S^ <= hi_thr.  The
-    // undecided ids go to the list in ascending order.
-    int n_in = 0, n_unc = 0;
+    // ---- certainly in: S^ > hi_thr; undecided: lo_thr <= S^ <= hi_thr
+    uint32_t in_m = 0u, ge_m = 0u;
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const bool ok = 64 * m + lane < n;
-      n_in += __builtin_popcountll(__ballot(ok && v[m] > hi_thr));
-      const bool u = ok && v[m] >= lo_thr && !(v[m] > hi_thr);
-      const unsigned long long um = __ballot(u);
-      // (a list longer than kListCap is not used: its last slot may hold any id)
-      const int at = n_unc + __builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
-      if (u) list_s[wave][min(at, kListCap - 1)] = (uint16_t)(64 * m + lane);
-      n_unc += __builtin_popcountll(um);
+      in_m |= v[m] > hi_thr ? 1u << m : 0u;
+      ge_m |= v[m] >= lo_thr ? 1u << m : 0u;
+    }
+    in_m &= valid_m;
+    const uint32_t unc_m = ge_m & valid_m & ~in_m;
+    // one scan for both counts: undecided in the low 16 bits, certainly-in above
+    const uint32_t cu = (uint32_t)__builtin_popcount(unc_m);
+    const uint32_t incl = wave_incl_scan(cu | ((uint32_t)__builtin_popcount(in_m) << 16));
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const int n_in = (int)(tot >> 16), n_unc = (int)(tot & 0xFFFFu);
+    {
+      // the undecided ids, ascending (a list longer than kListCap is not used:
+      // its last slot may hold any id)
+      int at = (int)(incl & 0xFFFFu) - (int)cu;
+      for (uint32_t mm = unc_m; mm; mm &= mm - 1u, ++at)
+        list_s[wave][min(at, kListCap - 1)] = (uint16_t)(c0 + __builtin_ctz(mm));
     }
     const int r_need = need - n_in;
     i32x4 qa[KC][3];
@@ -521,30 +551,31 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
       wave_lds_fence();
-      uint32_t k[32], valid = 0u;
+      float x[32];
+      read_row_lanes(row, lane, x);
+      uint32_t k[32];
 #pragma unroll
-      for (int m = 0; m < 32; ++m) {  // lane-major: candidate 32 lane + m
-        const int c = 32 * lane + m;
-        k[m] = c < n ? order_key(row[c]) : 0u;
-        valid |= (c < n) ? (1u << m) : 0u;
-      }
+      for (int m = 0; m < 32; ++m) k[m] = ((valid_m >> m) & 1u) ? order_key(x[m]) : 0u;
       uint32_t T, take_eq, o;
-      wave_select<32>(k, valid, (uint32_t)need, hist4[wave], T, take_eq);
-      const uint32_t keep = wave_keep<32>(k, valid, T, take_eq, &o);
+      wave_select<32>(k, valid_m, (uint32_t)need, hist4[wave], T, take_eq);
+      const uint32_t keep = wave_keep<32>(k, valid_m, T, take_eq, &o);
 #pragma unroll
       for (int m = 0; m < 32; ++m)
-        if ((keep >> m) & 1u) out[o++] = 32 * lane + m;
+        if ((keep >> m) & 1u) out[o++] = c0 + m;
       if (lane == 0) {
         out[need] = local;
         out_cnt[q] = top_k;
       }
       continue;
     }
+    uint32_t keep_m = in_m | unc_m;  // every undecided block needed (r_need >= n_unc)
     if (r_need < n_unc) {
-      // exact scores of the listed blocks into the row, then the r_need best
-      // of them by (exact score desc, id asc): chosen ones marked +inf, the
-      // others -inf
+      // exact scores of the listed blocks into their slots of the row, then the
+      // r_need best of them by (exact score desc, id asc), marked in a
+      // wave-private mask word per owning lane
       rescore_list<DI, HP>(kv, qa, lane, list_s[wave], n_unc, trow, lut, wsq_s[wave], row);
+      uint32_t* chosen = bins_s[wave];
+      chosen[lane] = 0u;
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
       wave_lds_fence();
@@ -554,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       for (int i = 0; i < 4; ++i) {  // lane l: list entries 4 l .. 4 l + 3 (ascending ids)
         const int e = 4 * lane + i;
         c2[i] = e < n_unc ? (int)list_s[wave][e] : 0;
-        k2[i] = e < n_unc ? order_key(row[c2[i]]) : 0u;
+        k2[i] = e < n_unc ? order_key(row[row_slot(c2[i])]) : 0u;
         valid2 |= (e < n_unc) ? (1u << i) : 0u;
       }
       uint32_t T2, take2, o2;
@@ -562,26 +593,17 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       const uint32_t keep2 = wave_keep<4>(k2, valid2, T2, take2, &o2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if ((valid2 >> i) & 1u) row[c2[i]] = ((keep2 >> i) & 1u) ? INFINITY : -INFINITY;
+        if ((keep2 >> i) & 1u) atomicOr(&chosen[c2[i] >> 5], 1u << (c2[i] & 31));
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
       wave_lds_fence();
+      keep_m = in_m | (chosen[lane] & unc_m);
     }
-    // ---- output: the kept candidates in ascending id, then the local block.
-    // Kept: S^ > hi_thr (certainly in), or marked +inf, or -- when every
-    // undecided block is needed -- undecided.
-    const bool take_unc = r_need >= n_unc;
-    int at = 0;
-#pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const int c = 64 * m + lane;
-      const float x = c < n ? row[c] : -INFINITY;
-      const bool kp = c < n && (x > hi_thr || (take_unc && x >= lo_thr));
-      const unsigned long long km = __ballot(kp);
-      if (kp)
-        out[at + __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u))] = c;
-      at += __builtin_popcountll(km);
+    // ---- output: the kept candidates in ascending id, then the local block
+    {
+      const uint32_t ck = (uint32_t)__builtin_popcount(keep_m);
+      int o = (int)(wave_incl_scan(ck) - ck);
+      for (uint32_t mm = keep_m; mm; mm &= mm - 1u) out[o++] = c0 + __builtin_ctz(mm);
     }
     if (lane == 0) {
       out[need] = local;  // the largest visible id: last in ascending order
