@@ -118,23 +118,27 @@ __device__ __forceinline__ void codes_of(const float (&x)[32], int e, int (&c)[8
 }
 
 // Exact scores of blocks j by one wave, written to row[row_slot(j)]: j =
-// list[e] for e in [0, n) (list != nullptr), or j = e (list == nullptr; row
-// then starts at a multiple of 256 blocks, so slots stay relative to it).  The int8
-// digit-plane products of score_i8_lds.h over 16-block tiles gathered from
-// the list; the scores are the oracle's float64 values rounded to fp32.
+// list[e] for e in [0, n) (list != nullptr), or j = e (list == nullptr).  The int8 digit-plane products of score_i8_lds.h over 16-block tiles
+// gathered from the list; the scores are the oracle's float64 values rounded
+// to fp32.  When two queries' heads fit the 16 matrix rows (2 HP <= 16), rows
+// HP .. 2 HP - 1 of qa hold a second query's heads (QueryRows::fetch_pair),
+// whose scores of the same blocks go to row_b; a null row or row_b leaves
+// that query's scores unstored.
 template <int DI, int HP>
-__device__ void rescore_list(const KvView& kv, const i32x4 (&qa)[DI / 64][3], int lane,
+__device__ __forceinline__ void rescore_list(const KvView& kv, const i32x4 (&qa)[DI / 64][3], int lane,
                              const uint16_t* list, int n, const int32_t* trow,
-                             const uint32_t* lut, const double* wsq, float* row) {
+                             const uint32_t* lut, const double* wsq, float* row, float* row_b) {
   constexpr int KC = DI / 64;
-  constexpr int kGroups = HP / 4;
+  constexpr int kGroups = HP / 4;                  // lane groups holding one query's heads
+  constexpr int kAll = 2 * HP <= 16 ? 2 * kGroups : kGroups;
   const int gq = lane >> 4, r = lane & 15;
   double wh[4];
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) wh[i4] = wsq[(4 * gq + i4) & 15];
-  // four 16-block tiles at a time: list entries, then table entries, then key
-  // rows, each level's loads all in flight together
-  constexpr int kTiles = 4;
+  // eight 16-block tiles at a time (typically both lists of a query pair):
+  // list entries, then table entries, then key rows, each level's loads all
+  // in flight together
+  constexpr int kTiles = 8;
   for (int t0 = 0; t0 < n; t0 += 16 * kTiles) {
     int j[kTiles], p[kTiles];
     // (columns past the list repeat its last entry: every load is in range
@@ -187,9 +191,10 @@ __device__ void rescore_list(const KvView& kv, const i32x4 (&qa)[DI / 64][3], in
       const double ksd = (double)ks[u];
       double acc = 0.0;
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
+      for (int g = 0; g < kAll; ++g) {
         double run = 0.0;
-        if (g > 0) run = __shfl(acc, (lane + 48) & 63, 64);  // the same column, group g - 1
+        // the same column, group g - 1 (the second query's sum starts afresh)
+        if (g > 0 && g != kGroups) run = __shfl(acc, (lane + 48) & 63, 64);
         if (gq == g) {
 #pragma clang fp contract(off)
           acc = run;
@@ -202,10 +207,25 @@ __device__ void rescore_list(const KvView& kv, const i32x4 (&qa)[DI / 64][3], in
           }
         }
       }
-      if (gq == kGroups - 1 && t0 + 16 * u + r < n) row[row_slot(j[u])] = (float)acc;
+      const bool col = t0 + 16 * u + r < n;
+      if (row != nullptr && gq == kGroups - 1 && col) row[row_slot(j[u])] = (float)acc;
+      if (kAll > kGroups && row_b != nullptr && gq == kAll - 1 && col)
+        row_b[row_slot(j[u])] = (float)acc;
     }
   }
 }
+
+// One query's selection state after its classification (per lane: the
+// candidates 32 lane .. 32 lane + 31 as bits 0 .. 31 of each mask).
+struct Sel {
+  int q = -1;  // < 0: nothing left to do (no query, or its output is written)
+  int n = 0, local = 0;
+  uint32_t valid_m = 0u, in_m = 0u, unc_m = 0u;
+  int n_unc = 0, r_need = 0, lbase = 0;  // undecided ids at list [lbase, lbase + n_unc)
+  __device__ bool rescore() const { return q >= 0 && r_need < n_unc; }
+  // too many undecided blocks for the list: every candidate scored exactly
+  __device__ bool all_exact() const { return rescore() && n_unc > kListCap; }
+};
 
 // grid (ceil(Nq / kQB)), block 256.  HP (4, 8 or 16) >= HI heads a query.
 template <int DI, int HP>
@@ -218,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
   // score rows, then one slot per lane for the stores of columns that hold no
   // candidate (so that the epilogue needs no branch)
   __shared__ float sc[kQB * kPitch + kThreads];
-  __shared__ uint16_t list_s[kWaves][kListCap];
+  __shared__ uint16_t list_s[kWaves][2 * kListCap];  // a wave's two queries' lists
   __shared__ uint4 hist4[kWaves][64];  // radix histograms (wave_select)
   __shared__ uint32_t bins_s[kWaves][64];
   __shared__ uint32_t lut[256];
@@ -433,34 +453,45 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) ksm = fmaxf(ksm, ksmax_s[w]);
 
-  // ---- 3. selection, one query at a time per wave
-  for (int ql = wave; ql < kQB; ql += kWaves) {
+  // ---- 3. selection.  Wave w selects queries ql = w and w + kWaves, each
+  // classified on its own.  The exact rescoring of both runs as one pass when
+  // their heads fit the 16 matrix rows together (2 HP <= 16) and they share a
+  // table row; otherwise one list at a time.
+  constexpr bool kPair = 2 * HP <= 16;
+  const int need = top_k - 1;
+  uint16_t* const lists = list_s[wave];
+  auto lds_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    wave_lds_fence();
+  };
+
+  // Approximate-score classification of query ql: certainly in, undecided
+  // (its ids, ascending, to lists[lbase ..]) or out.  Writes the output of the
+  // cases that need no choice and returns q = -1 for them.
+  auto classify = [&](int ql, int lbase) -> Sel {
+    Sel S;
+    S.lbase = lbase;
     const int q = q0 + ql;
-    if (q >= Q.nq) break;
-    const int s = seq_s[ql], n = n_s[ql], local = n;
-    const int need = top_k - 1;
+    if (q >= Q.nq) return S;
+    const int n = n_s[ql], local = n;
     int32_t* out = out_idx + (size_t)q * top_k;
     if (n <= need) {
       for (int i = lane; i < top_k; i += 64) out[i] = i <= local ? i : -1;
       if (lane == 0) out_cnt[q] = local + 1;
-      continue;
+      return S;
     }
     if (need == 0) {
       if (lane == 0) {
         out[0] = local;
         out_cnt[q] = 1;
       }
-      continue;
+      return S;
     }
-    // the query rows of the exact rescoring, requested now so that they arrive
-    // during the selection
-    QueryRows<DI> qr;
-    qr.fetch(Q, q, lane);
-    const int32_t* trow = kv.table + (size_t)s * kv.maxb;
-    float* row = sc + ql * kPitch;
+    const float* row = sc + ql * kPitch;
     // lane l owns candidates 32 l .. 32 l + 31: decisions become per-lane bit
-    // masks (bit m: candidate 32 l + m), and one wave prefix sum over their
-    // counts places each lane's ids, which keeps every list ascending
+    // masks, and one wave prefix sum over their counts places each lane's
+    // ids, which keeps every list ascending
     const int c0 = 32 * lane;
     const uint32_t valid_m =
         n - c0 >= 32 ? 0xFFFFFFFFu : (n - c0 <= 0 ? 0u : (1u << (n - c0)) - 1u);
@@ -474,29 +505,25 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    // ---- bracket the need-th largest S^: a histogram of 64 bins of width
-    // delta below the maximum (bin = floor((max - S^) / delta)); the bin b
-    // holding rank `need` gives T_lo = max - (b + 1) delta and T_hi = max -
-    // b delta, each widened by eps for the rounding of the bin arithmetic, so
-    // that #{S^ >= T_lo} >= need and #{S^ > T_hi} <= need - 1.
+    // bracket the need-th largest S^: a histogram of 64 bins of width delta
+    // below the maximum (bin = floor((max - S^) / delta)); the bin b holding
+    // rank `need` gives T_lo = max - (b + 1) delta and T_hi = max - b delta,
+    // each widened by eps for the rounding of the bin arithmetic, so that
+    // #{S^ >= T_lo} >= need and #{S^ > T_hi} <= need - 1.
     const float E = cq_s[ql] * ksm;  // |S^ - S| <= E for every candidate
     float delta = fmaxf(0.5f * E, fmaxf(fabsf(mx) * 1.1920929e-07f, 1e-30f));
     int b_star = -1;
     float T_lo = 0.f, T_hi = 0.f;
     for (int tries = 0; tries < 40; ++tries) {  // delta x8 a try: ends once 64 bins hold rank need
       bins_s[wave][lane] = 0u;
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
-      wave_lds_fence();
+      lds_sync();
       const float inv = 1.f / delta;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {
         const float b = (mx - v[m]) * inv;  // +inf for the padding
         if (b < 64.f) atomicAdd(&bins_s[wave][(int)b], 1u);
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
-      wave_lds_fence();
+      lds_sync();
       const uint32_t cum = wave_incl_scan(bins_s[wave][lane]);
       const unsigned long long hit = __ballot(cum >= (uint32_t)need);
       if (hit) {
@@ -512,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
     const float slack = (fabsf(mx) + fabsf(T_lo) + 2.f * E) * 9.5367431640625e-07f + 1e-30f;
     const float hi_thr = b_star >= 0 ? T_hi + 2.f * E + slack : INFINITY;
     const float lo_thr = b_star >= 0 ? T_lo - 2.f * E - slack : -INFINITY;
-    // ---- certainly in: S^ > hi_thr; undecided: lo_thr <= S^ <= hi_thr
+    // certainly in: S^ > hi_thr; undecided: lo_thr <= S^ <= hi_thr
     uint32_t in_m = 0u, ge_m = 0u;
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
@@ -526,88 +553,149 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
     const uint32_t incl = wave_incl_scan(cu | ((uint32_t)__builtin_popcount(in_m) << 16));
     const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     const int n_in = (int)(tot >> 16), n_unc = (int)(tot & 0xFFFFu);
-    {
-      // the undecided ids, ascending (a list longer than kListCap is not used:
-      // its last slot may hold any id)
-      int at = (int)(incl & 0xFFFFu) - (int)cu;
-      for (uint32_t mm = unc_m; mm; mm &= mm - 1u, ++at)
-        list_s[wave][min(at, kListCap - 1)] = (uint16_t)(c0 + __builtin_ctz(mm));
-    }
-    const int r_need = need - n_in;
-    i32x4 qa[KC][3];
-    if (r_need < n_unc) {
-      qr.build(lut, lane, true, wsq_s[wave], qa);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): wsq and the list written
-      __builtin_amdgcn_wave_barrier();
-      wave_lds_fence();
-    }
-    if (r_need < n_unc && n_unc > kListCap) {
-      // Degenerate scores (for instance all equal, or all zero): too many
-      // undecided blocks for the list.  Score every candidate exactly and
-      // select from the exact scores alone.
-      for (int base = 0; base < n; base += 1024)
-        rescore_list<DI, HP>(kv, qa, lane, nullptr, min(1024, n - base), trow + base, lut,
-                             wsq_s[wave], row + base);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
-      wave_lds_fence();
+    // the undecided ids, ascending (a list longer than kListCap is not used:
+    // its last slot may hold any id)
+    int at = (int)(incl & 0xFFFFu) - (int)cu;
+    for (uint32_t mm = unc_m; mm; mm &= mm - 1u, ++at)
+      lists[lbase + min(at, kListCap - 1)] = (uint16_t)(c0 + __builtin_ctz(mm));
+    S.q = q;
+    S.n = n;
+    S.local = local;
+    S.valid_m = valid_m;
+    S.in_m = in_m;
+    S.unc_m = unc_m;
+    S.n_unc = n_unc;
+    S.r_need = need - n_in;
+    return S;
+  };
+
+  // The kept candidates of a classified query (exact scores of its undecided
+  // blocks already in its row), in ascending id, then the local block.
+  auto finish = [&](const Sel& S, int ql) {
+    int32_t* out = out_idx + (size_t)S.q * top_k;
+    const float* row = sc + ql * kPitch;
+    const int c0 = 32 * lane;
+    if (S.all_exact()) {
       float x[32];
       read_row_lanes(row, lane, x);
       uint32_t k[32];
 #pragma unroll
-      for (int m = 0; m < 32; ++m) k[m] = ((valid_m >> m) & 1u) ? order_key(x[m]) : 0u;
+      for (int m = 0; m < 32; ++m) k[m] = ((S.valid_m >> m) & 1u) ? order_key(x[m]) : 0u;
       uint32_t T, take_eq, o;
-      wave_select<32>(k, valid_m, (uint32_t)need, hist4[wave], T, take_eq);
-      const uint32_t keep = wave_keep<32>(k, valid_m, T, take_eq, &o);
+      wave_select<32>(k, S.valid_m, (uint32_t)need, hist4[wave], T, take_eq);
+      const uint32_t keep = wave_keep<32>(k, S.valid_m, T, take_eq, &o);
 #pragma unroll
       for (int m = 0; m < 32; ++m)
         if ((keep >> m) & 1u) out[o++] = c0 + m;
-      if (lane == 0) {
-        out[need] = local;
-        out_cnt[q] = top_k;
-      }
-      continue;
-    }
-    uint32_t keep_m = in_m | unc_m;  // every undecided block needed (r_need >= n_unc)
-    if (r_need < n_unc) {
-      // exact scores of the listed blocks into their slots of the row, then the
-      // r_need best of them by (exact score desc, id asc), marked in a
-      // wave-private mask word per owning lane
-      rescore_list<DI, HP>(kv, qa, lane, list_s[wave], n_unc, trow, lut, wsq_s[wave], row);
-      uint32_t* chosen = bins_s[wave];
-      chosen[lane] = 0u;
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
-      wave_lds_fence();
-      uint32_t k2[4], valid2 = 0u;
-      int c2[4];
+    } else {
+      uint32_t keep_m = S.in_m | S.unc_m;  // every undecided block needed (r_need >= n_unc)
+      if (S.rescore()) {
+        // the r_need best listed blocks by (exact score desc, id asc), marked
+        // in a wave-private mask word per owning lane
+        uint32_t* chosen = bins_s[wave];
+        chosen[lane] = 0u;
+        lds_sync();
+        const uint16_t* list = lists + S.lbase;
+        uint32_t k2[4], valid2 = 0u;
+        int c2[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {  // lane l: list entries 4 l .. 4 l + 3 (ascending ids)
-        const int e = 4 * lane + i;
-        c2[i] = e < n_unc ? (int)list_s[wave][e] : 0;
-        k2[i] = e < n_unc ? order_key(row[row_slot(c2[i])]) : 0u;
-        valid2 |= (e < n_unc) ? (1u << i) : 0u;
-      }
-      uint32_t T2, take2, o2;
-      wave_select<4>(k2, valid2, (uint32_t)r_need, hist4[wave], T2, take2);
-      const uint32_t keep2 = wave_keep<4>(k2, valid2, T2, take2, &o2);
+        for (int i = 0; i < 4; ++i) {  // lane l: list entries 4 l .. 4 l + 3 (ascending ids)
+          const int e = 4 * lane + i;
+          c2[i] = e < S.n_unc ? (int)list[e] : 0;
+          k2[i] = e < S.n_unc ? order_key(row[row_slot(c2[i])]) : 0u;
+          valid2 |= (e < S.n_unc) ? (1u << i) : 0u;
+        }
+        uint32_t T2, take2, o2;
+        wave_select<4>(k2, valid2, (uint32_t)S.r_need, hist4[wave], T2, take2);
+        const uint32_t keep2 = wave_keep<4>(k2, valid2, T2, take2, &o2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if ((keep2 >> i) & 1u) atomicOr(&chosen[c2[i] >> 5], 1u << (c2[i] & 31));
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
-      wave_lds_fence();
-      keep_m = in_m | (chosen[lane] & unc_m);
-    }
-    // ---- output: the kept candidates in ascending id, then the local block
-    {
+        for (int i = 0; i < 4; ++i)
+          if ((keep2 >> i) & 1u) atomicOr(&chosen[c2[i] >> 5], 1u << (c2[i] & 31));
+        lds_sync();
+        keep_m = S.in_m | (chosen[lane] & S.unc_m);
+      }
       const uint32_t ck = (uint32_t)__builtin_popcount(keep_m);
       int o = (int)(wave_incl_scan(ck) - ck);
       for (uint32_t mm = keep_m; mm; mm &= mm - 1u) out[o++] = c0 + __builtin_ctz(mm);
     }
     if (lane == 0) {
-      out[need] = local;  // the largest visible id: last in ascending order
-      out_cnt[q] = top_k;
+      out[need] = S.local;  // the largest visible id: last in ascending order
+      out_cnt[S.q] = top_k;
+    }
+  };
+
+  if constexpr (kPair) {
+    const int qla = wave, qlb = wave + kWaves;
+    // both queries' rows for the exact rescoring, requested first so that
+    // they arrive during the classification
+    QueryRows<DI> qr;
+    qr.fetch_pair(Q, q0 + qla < Q.nq ? q0 + qla : -1, q0 + qlb < Q.nq ? q0 + qlb : -1, HP, lane);
+    const Sel A = classify(qla, 0);
+    const bool la = A.rescore() && !A.all_exact();  // A rescored from its list
+    const Sel B = classify(qlb, la ? A.n_unc : 0);  // B's list right after A's
+    const bool lb = B.rescore() && !B.all_exact();
+    if (A.rescore() || B.rescore()) {
+      i32x4 qa[KC][3];
+      qr.build(lut, lane, true, wsq_s[wave], qa);
+      lds_sync();  // wsq and the lists written
+      float* rowa = sc + qla * kPitch;
+      float* rowb = sc + qlb * kPitch;
+      const int32_t* trowa = kv.table + (size_t)seq_s[qla] * kv.maxb;
+      const int32_t* trowb = kv.table + (size_t)seq_s[qlb] * kv.maxb;
+      // one pass over both lists when the queries share a table row: each
+      // query's exact scores of all listed blocks go to its own row (those of
+      // the other query's blocks are never read)
+      const bool joint = la && lb && seq_s[qla] == seq_s[qlb];
+      // Up to four jobs through one call site: A's and B's candidates all
+      // scored exactly (all_exact), A's list (or both lists), B's list.
+      for (int jb = 0; jb < 4; ++jb) {
+        const uint16_t* list = nullptr;
+        int cnt = 0;
+        const int32_t* trow = trowa;
+        float* ra = nullptr;
+        float* rb = nullptr;
+        if (jb == 0 && A.all_exact()) {
+          cnt = A.n;
+          ra = rowa;
+        } else if (jb == 1 && B.all_exact()) {
+          cnt = B.n;
+          trow = trowb;
+          rb = rowb;
+        } else if (jb == 2 && la) {
+          list = lists + A.lbase;
+          cnt = joint ? A.n_unc + B.n_unc : A.n_unc;
+          ra = rowa;
+          rb = joint ? rowb : nullptr;
+        } else if (jb == 3 && lb && !joint) {
+          list = lists + B.lbase;
+          cnt = B.n_unc;
+          trow = trowb;
+          rb = rowb;
+        }
+        if (cnt > 0) rescore_list<DI, HP>(kv, qa, lane, list, cnt, trow, lut, wsq_s[wave], ra, rb);
+      }
+      lds_sync();
+    }
+    if (A.q >= 0) finish(A, qla);
+    if (B.q >= 0) finish(B, qlb);
+  } else {
+    for (int ql = wave; ql < kQB; ql += kWaves) {
+      if (q0 + ql >= Q.nq) break;
+      QueryRows<DI> qr;
+      qr.fetch(Q, q0 + ql, lane);
+      const Sel S = classify(ql, 0);
+      if (S.rescore()) {
+        i32x4 qa[KC][3];
+        qr.build(lut, lane, true, wsq_s[wave], qa);
+        lds_sync();  // wsq and the list written
+        // the listed blocks, or (all_exact) every candidate
+        rescore_list<DI, HP>(kv, qa, lane, S.all_exact() ? nullptr : lists,
+                             S.all_exact() ? S.n : S.n_unc,
+                             kv.table + (size_t)seq_s[ql] * kv.maxb, lut, wsq_s[wave],
+                             sc + ql * kPitch, nullptr);
+        lds_sync();
+      }
+      if (S.q >= 0) finish(S, ql);
     }
   }
 }

@@ -46,6 +46,25 @@ struct QueryRows {
     w = live ? Q.w[(size_t)qi * Q.hi + r] : 0.f;
   }
 
+  // Two queries' rows at once (at most hp heads each, 2 hp <= 16): lane
+  // (gq, r) takes head r of query q_a for r < hp and head r - hp of query
+  // q_b for hp <= r < 2 hp.  A query < 0, and heads past HI, give zero rows.
+  __device__ __forceinline__ void fetch_pair(const QView& Q, int q_a, int q_b, int hp,
+                                             int lane) {
+    const int gq = lane >> 4, r = lane & 15;
+    const bool second = r >= hp;
+    const int qi = second ? q_b : q_a, h = second ? r - hp : r;
+    live = qi >= 0 && h < Q.hi && r < 2 * hp;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        Q.q_idx + ((size_t)(live ? qi : 0) * Q.hi + (live ? h : 0)) * DI);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      raw[kc][0] = live ? src[8 * kc + 2 * gq] : make_uint4(0u, 0u, 0u, 0u);
+      raw[kc][1] = live ? src[8 * kc + 2 * gq + 1] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    w = live ? Q.w[(size_t)qi * Q.hi + h] : 0.f;
+  }
+
   // Quantize each head to E4M3 with its power-of-two scale 2^e (the smallest
   // with max |q| <= 448 2^e; round to nearest even) and split the codes into
   // digit planes.  When write_w, lane group 0 stores w[r] 2^(e - 18) to
