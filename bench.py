@@ -39,7 +39,7 @@ HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 INT8_PEAK_TOPS = 5000.0
 # what one fused step of the batched decode launches (the roofline's scope)
-STEP_KERNELS = "index_score_exact + sparse_attn_split (selects its blocks)"
+STEP_KERNELS = "index_score_i8_rows + sparse_attn_split (selects its blocks)"
 # the sources of the batched-decode step's kernels (the traffic counters are keyed to them)
 ATTN_SRCS = [os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", f)
              for f in ("attn.hip", "attn_tile.h", "cand_common.h", "select_common.h",

@@ -104,6 +104,27 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_exact(KvView kv, QV
   }
 }
 
+// grid (ceil(maxb / 64 kT), Nq), block 256: the rows of index_score_exact,
+// bit for bit, from the int8 matrix cores (score_chunk_i8: 18 int8 products
+// per 16 blocks instead of 256 float64 FMAs a lane).  Blocks past the local
+// block score -inf.
+template <int DI, int HP, int kT>
+__global__ __launch_bounds__(256) void index_score_i8_rows(KvView kv, QView Q,
+                                                           float* __restrict__ scores) {
+  __shared__ uint32_t lut[256];
+  __shared__ double wsq[16];
+  __shared__ float scw[64 * kT];
+  const int qi = blockIdx.y, chunk = blockIdx.x;
+  int local;
+  const bool any = score_chunk_i8<DI, HP, kT>(kv, Q, qi, chunk, lut, wsq, scw, local);
+  if (any) __syncthreads();  // uniform: the scores are visible to every wave
+  float* row = scores + (size_t)qi * kv.maxb;
+  for (int e = threadIdx.x; e < 64 * kT; e += 256) {
+    const int j = chunk * 64 * kT + e;
+    if (j < kv.maxb) row[j] = (any && j <= local) ? scw[e] : -INFINITY;
+  }
+}
+
 // grid (nwg, Nq), block 256: chunk `blockIdx.x` of query blockIdx.y scored on
 // the int8 matrix cores (score_chunk_i8: the same scores as above, bit for
 // bit), then its candidate list (chunk_candidates_lds; layout in
@@ -160,13 +181,22 @@ hipError_t launch_cand_di(const KvView& kv, const QView& Q, int need, float* ws,
   return launch_cand_t<DI, 16>(kv, Q, need, ws, done, st);
 }
 
+template <int DI, int HP>
+hipError_t launch_i8_rows_t(const KvView& kv, const QView& Q, float* scores, hipStream_t st) {
+  // one 16-block tile a wave: 64 blocks a workgroup
+  dim3 grid((kv.maxb + 63) / 64, Q.nq);
+  hipLaunchKernelGGL((index_score_i8_rows<DI, HP, 1>), grid, dim3(256), 0, st, kv, Q, scores);
+  return hipGetLastError();
+}
+
 template <int DI>
 hipError_t launch_di(const KvView& kv, const QView& Q, float* scores, hipStream_t st) {
   if (Q.hi <= 1) return launch_t<DI, 1>(kv, Q, scores, st);
   if (Q.hi <= 2) return launch_t<DI, 2>(kv, Q, scores, st);
-  if (Q.hi <= 4) return launch_t<DI, 4>(kv, Q, scores, st);
-  if (Q.hi <= 8) return launch_t<DI, 8>(kv, Q, scores, st);
-  return launch_t<DI, 16>(kv, Q, scores, st);
+  // four or more heads: the int8 matrix cores
+  if (Q.hi <= 4) return launch_i8_rows_t<DI, 4>(kv, Q, scores, st);
+  if (Q.hi <= 8) return launch_i8_rows_t<DI, 8>(kv, Q, scores, st);
+  return launch_i8_rows_t<DI, 16>(kv, Q, scores, st);
 }
 
 }  // namespace

@@ -225,21 +225,22 @@ __device__ __forceinline__ void score_tiles_i8(const KvView& kv, const i32x4 (&q
   }
 }
 
-// Exact scores of chunk `chunk` of query qi, logical blocks chunk 256 ..
-// + 256, by a workgroup of four waves on the int8 matrix cores, into
-// sc[j - chunk 256] (LDS, 256 floats; entries of blocks past the local block
-// are not meaningful).  Wave w scores the 16-block tiles w, w + 4, w + 8,
-// w + 12 of the chunk; each lane reads the block-table entries of its four
-// columns itself (clamped into the row and the pool, so that reads of
+// Exact scores of chunk `chunk` of query qi, logical blocks chunk 64 kT ..
+// + 64 kT, by a workgroup of four waves on the int8 matrix cores, into
+// sc[j - chunk 64 kT] (LDS, 64 kT floats; entries of blocks past the local
+// block are not meaningful).  Wave w scores the 16-block tiles w, w + 4, ..,
+// w + 4 (kT - 1) of the chunk; each lane reads the block-table entries of
+// its kT columns itself (clamped into the row and the pool, so that reads of
 // invisible blocks stay in bounds), before the query's position is known.
 // lut (256 words) and wsq (16 doubles) are LDS scratch.  Returns false,
 // uniformly, when the whole chunk lies past the local block (sc untouched);
 // every thread must call it.
-template <int DI, int HP>
+template <int DI, int HP, int kT = 4>
 __device__ __forceinline__ bool score_chunk_i8(const KvView& kv, const QView& Q, int qi, int chunk,
                                                uint32_t* lut, double* wsq, float* sc, int& local) {
   constexpr int KC = DI / 64;
   constexpr int kGroups = HP / 4;
+  constexpr int kChunkBlocks = 64 * kT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gq = lane >> 4, r = lane & 15;
   const int s = query_seq(Q, qi);
@@ -248,16 +249,16 @@ __device__ __forceinline__ bool score_chunk_i8(const KvView& kv, const QView& Q,
   const int len = kv.seq_lens[s];
   const int pos = Q.q_pos ? Q.q_pos[qi] : len - 1;
   const int32_t* trow = kv.table + (size_t)s * kv.maxb;
-  int p[4];
+  int p[kT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = chunk * 256 + 16 * (wave + 4 * i) + r;
+  for (int i = 0; i < kT; ++i) {
+    const int j = chunk * kChunkBlocks + 16 * (wave + 4 * i) + r;
     p[i] = min(max(trow[min(j, kv.maxb - 1)], 0), kv.num_blocks - 1);
   }
-  uint4 kw[4][KC];
-  float ks[4];
+  uint4 kw[kT][KC];
+  float ks[kT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kT; ++i) {
     const uint4* krow = reinterpret_cast<const uint4*>(kv.idx_keys + (size_t)p[i] * DI + 16 * gq);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) kw[i][kc] = krow[4 * kc];
@@ -266,7 +267,7 @@ __device__ __forceinline__ bool score_chunk_i8(const KvView& kv, const QView& Q,
   for (int c = threadIdx.x; c < 256; c += blockDim.x) lut[c] = digits_of_code((uint32_t)c);
   __syncthreads();
   local = pos >> kv.bs_shift;
-  if (chunk * 256 > local) return false;
+  if (chunk * kChunkBlocks > local) return false;
   i32x4 qa[KC][3];
   qr.build(lut, lane, wave == 0, wsq, qa);
   __syncthreads();
@@ -274,7 +275,7 @@ __device__ __forceinline__ bool score_chunk_i8(const KvView& kv, const QView& Q,
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) wh[i4] = wsq[(4 * gq + i4) & 15];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kT; ++i) {
     const double acc = tile_score_i8<DI, HP>(qa, kw[i], ks[i], lut, wh, lane);
     if (gq == kGroups - 1) sc[16 * (wave + 4 * i) + r] = (float)acc;
   }
