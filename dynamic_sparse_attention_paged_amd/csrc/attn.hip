@@ -410,6 +410,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
                                                            out, lse, partials, blockIdx.x, qi, g);
   if (!kFuse || done == nullptr || splits == 1) return;
   __shared__ float ml[2 * kFusedMergeMaxGS];
+  __shared__ float wf[kFusedMergeMaxGS];
+  __shared__ float hM[kFusedMergeMaxGS / 2], hL[kFusedMergeMaxGS / 2];  // per head (splits >= 2)
   __shared__ int last_s;
   const int tid = threadIdx.x;
   uint32_t* ctr = done + ((size_t)qi * kv.num_kv_heads + g) * kDoneLineWords;
@@ -420,39 +422,87 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   if (!__builtin_amdgcn_readfirstlane(last_s)) return;
   const int G = Q.hq / kv.num_kv_heads;
   const float* grp = partials + ((size_t)qi * Q.hq + g * G) * splits * kPartStride;
-  // every (head, split)'s m and l at once
-  for (int t = tid; t < G * splits; t += 64 * kAttnWaves) {
-    ml[2 * t] = ld_maybe_coh<true>(grp + (size_t)t * kPartStride);
-    ml[2 * t + 1] = ld_maybe_coh<true>(grp + (size_t)t * kPartStride + 1);
+  // kE output elements a thread, eight splits' o values at a time.  The
+  // first group's o values are requested together with every (head,
+  // split)'s m and l, so that a G <= 8, splits <= 8 merge waits for one
+  // round trip to memory.
+  constexpr int kE = 4, kT = 64 * kAttnWaves;
+  static_assert(kFusedMergeMaxGS <= 2 * kT, "at most two (m, l) pairs a thread");
+  const int GH = G * kHeadDim, GS = G * splits;
+  auto load_o = [&](int e0, int i0, float (&o)[kE][8]) {
+#pragma unroll
+    for (int x = 0; x < kE; ++x) {
+      const int e = min(e0 + x * kT, GH - 1);
+      const float* po = grp + ((size_t)(e / kHeadDim) * splits) * kPartStride + 2 + e % kHeadDim;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        o[x][u] = i0 + u < splits ? ld_maybe_coh<true>(po + (size_t)(i0 + u) * kPartStride) : 0.f;
+    }
+  };
+  float o[kE][8];
+  {
+    // (GS <= kFusedMergeMaxGS = 2 kT: at most two pairs a thread)
+    float mv[2], lv[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = tid + k * kT;
+      mv[k] = t < GS ? ld_maybe_coh<true>(grp + (size_t)t * kPartStride) : 0.f;
+      lv[k] = t < GS ? ld_maybe_coh<true>(grp + (size_t)t * kPartStride + 1) : 0.f;
+    }
+    load_o(tid, 0, o);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = tid + k * kT;
+      if (t < GS) {
+        ml[2 * t] = mv[k];
+        ml[2 * t + 1] = lv[k];
+      }
+    }
   }
   __syncthreads();
   if (tid == 0) st_maybe_coh<true>(ctr, 0u);
-  for (int e = tid; e < G * kHeadDim; e += 64 * kAttnWaves) {
-    const int h = e / kHeadDim, d = e % kHeadDim;
+  // per (head, split): its weight l 2^(m - M) (M the head's maximum m), and
+  // per head the sum L of its weights, in split order -- the merge_splits
+  // rule, evaluated once per head instead of once per output element
+  for (int t = tid; t < GS; t += kT) {
+    const int h = t / splits, i = t - h * splits;
     const float* hm = ml + 2 * h * splits;
-    const float* po = grp + ((size_t)h * splits) * kPartStride + 2 + d;
     float M = -INFINITY;
-    for (int i = 0; i < splits; ++i) M = fmaxf(M, hm[2 * i]);
-    float L = 0.f, O = 0.f;
-    // eight splits' o values in flight at a time
+    for (int k = 0; k < splits; ++k) M = fmaxf(M, hm[2 * k]);
+    const float m = hm[2 * i];
+    wf[t] = (m == -INFINITY) ? 0.f : hm[2 * i + 1] * exp2f(m - M);
+    if (i == 0) hM[h] = M;
+  }
+  __syncthreads();
+  for (int h = tid; h < G; h += kT) {
+    float L = 0.f;
+    for (int i = 0; i < splits; ++i) L += wf[h * splits + i];
+    hL[h] = L;
+    if (lse) lse[(size_t)qi * Q.hq + g * G + h] = (hM[h] + log2f(L)) * kLn2;
+  }
+  __syncthreads();
+  for (int e0 = tid; e0 < GH; e0 += kE * kT) {
+    float O[kE];
+#pragma unroll
+    for (int x = 0; x < kE; ++x) O[x] = 0.f;
     for (int i0 = 0; i0 < splits; i0 += 8) {
-      float o[8];
+      if (e0 != tid || i0 != 0) load_o(e0, i0, o);  // (the first group is loaded)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        o[u] = i0 + u < splits ? ld_maybe_coh<true>(po + (size_t)(i0 + u) * kPartStride) : 0.f;
+      for (int x = 0; x < kE; ++x) {
+        const int e = min(e0 + x * kT, GH - 1);
+        const float* hw = wf + (e / kHeadDim) * splits;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (i0 + u < splits) {
-          const float m = hm[2 * (i0 + u)];
-          const float f = (m == -INFINITY) ? 0.f : hm[2 * (i0 + u) + 1] * exp2f(m - M);
-          L += f;
-          O += f * o[u];
-        }
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u < splits) O[x] += hw[i0 + u] * o[x][u];
       }
     }
-    const int hg = g * G + h;
-    out[((size_t)qi * Q.hq + hg) * kHeadDim + d] = O / L;
-    if (lse && d == 0) lse[(size_t)qi * Q.hq + hg] = (M + log2f(L)) * kLn2;
+#pragma unroll
+    for (int x = 0; x < kE; ++x) {
+      const int e = e0 + x * kT;
+      if (e >= GH) break;
+      const int h = e / kHeadDim, d = e % kHeadDim;
+      out[((size_t)qi * Q.hq + g * G + h) * kHeadDim + d] = O[x] / hL[h];
+    }
   }
 }
 
