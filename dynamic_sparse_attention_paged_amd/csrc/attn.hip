@@ -92,6 +92,7 @@ __device__ __forceinline__ void attn_unit(
   __shared__ uint16_t vs_a[kAttnWaves][64 * kHeadDim];
   __shared__ uint16_t vs_b[kVBufs == 2 ? kAttnWaves : 1][kVBufs == 2 ? 64 * kHeadDim : 8];
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
+  __shared__ float wf_s[kAttnWaves][16], hl_s[16];  // the waves' merge, per head
   __shared__ int32_t sel_lds[kSelects ? kMaxSelectBlocks : 1];
   __shared__ uint4 hist4[kSelects ? 64 : 1];
   __shared__ int tab[kScores ? kMaxScoredBlocks : 1];
@@ -348,31 +349,45 @@ __device__ __forceinline__ void attn_unit(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wo[(wave * 16 + r) * kHeadDim + 16 * dt + 4 * gq + i] = st.o[dt][i];
   __syncthreads();
-  for (int e = threadIdx.x; e < G * kHeadDim; e += 64 * kAttnWaves) {
-    const int h = e / kHeadDim, d = e % kHeadDim;
+  // per head: the waves' maximum, each wave's scale 2^(m_w - M) and the
+  // scaled sum L, once (not per output element)
+  if ((int)threadIdx.x < G) {
+    const int h = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, wm[w][h]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
       // wave accumulators are unnormalised: sum_t 2^(x_t - m_w) V_t
       const float mw = wm[w][h];
       const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      wf_s[w][h] = f;
       L += f * wl[w][h];
-      O += f * wo[(w * 16 + h) * kHeadDim + d];
     }
+    hl_s[h] = L;
+    const int hg = g * G + h;
+    if (splits == 1) {
+      if (lse) lse[(size_t)qi * Q.hq + hg] = (M + log2f(L)) * kLn2;
+    } else {
+      float* pp = partials + (((size_t)qi * Q.hq + hg) * splits + sp) * kPartStride;
+      st_maybe_coh<kCohOut>(pp, M);
+      st_maybe_coh<kCohOut>(pp + 1, L);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * kHeadDim; e += 64 * kAttnWaves) {
+    const int h = e / kHeadDim, d = e % kHeadDim;
+    float O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) O += wf_s[w][h] * wo[(w * 16 + h) * kHeadDim + d];
+    const float L = hl_s[h];
     const int hg = g * G + h;
     if (splits == 1) {
       out[((size_t)qi * Q.hq + hg) * kHeadDim + d] = O / L;
-      if (lse && d == 0) lse[(size_t)qi * Q.hq + hg] = (M + log2f(L)) * kLn2;
     } else {
       float* pp = partials + (((size_t)qi * Q.hq + hg) * splits + sp) * kPartStride;
       st_maybe_coh<kCohOut>(pp + 2 + d, (L > 0.f) ? O / L : 0.f);
-      if (d == 0) {
-        st_maybe_coh<kCohOut>(pp, M);
-        st_maybe_coh<kCohOut>(pp + 1, L);
-      }
     }
   }
 }
