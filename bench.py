@@ -11,8 +11,9 @@ consecutive steps select different blocks (the 256 MiB last-level cache
 cannot serve a step from the previous one).
 
 Printed: one JSON line with queries/s (K back-to-back steps between two
-synchronizations), per-step HIP-event times (median, p10, p90; back to back
-and after a 1 GiB cache flush), the roofline of the step (algorithmic bytes
+synchronizations, launched from the host: a HIP graph replay per step adds a
+fixed ~5 us on this ROCm, and its rate is printed beside), per-step HIP-event
+times (median, p10, p90; back to back and after a 1 GiB cache flush), the roofline of the step (algorithmic bytes
 over its event time, against the 8 TB/s spec and the streaming-read ceiling
 measured in the same run), the attention kernel's own roofline (its launches
 back to back in one HIP graph, so that the time is the kernel's and not a
@@ -405,17 +406,19 @@ def hbm_roofline(nbytes, ms, kernel, scope, ceil_gbps=None, traffic=None):
 def decode_extra(w, steps, nsets, kv_layout=None, ceil_gbps=None):
     """q/s and HBM GB/s of a decode workload through the fused entry point.
     The rate (ms_per_step, queries_per_s, the step roofline) comes from `steps`
-    back-to-back replays between two HIP events, as the headline figure does;
-    step_ms and step_ms_flushed are per-call HIP-event times (each replay
+    back-to-back host launches between two HIP events, as the headline figure
+    does (graph_replay_ms_per_step: the same with one HIP graph replay a step);
+    step_ms and step_ms_flushed are per-call HIP-event times (each step
     bracketed by its own events, so they include the launch gap a lone call
     pays; the second after a cache flush).  The attention kernel is timed
     alone on the same selection."""
     import torch
     D = Device(w, nsets, kv_layout=kv_layout)
     D.capture()
-    ms = event_time_ms(D.replay, steps, 3)
-    b2b = step_times_ms(D.replay, steps, 3)
-    fl = step_times_ms(D.replay, max(5, steps // 2), 1, flush=Flusher())
+    ms = event_time_ms(D.fused, steps, 3)
+    g_ms = event_time_ms(D.replay, steps, 3)
+    b2b = step_times_ms(D.fused, steps, 3)
+    fl = step_times_ms(D.fused, max(5, steps // 2), 1, flush=Flusher())
     D.select()
     torch.cuda.synchronize()
     attn = step_times_ms(D.attn, steps, 3)
@@ -424,7 +427,8 @@ def decode_extra(w, steps, nsets, kv_layout=None, ceil_gbps=None):
     a_bytes = attn_bytes(w, cnt)
     byts = a_bytes + index_bytes(w)
     res = dict(workload=w.name, kv_layout=LAYOUT_NAMES[D.kv_layout], queries=w.num_queries,
-               ms_per_step=round(ms, 5), step_ms=dist(b2b), step_ms_flushed=dist(fl),
+               ms_per_step=round(ms, 5), graph_replay_ms_per_step=round(g_ms, 5),
+               step_ms=dist(b2b), step_ms_flushed=dist(fl),
                queries_per_s=round(w.num_queries / (ms * 1e-3), 1),
                roofline=hbm_roofline(byts, ms, "dsa_sparse_decode_fused (every launch of the step)",
                                      "step", ceil_gbps),
@@ -652,8 +656,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch every step from Python instead of replaying HIP graphs")
+    ap.add_argument("--graph", action="store_true",
+                    help="time per-step HIP graph replays instead of host launches (a replay "
+                         "adds a fixed ~5 us a step on this ROCm; the other mode is reported "
+                         "beside the figure either way)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--kv-layout", choices=["head_major", "token_major"], default="head_major",
@@ -700,11 +706,11 @@ def main():
     log(f"workload {w.name}: pool {w.num_blocks} blocks, {args.query_sets} query sets")
     D = Device(w, args.query_sets)
 
-    # timed region: K fused steps replayed from HIP graphs, inputs resident
-    step = D.fused
-    if not args.no_graph:
-        D.capture()
-        step = D.replay
+    # timed region: K fused steps launched back to back from the host (or, with
+    # --graph, replayed from one HIP graph a step), inputs resident
+    D.capture()
+    step = D.replay if args.graph else D.fused
+    other = D.fused if args.graph else D.replay
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -715,8 +721,11 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     log(f"fused step {ms_step * 1e3:.1f} us")
-    # the same steps, each bracketed by its own HIP events on the launch stream,
-    # back to back and after a 1 GiB cache flush
+    # the same K steps between two HIP events on the launch stream (the step
+    # roofline's time), the other launch mode likewise, and each step bracketed
+    # by its own events, back to back and after a 1 GiB cache flush
+    ms_ev = event_time_ms(step, args.steps, 2)
+    ms_other = event_time_ms(other, args.steps, 2)
     b2b = step_times_ms(step, args.steps, 2)
     flushed = step_times_ms(step, args.steps, 2, flush=Flusher())
 
@@ -740,7 +749,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    step_mean = dist(b2b)["mean"]
     result = {
         "metric": METRIC,
         "value": round(w.num_queries / (ms_step * 1e-3), 1),
@@ -759,12 +767,15 @@ def main():
                    "idx_heads": 8, "idx_dim": 128, "top_k": w.top_k,
                    "query_sets": args.query_sets, "kv_layout": args.kv_layout,
                    "entry": "dsa_sparse_decode_fused",
-                   "launch": "eager" if args.no_graph else "hip_graph_replay"},
+                   "launch": "hip_graph_replay" if args.graph else "host_launch"},
         "hbm_gbps": round(path_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_ms_events": round(ms_ev, 5),
+        "other_launch": {"launch": "host_launch" if args.graph else "hip_graph_replay",
+                         "ms_per_step": round(ms_other, 5)},
         "step_ms": dist(b2b),
         "step_ms_flushed": dist(flushed),
-        "roofline": hbm_roofline(path_bytes, step_mean, STEP_KERNELS, "step", ceil_gbps, traffic),
+        "roofline": hbm_roofline(path_bytes, ms_ev, STEP_KERNELS, "step", ceil_gbps, traffic),
         "attention_kernel": hbm_roofline(a_bytes, attn_ms,
                                          "sparse_attn_split (given lists)", "kernel", ceil_gbps,
                                          traffic_given),
