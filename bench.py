@@ -13,11 +13,14 @@ cannot serve a step from the previous one).
 Printed: one JSON line with queries/s (K back-to-back steps between two
 synchronizations, launched from the host: a HIP graph replay per step adds a
 fixed ~5 us on this ROCm, and its rate is printed beside), per-step HIP-event
-times (median, p10, p90; back to back and after a 1 GiB cache flush), the roofline of the step (algorithmic bytes
-over its event time, against the 8 TB/s spec and the streaming-read ceiling
-measured in the same run), the attention kernel's own roofline (its launches
-back to back in one HIP graph, so that the time is the kernel's and not a
-lone call's; per-call times beside it), and the oracle timed on the host's cores on a
+times (median, p10, p90; back to back and after a 1 GiB cache flush), the
+roofline of the step's dominant kernel (the attention kernel that selects its
+blocks from the scores, launched alone through dsa_sparse_attn_decode_topk:
+algorithmic bytes over its time from back-to-back launches in one HIP graph,
+so that the time is the kernel's and not a lone call's; per-call times
+beside it), the same for the whole step and for the given-list attention
+kernel, each against the 8 TB/s spec and the streaming-read ceiling
+measured in the same run, and the oracle timed on the host's cores on a
 bounded sample.  Extra fields report the other workloads (tiny, ragged,
 million-token decode; the chunked-prefill indexer) with their own rooflines,
 and the chip's measured ceilings.
@@ -43,6 +46,8 @@ FP8_PEAK_TFLOPS = 5000.0
 INT8_PEAK_TOPS = 5000.0
 # what one fused step of the batched decode launches (the roofline's scope)
 STEP_KERNELS = "index_score_i8_rows + sparse_attn_split (selects its blocks)"
+# the step's dominant kernel (the roofline's), as the kernel trace names it
+SELECT_KERNEL = "sparse_attn_split<4, 2, 1, 0, 0, true>"
 # the sources of the batched-decode step's kernels (the traffic counters are keyed to them)
 ATTN_SRCS = [os.path.join(ROOT, "dynamic_sparse_attention_paged_amd", "csrc", f)
              for f in ("attn.hip", "attn_tile.h", "cand_common.h", "select_common.h",
@@ -62,6 +67,13 @@ def attn_bytes(w, cnt):
     blk = w.block_size * w.num_kv_heads * w.head_dim * 2 * 2
     per_q_fixed = w.num_q_heads * w.head_dim * (2 + 4) + w.num_q_heads * 4 + 4
     return int(sum(int(c) * (blk + 8) for c in cnt)) + w.num_queries * per_q_fixed
+
+
+def select_attn_bytes(w, cnt):
+    """Algorithmic bytes of the attention kernel that selects its blocks itself:
+    those of the given-list kernel plus each query's row of scores (4 B per
+    candidate block)."""
+    return attn_bytes(w, cnt) + sum(4 * (int(p) // w.block_size) for p in w.q_pos)
 
 
 def index_bytes(w):
@@ -120,6 +132,8 @@ class Device:
         self.ws_attn = dsa.make_workspace(_lib.OP_ATTN_DECODE, self.kv, self.sets[0], w.top_k)
         self.scores = torch.empty(nq, w.block_table.shape[1], dtype=torch.float32, device="cuda")
         self.dsa = dsa
+        self.sc_sets = None  # per query set: its scores (for the selecting attention alone)
+        self.graphs_of = {}
 
     def fused(self, i, with_idx=False):
         s = i % len(self.sets)
@@ -162,6 +176,37 @@ class Device:
         if getattr(self, "attn_graph", None) is None:
             self.capture_attn()
         return event_time_ms(lambda i: self.attn_graph.replay(), n, 2) / self.attn_reps
+
+    def score_sets(self):
+        """Every query set's scores (dsa_index_score), kept for attn_sel."""
+        import torch
+        self.sc_sets = [torch.empty_like(self.scores) for _ in self.sets]
+        for s in range(len(self.sets)):
+            self.dsa.index_score(self.kv, self.sets[s], scores=self.sc_sets[s])
+        torch.cuda.synchronize()
+
+    def attn_sel(self, i):
+        """The fused step's attention kernel alone: it selects each query's blocks
+        from the scores, then attends them (dsa_sparse_attn_decode_topk)."""
+        s = i % len(self.sets)
+        self.dsa.sparse_attn_decode_topk(self.kv, self.sets[s], self.sc_sets[s], self.w.top_k,
+                                         self.w.softmax_scale, out=self.out, lse=self.lse,
+                                         workspace=self.ws_attn)
+
+    def launch_ms(self, name, fn, n, reps=16):
+        """Average HIP-event time (ms) of one launch of fn, from n replays of one
+        HIP graph holding `reps` back-to-back calls fn(0), fn(1), ..."""
+        import torch
+        if name not in self.graphs_of:
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    fn(i)
+            torch.cuda.synchronize()
+            self.graphs_of[name] = g
+        g = self.graphs_of[name]
+        return event_time_ms(lambda i: g.replay(), n, 2) / reps
 
     def select(self):
         for s in range(len(self.sets)):
@@ -267,18 +312,19 @@ KV_LAYOUT = 1
 
 def traffic_from_profile():
     """Measured HBM bytes (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on a
-    device copy) of the batched-decode step and of the given-list attention
-    kernel, if the counters in profiles/ were taken on the current sources:
-    (step_bytes, given_list_bytes), else (None, None)."""
+    device copy) of the batched-decode step, of its selecting attention kernel
+    and of the given-list attention kernel, if the counters in profiles/ were
+    taken on the current sources: (step, selecting, given_list), else Nones."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         src = hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()
         if t.get("src_sha256") != src or t.get("kv_layout") != LAYOUT_NAMES[KV_LAYOUT]:
-            return None, None
-        return t.get("step_bytes"), t.get("given_list_bytes")
+            return None, None, None
+        sel = t.get("kernels", {}).get(SELECT_KERNEL, {}).get("bytes_per_dispatch")
+        return t.get("step_bytes"), sel, t.get("given_list_bytes")
     except (OSError, ValueError):
-        return None, None
+        return None, None, None
 
 
 def _oracle_decode_loop(w, budget_s, qseed0):
@@ -736,10 +782,15 @@ def main():
     attn_ms = D.attn_launch_ms(max(3, args.steps // 8))
     score_ms = event_time_ms(D.score, args.steps, 3)
     topk_ms = event_time_ms(D.topk, args.steps, 3)
+    # the step's own attention kernel (it selects from the scores) alone
+    D.score_sets()
+    sel_t = step_times_ms(D.attn_sel, args.steps, 3)
+    sel_ms = D.launch_ms("attn_sel", D.attn_sel, max(3, args.steps // 8))
     cnt = D.cnt[0].cpu().numpy()
     a_bytes = attn_bytes(w, cnt)
+    s_bytes = select_attn_bytes(w, cnt)
     path_bytes = a_bytes + index_bytes(w)
-    traffic, traffic_given = traffic_from_profile()
+    traffic, traffic_sel, traffic_given = traffic_from_profile()
 
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -775,15 +826,20 @@ def main():
                          "ms_per_step": round(ms_other, 5)},
         "step_ms": dist(b2b),
         "step_ms_flushed": dist(flushed),
-        "roofline": hbm_roofline(path_bytes, ms_ev, STEP_KERNELS, "step", ceil_gbps, traffic),
+        "roofline": hbm_roofline(s_bytes, sel_ms,
+                                 f"{SELECT_KERNEL}: the step's attention kernel, selecting its "
+                                 "blocks from the scores (dsa_sparse_attn_decode_topk)",
+                                 "kernel", ceil_gbps, traffic_sel),
+        "step_roofline": hbm_roofline(path_bytes, ms_ev, STEP_KERNELS, "step", ceil_gbps, traffic),
         "attention_kernel": hbm_roofline(a_bytes, attn_ms,
                                          "sparse_attn_split (given lists)", "kernel", ceil_gbps,
                                          traffic_given),
         "stages_ms": {"index_score": round(score_ms, 5), "topk": round(topk_ms, 5),
-                      "sparse_attn": round(attn_ms, 5)},
+                      "sparse_attn": round(attn_ms, 5), "sparse_attn_topk": round(sel_ms, 5)},
         "ceilings": ceil,
     }
     result["attention_kernel"]["per_call_ms"] = dist(attn_t)
+    result["roofline"]["per_call_ms"] = dist(sel_t)
     del D
     torch.cuda.empty_cache()
 

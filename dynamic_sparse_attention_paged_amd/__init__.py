@@ -19,7 +19,8 @@ import torch
 from . import _lib
 
 __all__ = ["PagedKV", "Queries", "DSAError", "index_score", "topk_blocks",
-           "sparse_attn_decode", "sparse_attn_prefill", "decode_fused", "decode_fused_noalloc",
+           "sparse_attn_decode", "sparse_attn_decode_topk", "sparse_attn_prefill", "decode_fused",
+           "decode_fused_noalloc",
            "index_topk",
            "workspace_size", "make_workspace", "KV_TOKEN_MAJOR", "KV_HEAD_MAJOR", "abi_version", "check_inputs",
            "kv_write", "index_key_write"]
@@ -193,6 +194,30 @@ def sparse_attn_decode(kv, qs, block_idx, block_cnt, top_k, softmax_scale, out=N
                                       out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                       workspace.numel(), _stream(dev)))
     return out, lse
+
+
+def sparse_attn_decode_topk(kv, qs, scores, top_k, softmax_scale, out=None, lse=None,
+                            block_idx=None, block_cnt=None, workspace=None):
+    """Decode attention that selects each query's blocks from its indexer scores
+    (as index_score writes them) itself.  Returns (out, lse, block_idx, block_cnt);
+    block_idx / block_cnt are None unless tensors are passed in to receive them."""
+    lib = _lib.load()
+    _check_tensors(scores, block_idx, block_cnt, *_kv_tensors(kv), *_q_tensors(qs))
+    dev = kv.k_cache.device
+    nq, hq = qs.q.shape[0], qs.q.shape[1]
+    if out is None:
+        out = torch.empty(nq, hq, 128, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(nq, hq, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(workspace_size(_lib.OP_ATTN_DECODE, kv, qs, top_k), dev)
+    kvs, qss = kv.struct(), qs.struct()
+    _check(lib.dsa_sparse_attn_decode_topk(
+        ctypes.byref(kvs), ctypes.byref(qss), scores.data_ptr(), top_k, float(softmax_scale),
+        out.data_ptr(), lse.data_ptr(), block_idx.data_ptr() if block_idx is not None else None,
+        block_cnt.data_ptr() if block_cnt is not None else None, workspace.data_ptr(),
+        workspace.numel(), _stream(dev)))
+    return out, lse, block_idx, block_cnt
 
 
 def sparse_attn_prefill(kv, qs, block_idx, block_cnt, top_k, softmax_scale, out=None, lse=None):

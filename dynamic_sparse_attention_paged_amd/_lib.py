@@ -16,6 +16,7 @@ OP_PREFILL_FUSED = 4
 NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # DSA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["dsa_index_score", "dsa_topk_blocks", "dsa_sparse_attn_decode",
+           "dsa_sparse_attn_decode_topk",
            "dsa_sparse_attn_prefill", "dsa_sparse_decode_fused", "dsa_sparse_decode_fused_noalloc",
            "dsa_sparse_prefill_fused",
            "dsa_index_topk",
@@ -92,6 +93,7 @@ def load():
         "dsa_index_score": [kvp, qp, vp, vp],
         "dsa_topk_blocks": [vp, kvp, qp, i32, vp, vp, vp],
         "dsa_sparse_attn_decode": [kvp, qp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
+        "dsa_sparse_attn_decode_topk": [kvp, qp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp],
         "dsa_sparse_attn_prefill": [kvp, qp, vp, vp, i32, f32, vp, vp, vp],
         "dsa_sparse_decode_fused": [kvp, qp, i32, f32, vp, vp, vp, vp, vp, sz, vp],
         "dsa_sparse_decode_fused_noalloc": [kvp, qp, i32, f32, vp, vp, vp, vp, vp],

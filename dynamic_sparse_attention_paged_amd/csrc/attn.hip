@@ -191,10 +191,11 @@ __device__ __forceinline__ void attn_unit(
     __syncthreads();
     n_sel = cnt_lds;
     sel = sel_lds;
-    if (idx_out && sp == 0 && g == 0) {
-      for (int i = threadIdx.x; i < top_k; i += 64 * kAttnWaves)
-        idx_out[(size_t)qi * top_k + i] = sel_lds[i];
-      if (threadIdx.x == 0) cnt_out[qi] = n_sel;
+    if (sp == 0 && g == 0) {  // each output optional on its own
+      if (idx_out)
+        for (int i = threadIdx.x; i < top_k; i += 64 * kAttnWaves)
+          idx_out[(size_t)qi * top_k + i] = sel_lds[i];
+      if (cnt_out && threadIdx.x == 0) cnt_out[qi] = n_sel;
     }
   } else {
     n_sel = given_n;

@@ -431,6 +431,43 @@ dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
       "sparse_attn_decode launch");
 }
 
+dsa_status dsa_sparse_attn_decode_topk(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                       const float* scores, int32_t top_k, float softmax_scale,
+                                       float* out, float* lse, int32_t* block_idx_out,
+                                       int32_t* block_cnt_out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = check_common(kv, qs, kNeedAttn);
+  if (st != DSA_OK) return st;
+  if ((st = check_topk(top_k)) != DSA_OK) return st;
+  if (!scores || !out) return fail(DSA_ERR_NULL, "scores/out NULL");
+  if (!aligned(scores, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) ||
+      (block_idx_out && !aligned(block_idx_out, 4)) || (block_cnt_out && !aligned(block_cnt_out, 4)))
+    return fail(DSA_ERR_ALIGN, "scores/out/lse/block_idx_out/block_cnt_out need 4 B alignment");
+  if (kv->max_blocks_per_seq > 2048 || top_k > 2048)
+    return fail(DSA_ERR_UNSUPPORTED, "selection inside attention: at most 2048 blocks per "
+                "sequence and top_k <= 2048 (got %d, %d)", kv->max_blocks_per_seq, top_k);
+  const AttnLayout a = attn_layout(kv, qs, top_k, 0);
+  const size_t need = a.total;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu B < required %zu B", workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace needs 256 B alignment");
+  if (qs->num_queries == 0) return ok();
+  // the selecting kernel runs four waves a workgroup; the eight-wave plan of a
+  // short list (one split, no partials) becomes the four-wave one
+  dsa::AttnPlan plan = a.plan;
+  if (plan.waves != 4) {
+    plan.waves = 4;
+    plan.splits = 1;
+  }
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(
+      dsa::launch_sparse_attn_select(kv_view(kv), q_view(qs), scores, top_k, softmax_scale, out,
+                                     lse, plan.splits > 1 ? reinterpret_cast<float*>(ws + a.partials)
+                                                          : nullptr,
+                                     plan, block_idx_out, block_cnt_out, stream),
+      "sparse_attn_decode_topk launch");
+}
+
 dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs,
                                    const int32_t* block_idx, const int32_t* block_cnt,
                                    int32_t top_k, float softmax_scale, float* out, float* lse,

@@ -181,6 +181,29 @@ dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode attention with the Top-K selection fused in ([P3] "Day-0
+ * Adaptation for Trillion-Parameter Models...", section 4.1: Top-K fused with
+ * the operators before and after it; [P5] "Day-0 Readiness...",
+ * "Differentiated Adaptation of Prefill and Decode": selection, gather and
+ * attention fused in decode).  scores: fp32 [num_queries,
+ * max_blocks_per_seq] as dsa_index_score writes them (only a query's visible
+ * blocks 0 .. pos / block_size - 1 are read), 4 B aligned.  Every attention
+ * workgroup selects its query's blocks from that row with dsa_topk_blocks's
+ * rule, into on-chip memory, and attends them: the selection is the one
+ * dsa_topk_blocks returns and the outputs are those of dsa_sparse_attn_decode
+ * on it (within the decode tolerance).  block_idx_out / block_cnt_out
+ * (nullable, each on its own) receive the selection.  Limits:
+ * max_blocks_per_seq <= 2048 and top_k <= 2048 (DSA_ERR_UNSUPPORTED).
+ * workspace: at least dsa_workspace_size(DSA_OP_ATTN_DECODE) bytes, 256 B
+ * aligned (may be NULL when that size is 0).
+ */
+dsa_status dsa_sparse_attn_decode_topk(const dsa_paged_kv* kv, const dsa_queries* qs,
+                                       const float* scores, int32_t top_k, float softmax_scale,
+                                       float* out, float* lse, int32_t* block_idx_out,
+                                       int32_t* block_cnt_out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Sparse attention of a chunk of prefill queries ([P3] section 4.3 and [P5]
  * "Differentiated Adaptation of Prefill and Decode": the prefill path is
  * compute-bound and batches many queries).  Same result as

@@ -161,6 +161,31 @@ def test_write_path_validation(lib):
     assert ikw(_kv(), n=0) == 0
 
 
+def test_decode_topk_contract(lib):
+    """Decode attention that selects from given scores: its own checks."""
+    E = {v: k for k, v in _lib.STATUS.items()}
+    kv, qs = _kv(), _qs()
+
+    def call(kv=kv, sc=FAKE, top_k=4, out=FAKE, lse=None, bi=None, bc=None, ws=FAKE, n=1 << 20):
+        return lib.dsa_sparse_attn_decode_topk(ctypes.byref(kv), ctypes.byref(qs), sc, top_k, 0.1,
+                                               out, lse, bi, bc, ws, n, None)
+    assert call(sc=None) == E["DSA_ERR_NULL"]
+    assert call(out=None) == E["DSA_ERR_NULL"]
+    assert call(sc=FAKE + 2) == E["DSA_ERR_ALIGN"]
+    assert call(bc=FAKE + 2) == E["DSA_ERR_ALIGN"]
+    assert call(top_k=0) == E["DSA_ERR_SHAPE"]
+    # the selection inside attention covers at most 2048 blocks and top_k <= 2048
+    assert call(top_k=2049) == E["DSA_ERR_UNSUPPORTED"]
+    assert call(kv=_kv(max_blocks_per_seq=2049, num_blocks=4100)) == E["DSA_ERR_UNSUPPORTED"]
+    # the split partials' workspace is checked like dsa_sparse_attn_decode's
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_workspace_size(_lib.OP_ATTN_DECODE, ctypes.byref(kv), ctypes.byref(qs), 4,
+                                  ctypes.byref(n)) == 0
+    if n.value > 0:
+        assert call(ws=None) == E["DSA_ERR_WORKSPACE"]
+        assert call(n=n.value - 1) == E["DSA_ERR_WORKSPACE"]
+
+
 def test_workspace_contract(lib):
     E = {v: k for k, v in _lib.STATUS.items()}
     kv, qs = _kv(), _qs()

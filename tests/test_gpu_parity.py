@@ -68,7 +68,26 @@ def _run_all_stages(dsa, w, label, kv_layout=0):
     ri, rc = torch.from_numpy(ref_idx).cuda(), torch.from_numpy(ref_cnt).cuda()
     out2, lse2 = dsa.sparse_attn_decode(kv, qs, ri, rc, K, w.softmax_scale) if w.decode else \
         dsa.sparse_attn_prefill(kv, qs, ri, rc, K, w.softmax_scale)
+    # decode attention that selects from the scores itself: on the library's
+    # scores (the selection bit for bit the Top-K kernel's) and on the oracle's
+    # (the oracle's selection); only the count is asked for in the second call
+    fused_sel = w.decode and maxb <= 2048 and K <= 2048
+    if fused_sel:
+        bi3 = torch.empty_like(idx)
+        bc3 = torch.empty_like(cnt)
+        out3, lse3, _, _ = dsa.sparse_attn_decode_topk(kv, qs, scores, K, w.softmax_scale,
+                                                       block_idx=bi3, block_cnt=bc3)
+        bc4 = torch.empty_like(cnt)
+        out4, lse4, _, _ = dsa.sparse_attn_decode_topk(kv, qs, torch.from_numpy(ref_scores).cuda(),
+                                                       K, w.softmax_scale, block_cnt=bc4)
     torch.cuda.synchronize()
+    if fused_sel:
+        assert np.array_equal(bi3.cpu().numpy(), idx_h) and np.array_equal(bc3.cpu().numpy(), cnt_h), \
+            f"{label}: selection inside attention differs from the Top-K kernel's"
+        assert np.array_equal(bc4.cpu().numpy(), ref_cnt)
+        extra = [(out3, lse3), (out4, lse4)]
+    else:
+        extra = []
 
     worst = (0.0, 0.0)
     for qi, r in enumerate(refs):
@@ -78,7 +97,8 @@ def _run_all_stages(dsa, w, label, kv_layout=0):
         assert int(cnt2[qi]) == r["cnt"]
         ok, _ = parity.check_indices(idx_h[qi], cnt_h[qi], r, K)
         assert ok, f"{label} q{qi}: idx {idx_h[qi]} cnt {cnt_h[qi]} vs {r['idx']} {r['cnt']}"
-        for o, l in ((out_h[qi], lse_h[qi]), (out2[qi].cpu().numpy(), lse2[qi].cpu().numpy())):
+        for o, l in [(out_h[qi], lse_h[qi]), (out2[qi].cpu().numpy(), lse2[qi].cpu().numpy())] + \
+                [(o_[qi].cpu().numpy(), l_[qi].cpu().numpy()) for o_, l_ in extra]:
             good, a, rel = parity.attn_ok(o, r["out"])
             assert good, f"{label} q{qi}: attention max-abs {a:.3e} max-rel {rel:.3e}"
             la, _ = parity.attn_errors(l, r["lse"])
