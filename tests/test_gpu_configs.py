@@ -85,6 +85,20 @@ def test_batched_decode_full(dsa, kv_layout):
     _say(f"batched decode 32 x 32768, all queries, kv_layout {kv_layout}")
     idx, cnt, out, lse = _fused(dsa, w, kv_layout)
     _check(w, range(w.num_queries), idx, cnt, out, lse, "batched_decode")
+    # the fused step's attention kernel alone, as bench.py times it for its
+    # roofline: scores from dsa_index_score, selection inside the attention
+    kv, qs = parity.to_device(w, kv_layout=kv_layout)
+    scores = dsa.index_score(kv, qs)
+    bi = torch.empty(w.num_queries, w.top_k, dtype=torch.int32, device="cuda")
+    bc = torch.empty(w.num_queries, dtype=torch.int32, device="cuda")
+    o2, l2, _, _ = dsa.sparse_attn_decode_topk(kv, qs, scores, w.top_k, w.softmax_scale,
+                                               block_idx=bi, block_cnt=bc)
+    torch.cuda.synchronize()
+    assert np.array_equal(bi.cpu().numpy(), idx) and np.array_equal(bc.cpu().numpy(), cnt)
+    # the same kernel as the fused step's, on the same selection: the same bits
+    assert np.array_equal(o2.cpu().numpy(), out) and np.array_equal(l2.cpu().numpy(), lse)
+    del kv, qs, scores, o2, l2
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("kv_layout", [0, 1], ids=["token_major", "head_major"])
