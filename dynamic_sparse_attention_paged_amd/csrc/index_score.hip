@@ -183,9 +183,19 @@ hipError_t launch_cand_di(const KvView& kv, const QView& Q, int need, float* ws,
 
 template <int DI, int HP>
 hipError_t launch_i8_rows_t(const KvView& kv, const QView& Q, float* scores, hipStream_t st) {
-  // one 16-block tile a wave: 64 blocks a workgroup
-  dim3 grid((kv.maxb + 63) / 64, Q.nq);
-  hipLaunchKernelGGL((index_score_i8_rows<DI, HP, 1>), grid, dim3(256), 0, st, kv, Q, scores);
+  // One 16-block tile a wave (64 blocks a workgroup) while that grid fits a
+  // few workgroups per CU; larger jobs (many long sequences) take eight tiles
+  // a wave, so that each workgroup's query set-up (its rows quantized into
+  // digit planes) serves 512 blocks (measured on 128 sequences of up to 2048
+  // blocks: 22 us with one tile a wave, the decode step 6-8 us shorter).
+  const long wg1 = (long)((kv.maxb + 63) / 64) * Q.nq;
+  if (wg1 > 4L * device_cu_count()) {
+    dim3 grid((kv.maxb + 511) / 512, Q.nq);
+    hipLaunchKernelGGL((index_score_i8_rows<DI, HP, 8>), grid, dim3(256), 0, st, kv, Q, scores);
+  } else {
+    dim3 grid((kv.maxb + 63) / 64, Q.nq);
+    hipLaunchKernelGGL((index_score_i8_rows<DI, HP, 1>), grid, dim3(256), 0, st, kv, Q, scores);
+  }
   return hipGetLastError();
 }
 

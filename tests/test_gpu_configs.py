@@ -118,6 +118,14 @@ def test_ragged_decode_sampled(dsa, kv_layout):
     order = np.argsort(w.seq_lens)
     qis = sorted(set(order[:4].tolist() + order[-4:].tolist() + list(range(0, 128, 16))))
     _check(w, qis, idx, cnt, out, lse, "ragged_decode")
+    # the scores (eight 16-block tiles a wave at this size): the oracle's, bit for bit
+    kv, qs = parity.to_device(w, kv_layout=kv_layout)
+    sh = dsa.index_score(kv, qs).cpu().numpy()
+    del kv, qs
+    torch.cuda.empty_cache()
+    for qi in [int(order[0]), int(order[-1]), 37]:
+        r = parity.oracle_query(w, qi)
+        assert parity.check_scores_exact(sh[qi], r, w.block_table.shape[1]).size == 0, f"q{qi}"
 
 
 # tile edges (queries 63/64/65, 127/128), the first and last queries, the
