@@ -191,8 +191,9 @@ dsa_status dsa_sparse_attn_decode(const dsa_paged_kv* kv, const dsa_queries* qs,
  * workgroup selects its query's blocks from that row with dsa_topk_blocks's
  * rule, into on-chip memory, and attends them: the selection is the one
  * dsa_topk_blocks returns and the outputs are those of dsa_sparse_attn_decode
- * on it (within the decode tolerance).  block_idx_out / block_cnt_out
- * (nullable, each on its own) receive the selection.  Limits:
+ * on it (within the decode tolerance); out and lse (nullable) as there.
+ * block_idx_out / block_cnt_out (nullable, each on its own) receive the
+ * selection.  Limits:
  * max_blocks_per_seq <= 2048 and top_k <= 2048 (DSA_ERR_UNSUPPORTED).
  * workspace: at least dsa_workspace_size(DSA_OP_ATTN_DECODE) bytes, 256 B
  * aligned (may be NULL when that size is 0).
@@ -218,8 +219,8 @@ dsa_status dsa_sparse_attn_prefill(const dsa_paged_kv* kv, const dsa_queries* qs
  * One-call decode ([P5] "Differentiated Adaptation of Prefill and Decode":
  * fuse index selection, gather and attention in decode): dsa_index_score,
  * dsa_topk_blocks and dsa_sparse_attn_decode in one entry point with the
- * same results.  block_idx_out / block_cnt_out (nullable) receive the
- * selection.  workspace: at least dsa_workspace_size(DSA_OP_DECODE_FUSED)
+ * same results.  block_idx_out / block_cnt_out (nullable, each on its
+ * own) receive the selection.  workspace: at least dsa_workspace_size(DSA_OP_DECODE_FUSED)
  * bytes, 256 B aligned.
  */
 dsa_status dsa_sparse_decode_fused(const dsa_paged_kv* kv, const dsa_queries* qs, int32_t top_k,
