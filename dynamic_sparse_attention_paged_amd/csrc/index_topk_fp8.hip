@@ -79,7 +79,7 @@ constexpr int kQB = 8;            // queries per workgroup (two groups of four)
 constexpr int kMaxBlocks = 2048;  // blocks per sequence: scores of kQB queries in LDS
 constexpr int kPitch = kMaxBlocks + 16;  // rows 16 banks apart
 constexpr int kListCap = 256;     // undecided blocks ranked from a list (more: every block rescored)
-constexpr int kChunk = 4;         // column tiles per pipeline step
+constexpr int kChunk = 2;         // column tiles per pipeline step
 // the error bound's unit: 448 ks_max 2^-13 per unit of |a| (7 sum_g Mq + 3 max|q8|)
 constexpr float kErrUnit = 448.f * 0.0001220703125f;
 
@@ -434,8 +434,9 @@ __global__ __launch_bounds__(kThreads, 2) void index_topk_fp8(KvView kv, QView Q
       }
     };
     // Software pipeline, three stages: table entries three chunks ahead, key
-    // rows two chunks ahead (eight column tiles in flight: the key rows are
-    // scattered and their latency is long).  Vector-memory loads complete in
+    // rows two chunks ahead (four column tiles in flight: the key rows are
+    // scattered and their latency is long; eight, with four-tile chunks, took
+    // 224 registers a lane and measured slower).  Vector-memory loads complete in
     // order, so each step issues the table loads of chunk c + 3 before the
     // key loads of chunk c + 2 (whose table entries came a step earlier):
     // waiting for those entries then never waits for keys still in use.
