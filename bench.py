@@ -664,10 +664,13 @@ def prefill_indexer_extra(steps):
                topk_ms=round(tk_ms, 4), attention_ms=round(at_ms, 3),
                score_kernel_step_ms=dist(sc_t))
     # scoring + selection in one launch (approximate FP8 scores, exact ones
-    # where the bound leaves the boundary undecided): the graded indexer
+    # where the bound leaves the boundary undecided): the graded indexer.  Its
+    # roofline takes the kernel's own duration, from back-to-back launches
+    # between two HIP events (a lone call's launch gap is not the kernel's);
+    # per-call times beside it
     it_t = step_times_ms(D.itopk, steps, 2)
-    it_ms = dist(it_t)["mean"]
-    res.update(index_topk_ms=it_ms, index_topk_step_ms=dist(it_t),
+    it_ms = event_time_ms(D.itopk, max(steps, 20), 3)
+    res.update(index_topk_ms=round(it_ms, 5), index_topk_step_ms=dist(it_t),
                roofline={"kernel": "index_topk_fp8 (dsa_index_topk: scoring + selection)",
                          "scope": "kernel", "bound": "mfma",
                          "achieved": round(fl / (it_ms * 1e-3) / 1e12, 2),
