@@ -138,3 +138,42 @@ def test_fp8_selection_zero_query_rows(dsa):
     qb[11, :5, :] = 0
     w = _with(w, q_idx_bits=qb)
     _check(dsa, w, "fp8 index_topk zero query rows", oracle_all=False, sample=[3, 10, 11, 12])
+
+
+def _e4m3_codes(x):
+    """E4M3 codes (uint8) of x by torch's float8_e4m3fn conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def _bf16_bits(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def test_fp8_selection_outlier_operands(dsa):
+    """Keys and query rows made mostly of small values with a few large ones
+    in random dims (the FP8 matrix unit's truncation errors are then largest
+    against the products that survive), and pairs of blocks with identical
+    keys and scales (exact ties that the bound must leave undecided): the
+    selection still equals the exact one for every query."""
+    w = workload.small_prefill(seed=4070, L=64 * 1100 + 5, count=264, hi=8, di=128, top_k=24)
+    rng = np.random.default_rng(4071)
+    P, dI = w.idx_keys.shape
+    kx = rng.standard_normal((P, dI)) * 0.05
+    hit = rng.random((P, dI)) < 0.04
+    kx = np.where(hit, rng.standard_normal((P, dI)) * 3.0, kx)
+    kx = kx * (448.0 / np.maximum(np.abs(kx).max(axis=1, keepdims=True), 1e-30))
+    keys = _e4m3_codes(kx)
+    ks = (rng.uniform(0.5, 2.0, P) / 448.0).astype(np.float32)
+    twin = rng.random(P) < 0.1  # block p takes block p - 1's key and scale
+    for p in np.flatnonzero(twin[1:]) + 1:
+        keys[p] = keys[p - 1]
+        ks[p] = ks[p - 1]
+    nq, hi = w.q_idx_bits.shape[0], w.q_idx_bits.shape[1]
+    qx = rng.standard_normal((nq, hi, dI)) * 0.1
+    qhit = rng.random((nq, hi, dI)) < 0.05
+    qx = np.where(qhit, rng.standard_normal((nq, hi, dI)) * 4.0, qx)
+    w = _with(w, idx_keys=keys, idx_scale=ks, q_idx_bits=_bf16_bits(qx))
+    _check(dsa, w, "fp8 index_topk outlier operands", oracle_all=False,
+           sample=[0, 1, 63, 64, 131, 263])
