@@ -12,6 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
+# diagnostic variant: the attention kernel records per-wave clocks (wave_clocks.py)
+LIB_CLOCKS = os.path.join(HERE, "libdsa_clocks.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -23,8 +25,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
 SOURCES = ["support.hip", "index_score.hip", "index_score_mfma.hip", "index_topk_fused.hip", "index_topk_fp8.hip", "topk.hip", "attn.hip", "prefill_inv.hip", "moe.hip", "check.hip", "write.hip", "dsa_api.cpp"]
 
 
-def _compile(src, obj):
-    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, obj, extra=()):
+    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
@@ -38,6 +40,8 @@ def build(verbose=False):
         obj = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
         objs.append(obj)
         procs.append((s, _compile(s, obj)))
+    clk_obj = os.path.join(BUILD, "attn_clocks.o")
+    procs.append(("attn.hip (wave clocks)", _compile("attn.hip", clk_obj, ["-DDSA_WAVE_CLOCKS"])))
     failed = False
     for s, p in procs:
         out, _ = p.communicate()
@@ -55,6 +59,11 @@ def build(verbose=False):
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = LIB_CLOCKS + ".tmp"
+    clk_objs = [clk_obj if os.path.basename(o) == "attn.o" else o for o in objs]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + clk_objs
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_CLOCKS)
     return LIB
 
 

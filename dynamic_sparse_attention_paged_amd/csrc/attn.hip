@@ -39,6 +39,17 @@
 namespace dsa {
 namespace {
 
+#ifdef DSA_WAVE_CLOCKS
+// Diagnostic build only (not part of the library's default build): every
+// attention wave records its start and end on the constant-rate wall clock
+// (100 MHz) with the raw HW_ID and XCC_ID hardware registers, indexed by
+// ((KV head * Nq + query) * splits + split) * waves + wave, for timelines of
+// one launch.
+constexpr long kClockWaves = 1 << 16;
+__device__ unsigned long long g_wave_clock[kClockWaves][2];
+__device__ unsigned int g_wave_where[kClockWaves][2];
+#endif
+
 // split partials: one record per (query, head, split): m, l, o[128], two
 // floats of padding (16-byte records)
 constexpr int kPartStride = kHeadDim + 4;
@@ -421,9 +432,25 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_split(
   const int32_t* given_sel = kMode == kAttnGiven ? idx + (size_t)qi * top_k : nullptr;
   const int given_n = kMode == kAttnGiven ? cnt[qi] : 0;
   constexpr bool kFuse = kMode == kAttnCand;
+#ifdef DSA_WAVE_CLOCKS
+  const unsigned long long t_start = wall_clock64();
+#endif
   attn_unit<kAttnWaves, kVBufs, kMode, DI, HP, kNT, kFuse>(kv, Q, given_sel, given_n, scores,
                                                            idx_out, cnt_out, top_k, scale2, splits,
                                                            out, lse, partials, blockIdx.x, qi, g);
+#ifdef DSA_WAVE_CLOCKS
+  {
+    const unsigned long long t_end = wall_clock64();
+    const long wid = (((long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) *
+                         kAttnWaves + (threadIdx.x >> 6);
+    if ((threadIdx.x & 63) == 0 && wid < kClockWaves) {
+      g_wave_clock[wid][0] = t_start;
+      g_wave_clock[wid][1] = t_end;
+      g_wave_where[wid][0] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID, 32 bits
+      g_wave_where[wid][1] = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // XCC_ID, 16 bits
+    }
+  }
+#endif
   if (!kFuse || done == nullptr || splits == 1) return;
   __shared__ float ml[2 * kFusedMergeMaxGS];
   __shared__ float wf[kFusedMergeMaxGS];
@@ -741,3 +768,18 @@ hipError_t launch_sparse_attn_cand(const KvView& kv, const QView& Q, float* ws, 
 }
 
 }  // namespace dsa
+
+#ifdef DSA_WAVE_CLOCKS
+// Copies the first n waves' records of the last instrumented launch:
+// clocks [n][2] (start, end), where [n][2] (HW_ID, XCC_ID).  0 on success.
+extern "C" int dsa_wave_clocks_read(unsigned long long* clocks, unsigned int* where, int n) {
+  if (!clocks || !where || n < 1 || n > dsa::kClockWaves) return -1;
+  if (hipMemcpyFromSymbol(clocks, HIP_SYMBOL(dsa::g_wave_clock), sizeof(unsigned long long) * 2 * n,
+                          0, hipMemcpyDeviceToHost) != hipSuccess)
+    return -6;
+  if (hipMemcpyFromSymbol(where, HIP_SYMBOL(dsa::g_wave_where), sizeof(unsigned int) * 2 * n, 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return -6;
+  return 0;
+}
+#endif

@@ -305,3 +305,25 @@ def test_noalloc_rejects_oversized_scratch(lib):
     assert rc == -3
     assert b"scratch" in lib.dsa_last_error()
     assert _lib.NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024
+
+
+def test_wave_clock_build_is_separate(lib):
+    """The per-wave clock reader exists only in the diagnostic library
+    (libdsa_clocks.so), which exports the same entry points besides it; the
+    reader rejects a null buffer or a count outside 1..65536 on the host."""
+    assert not hasattr(lib, "dsa_wave_clocks_read")
+    path = os.path.join(_lib.HERE, "libdsa_clocks.so")
+    if not os.path.exists(path):
+        pytest.fail("libdsa_clocks.so not built: run __graft_entry__.build()")
+    clk = ctypes.CDLL(path)
+    for n in _declared():
+        assert hasattr(clk, n), n
+    read = clk.dsa_wave_clocks_read
+    read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    read.restype = ctypes.c_int
+    buf = (ctypes.c_ulonglong * 2)()
+    where = (ctypes.c_uint * 2)()
+    assert read(None, ctypes.addressof(where), 1) == -1
+    assert read(ctypes.addressof(buf), None, 1) == -1
+    assert read(ctypes.addressof(buf), ctypes.addressof(where), 0) == -1
+    assert read(ctypes.addressof(buf), ctypes.addressof(where), (1 << 16) + 1) == -1
