@@ -1,6 +1,7 @@
 """The fused decode captured in a HIP graph: every replay, with eager work and
 synchronizations between replays, equals the eager result bit for bit."""
 
+import numpy as np
 import pytest
 
 from dsa_synth import workload
@@ -172,3 +173,61 @@ def test_moe_grouped_gemm_graph_replays_match_eager():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(out, ref), (mode, rep)
+
+
+def test_fused_decode_on_any_workspace_contents():
+    """The fused decode needs no particular workspace contents: on a workspace
+    of random bytes, eager calls and graph replays equal the stage-wise path
+    (scores, Top-K, attention) bit for bit, and the selection equals the
+    oracle's.  Shapes: 32 sequences x 8 KV heads of 260 blocks (one split,
+    selection inside attention) and 4 x 4 (six splits, merged by a second
+    launch)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dynamic_sparse_attention_paged_amd as dsa
+    cases = [workload.small_decode(seed=2311, hq=64, hkv=8, hi=8, top_k=32,
+                                   lens=tuple(64 * 260 - 37 * (s % 5) for s in range(32))),
+             workload.small_decode(seed=2312, hq=32, hkv=4, hi=4, top_k=24,
+                                   lens=(64 * 700, 64 * 300 + 1, 64 * 5, 64 * 900))]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2313)
+    for w in cases:
+        kv, qs = parity.to_device(w)
+        K, nq = w.top_k, w.num_queries
+        sc = dsa.index_score(kv, qs)
+        ri, rc = dsa.topk_blocks(sc, kv, qs, K)
+        ro, rl = dsa.sparse_attn_decode(kv, qs, ri, rc, K, w.softmax_scale)
+        torch.cuda.synchronize()
+        ref = (ro.clone(), rl.clone(), ri.clone(), rc.clone())
+        for qi in (0, nq - 1):
+            r = parity.oracle_select(w, qi)
+            assert np.array_equal(ri[qi].cpu().numpy(), r["idx"]), (w.name, qi)
+        nbytes = dsa.workspace_size(dsa._lib.OP_DECODE_FUSED, kv, qs, K)
+        ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
+        out = torch.empty(nq, w.num_q_heads, 128, dtype=torch.float32, device="cuda")
+        lse = torch.empty(nq, w.num_q_heads, dtype=torch.float32, device="cuda")
+        bi = torch.empty(nq, K, dtype=torch.int32, device="cuda")
+        bc = torch.empty(nq, dtype=torch.int32, device="cuda")
+
+        def check(label):
+            for a, b in zip((out, lse, bi, bc), ref):
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (w.name, label)
+
+        for rep in range(3):
+            dsa.decode_fused(kv, qs, K, w.softmax_scale, out=out, lse=lse, block_idx=bi,
+                             block_cnt=bc, workspace=ws)
+            torch.cuda.synchronize()
+            check(f"eager {rep}")
+        ws.random_(0, 256, generator=gen)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dsa.decode_fused(kv, qs, K, w.softmax_scale, out=out, lse=lse, block_idx=bi,
+                             block_cnt=bc, workspace=ws)
+        for rep in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            check(f"replay {rep}")
+        del kv, qs, ws, g
+        torch.cuda.empty_cache()
