@@ -42,7 +42,8 @@ namespace {
 #ifdef DSA_WAVE_CLOCKS
 // Diagnostic build only (not part of the library's default build): every
 // attention wave records its start and end on the constant-rate wall clock
-// (100 MHz) with the raw HW_ID and XCC_ID hardware registers, indexed by
+// (100 MHz on MI355X; dsa_wave_clock_khz gives the rate) with the raw HW_ID
+// and XCC_ID hardware registers, indexed by
 // ((KV head * Nq + query) * splits + split) * waves + wave, for timelines of
 // one launch.
 constexpr long kClockWaves = 1 << 16;
@@ -779,6 +780,16 @@ extern "C" int dsa_wave_clocks_read(unsigned long long* clocks, unsigned int* wh
     return -6;
   if (hipMemcpyFromSymbol(where, HIP_SYMBOL(dsa::g_wave_where), sizeof(unsigned int) * 2 * n, 0,
                           hipMemcpyDeviceToHost) != hipSuccess)
+    return -6;
+  return 0;
+}
+
+// The current device's wall-clock rate in kHz (the stamps' unit).  0 on success.
+extern "C" int dsa_wave_clock_khz(int* khz) {
+  int dev = 0;
+  if (!khz) return -1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
     return -6;
   return 0;
 }

@@ -7,7 +7,7 @@ dsa_sparse_attn_decode_topk -- the fused step's attention kernel, which
 selects its blocks from the scores -- and prints one JSON line: the launch's
 span, each wave's start-to-end time summarized per XCD (XCC_ID) and per KV
 head, and the spread of start and end times.  Clocks are the constant-rate
-wall clock (100 MHz, 10 ns a tick).
+wall clock, converted at the rate the device reports (100 MHz on MI355X).
 
     python -m dynamic_sparse_attention_paged_amd.wave_clocks [--layout head_major|token_major]
 """
@@ -25,7 +25,6 @@ ROOT = os.path.dirname(HERE)
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-TICK_US = 0.01  # 100 MHz
 
 
 def _stats(a):
@@ -52,6 +51,9 @@ def main():
     read = lib.dsa_wave_clocks_read
     read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     read.restype = ctypes.c_int
+    khz = ctypes.c_int(0)
+    assert lib.dsa_wave_clock_khz(ctypes.byref(khz)) == 0 and khz.value > 0, "wall-clock rate"
+    tick_us = 1e3 / khz.value
 
     w = workload.batched_decode()
     t = synth_dev.upload(w)
@@ -92,14 +94,14 @@ def main():
     start = clocks[:, 0].astype(np.int64)
     end = clocks[:, 1].astype(np.int64)
     t0 = start.min()
-    s_us = (start - t0) * TICK_US
-    e_us = (end - t0) * TICK_US
+    s_us = (start - t0) * tick_us
+    e_us = (end - t0) * tick_us
     body = e_us - s_us
     xcc = (where[:, 1] & 0xF).astype(int)
     hw = where[:, 0].astype(np.int64)
     cu_key = xcc * 4096 + ((hw >> 13) & 7) * 512 + ((hw >> 12) & 1) * 256 + ((hw >> 8) & 15)
     g = np.arange(n) // (nq * splits * waves)
-    res = dict(workload=w.name, kv_layout=args.layout,
+    res = dict(workload=w.name, kv_layout=args.layout, wall_clock_khz=khz.value,
                kernel="sparse_attn_split<4, 2, 1, 0, 0, true> (dsa_sparse_attn_decode_topk)",
                waves=n, splits=splits, span_us=round(float(e_us.max()), 2),
                wave_start_us=_stats(s_us), wave_end_us=_stats(e_us), wave_body_us=_stats(body),

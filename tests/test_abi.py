@@ -327,3 +327,5 @@ def test_wave_clock_build_is_separate(lib):
     assert read(ctypes.addressof(buf), None, 1) == -1
     assert read(ctypes.addressof(buf), ctypes.addressof(where), 0) == -1
     assert read(ctypes.addressof(buf), ctypes.addressof(where), (1 << 16) + 1) == -1
+    assert clk.dsa_wave_clock_khz(None) == -1
+    assert not hasattr(lib, "dsa_wave_clock_khz")
