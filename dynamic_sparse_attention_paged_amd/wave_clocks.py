@@ -2,7 +2,8 @@
 
 Loads libdsa_clocks.so, the library built with per-wave clock stamps in the
 attention kernel (the default libdsa.so has none), runs the batched decode
-(32 x 32768 tokens, 64-token blocks, Top-K 32, head-major cache) through
+(32 x 32768 tokens, 64-token blocks, Top-K 32; head-major cache unless
+--layout token_major) through
 dsa_sparse_attn_decode_topk -- the fused step's attention kernel, which
 selects its blocks from the scores -- and prints one JSON line: the launch's
 span, each wave's start-to-end time summarized per XCD (XCC_ID) and per KV
@@ -24,7 +25,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
-
 
 
 def _stats(a):
