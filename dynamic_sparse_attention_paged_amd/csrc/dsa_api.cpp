@@ -69,7 +69,7 @@ dsa_status check_common(const dsa_paged_kv* kv, const dsa_queries* qs, unsigned 
   if (!block_size_ok(kv->block_size))
     return fail(DSA_ERR_UNSUPPORTED, "block_size %d: supported 64, 128, 256, 512", kv->block_size);
   if (kv->head_dim != dsa::kHeadDim)
-    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: this build supports 128", kv->head_dim);
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: the library supports 128 only", kv->head_dim);
   if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1 ||
       kv->num_kv_heads < 1)
     return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq, num_kv_heads must be >= 1");
@@ -577,7 +577,7 @@ dsa_status dsa_kv_write(const dsa_paged_kv* kv, int32_t n_tokens, const int32_t*
   if (!block_size_ok(kv->block_size))
     return fail(DSA_ERR_UNSUPPORTED, "block_size %d: supported 64, 128, 256, 512", kv->block_size);
   if (kv->head_dim != dsa::kHeadDim)
-    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: this build supports 128", kv->head_dim);
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d: the library supports 128 only", kv->head_dim);
   if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks_per_seq < 1 ||
       kv->num_kv_heads < 1)
     return fail(DSA_ERR_SHAPE, "num_blocks, num_seqs, max_blocks_per_seq, num_kv_heads must be >= 1");

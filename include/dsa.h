@@ -50,7 +50,7 @@ typedef enum {
   DSA_OK = 0,
   DSA_ERR_NULL = -1,        /* a required pointer is NULL                        */
   DSA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range                */
-  DSA_ERR_UNSUPPORTED = -3, /* a size this build has no kernel for               */
+  DSA_ERR_UNSUPPORTED = -3, /* a size the library has no kernel for             */
   DSA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented            */
   DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than dsa_workspace_size */
   DSA_ERR_HIP = -6          /* the HIP runtime reported an error                 */
@@ -92,7 +92,7 @@ typedef struct {
   int32_t num_blocks;          /* physical blocks in the pool, >= 1                                  */
   int32_t block_size;          /* tokens per block: 64, 128, 256 or 512 (see below)                  */
   int32_t num_kv_heads;        /* >= 1                                                               */
-  int32_t head_dim;            /* this build: 128                                                    */
+  int32_t head_dim;            /* 128: the one head size the kernels support                         */
   int32_t idx_dim;             /* coarse key length: 64 or 128                                       */
   int32_t num_seqs;            /* >= 1                                                               */
   int32_t max_blocks_per_seq;  /* row length of block_table, >= 1                                    */
